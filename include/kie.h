@@ -1,0 +1,229 @@
+/*
+ * kie.h -- C ABI of the persistent batch-1 decode monokernel for one AMD
+ * MI355X (gfx950).
+ *
+ * What the library computes.  Greedy autoregressive decoding of one request
+ * (batch 1) through a dense, pre-norm, decoder-only transformer (RMSNorm,
+ * rotary position embedding, grouped-query attention, SwiGLU feed-forward,
+ * untied LM head).  Every decode step of a kie_decode() call -- embedding,
+ * all layers, LM head, greedy argmax and the EOS test -- runs inside ONE
+ * grid-resident persistent kernel, which loops over tokens without returning
+ * to the host and without a kernel launch per token or per layer.  This is the
+ * "monokernel" of the Kog Inference Engine pages: revietech.ru, "Kog
+ * vyzhimayet maksimum iz GPU: 3000 tokenov/s", section "Chto takoye
+ * monokernel" (one resident program covering prefill, decode, LM-head
+ * sampling and the EOS check, no CPU return, no per-token launch); remio.ai,
+ * "Kog stawia na glebsza optymalizacje GPU...", section "Dlaczego Kog idzie
+ * glebiej" (the decode sequence lives in one persistent kernel); lehuy.net,
+ * "Kog dat toc do suy luan 3.000 token/giay...", section "Giai phap
+ * Monokernel" (launch cost removed, CPU-GPU synchronisation minimised).
+ *
+ * Work-groups hand data to each other through device buffers that are
+ * pre-filled with a NaN bit pattern; consumers poll the data words themselves
+ * until they stop being NaN, instead of counting arrivals with atomics
+ * (revietech.ru page, section "Chto takoye monokernel", the paragraph on
+ * synchronisation).  Projections at batch 1 are matrix-vector products run on
+ * the packed dot2 vector ALU instructions, not on matrix cores (revietech.ru
+ * page, section "Arkhitektura i osobennosti", first bullet, and its FAQ).
+ *
+ * Conventions shared by every entry point
+ *  - Memory.  The caller owns every device buffer: weights and the workspace.
+ *    The library never allocates or frees device memory; the opaque engine
+ *    handle (host memory) is the only object it owns.
+ *  - Pointers marked _dev are device pointers, _host are host pointers.
+ *  - Matrices are row-major [out][in] (PyTorch nn.Linear layout), elements of
+ *    the engine dtype (IEEE fp16 or bf16 as raw 16-bit words).
+ *  - Calls are synchronous on the stream given to kie_create(): they return
+ *    after the GPU work finished, so their status covers failures found by the
+ *    kernel itself (a poll that timed out).
+ *  - Threads.  An engine must be used by one host thread at a time.  Two
+ *    engines on one GPU must not run kie_prefill/kie_decode concurrently: the
+ *    persistent kernel occupies every compute unit.
+ *  - Errors.  Every call returns a kie_status; on any error no output argument
+ *    is written unless stated otherwise.
+ */
+#ifndef KIE_H
+#define KIE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  kie_status_string() gives a short English text. */
+typedef enum {
+  KIE_OK = 0,
+  KIE_ERR_ARG = -1,         /* null pointer, size or range error in arguments */
+  KIE_ERR_STATE = -2,       /* call out of order (decode before prefill ...) */
+  KIE_ERR_CAPACITY = -3,    /* position would exceed max_seq, workspace too small */
+  KIE_ERR_UNSUPPORTED = -4, /* shape the kernels do not implement */
+  KIE_ERR_HIP = -5,         /* a HIP runtime call failed (no device, launch error) */
+  KIE_ERR_TIMEOUT = -6,     /* a device-side poll exceeded its deadline */
+  KIE_ERR_ABORTED = -7      /* the kernel stopped on the engine's abort request */
+} kie_status;
+
+typedef enum { KIE_F16 = 1, KIE_BF16 = 2 } kie_dtype;
+
+/* Model shape.  Supported: head_dim in {64, 128}; n_heads a multiple of
+ * n_kv_heads; n_heads / n_kv_heads <= 8; d_model, n_heads*head_dim and d_ffn
+ * multiples of 256; vocab >= 1; max_seq >= 1. */
+typedef struct {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;     /* query heads Hq */
+  int32_t n_kv_heads;  /* key/value heads Hkv */
+  int32_t head_dim;    /* hd */
+  int32_t d_ffn;       /* SwiGLU hidden width F */
+  int32_t vocab;       /* V */
+  int32_t max_seq;     /* KV-cache capacity in positions */
+  float rms_eps;       /* RMSNorm epsilon, e.g. 1e-5 */
+  float rope_base;     /* rotary base, e.g. 10000 */
+  int32_t dtype;       /* kie_dtype of weights, KV cache and activations fed to dot2 */
+} kie_config;
+
+/* Device pointers to the weights, all of engine dtype.  The library borrows
+ * them: the caller keeps them alive and unchanged until kie_destroy() or the
+ * next kie_load_weights().  Per-layer fields point to host arrays of
+ * n_layers device pointers (the arrays are copied during the call).
+ *   tok_emb   [vocab][d_model]          lm_head   [vocab][d_model]
+ *   final_norm[d_model]
+ *   attn_norm [d_model]                 ffn_norm  [d_model]
+ *   wq [Hq*hd][d_model]   wk, wv [Hkv*hd][d_model]   wo [d_model][Hq*hd]
+ *   w_gate, w_up [d_ffn][d_model]       w_down [d_model][d_ffn]          */
+typedef struct {
+  const void* tok_emb;
+  const void* final_norm;
+  const void* lm_head;
+  const void* const* attn_norm;
+  const void* const* wq;
+  const void* const* wk;
+  const void* const* wv;
+  const void* const* wo;
+  const void* const* ffn_norm;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+} kie_weights;
+
+typedef struct kie_engine kie_engine; /* opaque, owned by the library */
+
+/* Short static text for a status code; never NULL. */
+const char* kie_status_string(kie_status s);
+
+/* Host-only check of a configuration: KIE_OK, KIE_ERR_ARG (null or a value
+ * out of range) or KIE_ERR_UNSUPPORTED.  Touches no GPU. */
+kie_status kie_config_validate(const kie_config* cfg);
+
+/* Bytes of device workspace kie_create() needs for cfg (0 if cfg is invalid).
+ * Covers the KV cache [2][n_layers][Hkv][max_seq][hd] of engine dtype, the
+ * rotary table, the NaN-initialised exchange buffers and control words.
+ * Touches no GPU. */
+size_t kie_workspace_bytes(const kie_config* cfg);
+
+/* Create an engine on the current HIP device.  workspace_dev: device buffer of
+ * ws_bytes >= kie_workspace_bytes(cfg), 256-byte aligned, owned by the caller
+ * and kept alive until kie_destroy().  hip_stream: a hipStream_t, or NULL for
+ * the default stream; every call of this engine runs on it.  Writes the rotary
+ * table into the workspace.  On success *out is a new handle. */
+kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes,
+                      void* hip_stream, kie_engine** out);
+
+/* Register the weights (device pointers, see kie_weights).  Resets the
+ * sequence: a kie_prefill() or kie_import_kv() must follow before decoding. */
+kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
+
+/* Run the prompt through the model inside the persistent kernel, one position
+ * per loop iteration with the prompt tokens fed instead of sampled ones.
+ * Starts a new sequence: the KV cache is rewritten from position 0.
+ *   prompt_host[n_prompt]: token ids in [0, vocab), 1 <= n_prompt <= max_seq.
+ *   next_token_host: receives the greedy token after the last prompt position.
+ *   logits_dev: NULL, or device float[vocab] receiving the logits of the last
+ *   prompt position.
+ * After success the engine holds pos = n_prompt and the new token pending. */
+kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prompt,
+                       int32_t* next_token_host, float* logits_dev);
+
+/* Greedy decode of up to n_steps tokens in ONE persistent kernel launch.
+ * Step i feeds the pending token at position pos+i and emits token i.  If
+ * eos_id >= 0 and a step emits eos_id, that token is written and counted and
+ * the loop stops.
+ *   tokens_host[n_steps]: receives the emitted tokens.
+ *   n_generated: receives the number of emitted tokens (<= n_steps).
+ *   logits_dev: NULL, or device float[n_steps][vocab] receiving the logits of
+ *   every executed step (parity mode; costs extra writes).
+ * Requires a prefilled sequence and pos + n_steps <= max_seq (else
+ * KIE_ERR_CAPACITY before any launch).  Repeated calls continue the sequence.
+ * On KIE_ERR_TIMEOUT or KIE_ERR_ABORTED, tokens_host and n_generated hold the
+ * steps that completed, and the sequence must be restarted by kie_prefill()
+ * or kie_import_kv(). */
+kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id, int32_t* tokens_host,
+                      int32_t* n_generated, float* logits_dev);
+
+/* Release the handle.  NULL-safe.  Frees no caller memory. */
+void kie_destroy(kie_engine* e);
+
+/* ---- sequence state: checkpoint / resume -------------------------------- */
+
+/* Replace the sequence state: positions [0, n_pos) of the KV cache are copied
+ * from k_dev and v_dev, device arrays [n_layers][Hkv][n_pos][hd] of engine
+ * dtype (keys already rotated), pos becomes n_pos and pending_token the token
+ * the next decode step feeds.  0 <= n_pos < max_seq. */
+kie_status kie_import_kv(kie_engine* e, const void* k_dev, const void* v_dev, int32_t n_pos,
+                         int32_t pending_token);
+
+/* Copy the current KV cache rows [0, pos) out to k_dev / v_dev, device arrays
+ * [n_layers][Hkv][pos][hd] sized by the caller from *n_pos_io on input (the
+ * capacity in positions); on output *n_pos_io = pos and *pending_token = the
+ * token the next decode step feeds (-1 if none). */
+kie_status kie_export_kv(kie_engine* e, void* k_dev, void* v_dev, int32_t* n_pos_io,
+                         int32_t* pending_token);
+
+/* ---- diagnostics ---------------------------------------------------------- */
+
+typedef struct {
+  int32_t grid;           /* work-groups of the persistent kernel (one per CU) */
+  int32_t block;          /* threads per work-group */
+  int32_t lds_bytes;      /* dynamic LDS per work-group */
+  int32_t cu_count;       /* compute units reported by the device */
+  int32_t attn_max_chunks;/* split-KV chunks per KV head at most */
+  int32_t pos;            /* current sequence length */
+  float last_kernel_ms;   /* duration of the last persistent launch, HIP events
+                             recorded on the engine stream around that launch */
+  int32_t last_steps;     /* loop iterations the last launch executed */
+} kie_info;
+
+kie_status kie_get_info(const kie_engine* e, kie_info* out);
+
+/* Deadline of every device-side poll, in ticks of the 100 MHz real-time
+ * counter (default 2e8 = 2 s).  A poll that exceeds it makes every
+ * work-group leave the kernel and the call return KIE_ERR_TIMEOUT.  A tiny
+ * value forces that path from the host (failure-handling tests).  0 restores
+ * the default. */
+kie_status kie_set_poll_timeout(kie_engine* e, uint64_t ticks);
+
+/* Ask the next kie_decode() to stop after abort_after_steps completed steps
+ * (-1 = never), returning KIE_ERR_ABORTED with the partial tokens.  The
+ * request is consumed by that call. */
+kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_steps);
+
+/* ---- isolated GEMV probe -------------------------------------------------- */
+
+/* y[i] = W * x[i] for i < n_vec, in ONE persistent launch of the same GEMV
+ * engine the decode kernel uses (dwordx4 weight streaming, dot2 with fp32
+ * accumulation, per-row split-K reduction inside each work-group).  W_dev
+ * [n_copies][rows][cols] of dtype: vector i uses copy i % n_copies (several
+ * copies defeat the memory-side cache).  x_dev [n_vec][cols] of dtype;
+ * y_dev [n_vec][rows] float.  cols a multiple of 256; rows >= 1.
+ * *kernel_ms receives the launch duration (HIP events) if not NULL.
+ * Runs on hip_stream (NULL = default) and synchronises it. */
+kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
+                          const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
+                          void* hip_stream, float* kernel_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIE_H */

@@ -208,6 +208,13 @@ kie_status kie_set_poll_timeout(kie_engine* e, uint64_t ticks);
  * request is consumed by that call. */
 kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_steps);
 
+/* Fault injection for failure-handling tests: work-group `wg` of the next
+ * persistent launches never publishes its end-of-step partial, so every other
+ * work-group's poll for it must expire and the call must return
+ * KIE_ERR_TIMEOUT (after the poll deadline) with every work-group having left
+ * the kernel.  -1 (default) disables it. */
+kie_status kie_set_withhold(kie_engine* e, int32_t wg);
+
 /* ---- isolated GEMV probe -------------------------------------------------- */
 
 /* y[i] = W * x[i] for i < n_vec, in ONE persistent launch of the same GEMV

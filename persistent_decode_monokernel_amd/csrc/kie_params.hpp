@@ -1,0 +1,67 @@
+// Parameters and layout shared by the host runtime and the device kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kie {
+
+constexpr int kThreads = 512;            // threads per work-group (8 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxWG = 1024;             // upper bound on the persistent grid
+constexpr int kRingSets = 3;             // exchange sets rotating over decode steps
+constexpr int kClMin = 16;               // shortest split-KV chunk (positions)
+constexpr int kAttnUnits = 256;          // target (KV head, chunk) units per layer
+constexpr int kRedCap = 4096;            // LDS floats for per-wave GEMV partial sums
+constexpr int kYCap = 1024;              // LDS floats for finished GEMV rows
+constexpr int kDepth = 16;               // weight vectors in flight per thread
+constexpr uint32_t kSent = 0xFFFFFFFFu;  // NaN pattern that marks "not written yet"
+
+// per-layer weight slots in the device pointer table
+enum : int {
+  W_ATTN_NORM = 0, W_Q, W_K, W_V, W_O, W_FFN_NORM, W_GATE, W_UP, W_DOWN, W_PER_LAYER
+};
+
+// control words
+enum : int { CTL_STATUS = 0, CTL_DONE = 1, CTL_LAST = 2, CTL_WORDS = 64 };
+
+// Word offsets of the sub-buffers of one exchange set (fp32 words).
+struct XchLayout {
+  uint64_t xmid;   // [L][d]        residual after attention
+  uint64_t xout;   // [L][d]        residual after the feed-forward block
+  uint64_t qkv;    // [L][(Hq+2Hkv)*hd] q, k, v before the rotary embedding
+  uint64_t a;      // [L][Hq*hd]    merged attention output
+  uint64_t h;      // [L][F]        silu(gate) * up
+  uint64_t arg;    // [kMaxWG][2]   per-work-group (max logit, index)
+  uint64_t att;    // [L][Hq][cmax][astride]  split-KV partials (m, l, pad, pad, o[hd])
+  uint64_t dense;  // words before att (reset wholesale)
+  uint64_t words;  // total words of one set
+};
+
+struct Params {
+  // model
+  int L, d, hq, hkv, hd, F, V, max_seq;
+  float eps;
+  int cmax, astride, cl_cap;
+  // weights (16-bit words of the engine dtype)
+  const uint16_t* tok_emb;
+  const uint16_t* final_norm;
+  const uint16_t* lm_head;
+  const uint16_t* const* lw;  // device table [L][W_PER_LAYER]
+  // workspace
+  uint16_t* kc;               // [L][Hkv][max_seq][hd]
+  uint16_t* vc;
+  const float* rope;          // [max_seq][hd/2][2] = (cos, sin)
+  uint32_t* xch;              // kRingSets exchange sets
+  XchLayout xl;
+  uint32_t* ctl;              // control words
+  int* tok_out;               // [n_steps] emitted tokens
+  float* logits;              // [n_steps][V] or [1][V] (prefill) or null
+  const int* forced;          // prompt tokens (prefill) or null
+  // launch
+  int pos0, n_steps, eos_id, in_tok, abort_after, lm_last_only, withhold_wg;
+  uint64_t timeout;           // poll deadline, ticks of the 100 MHz counter
+  // dynamic LDS layout (bytes)
+  int lds_xres, lds_xn, lds_scr, lds_misc, lds_bytes;
+};
+
+}  // namespace kie

@@ -1,0 +1,535 @@
+// Host runtime behind include/kie.h: validation, workspace layout, the rotary
+// table, weight registration, the persistent launches, status mapping.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kie.h"
+#include "kie_params.hpp"
+
+namespace kie {
+const void* monokernel_fn_f16(int group);
+const void* monokernel_fn_bf16(int group);
+const void* gemv_probe_fn(int dtype);
+hipError_t launch_fill(uint32_t* p, uint64_t n, uint32_t v, hipStream_t st);
+}  // namespace kie
+
+using namespace kie;
+
+namespace {
+
+constexpr uint64_t kDefaultTimeout = 200000000ull;  // 2 s at 100 MHz
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool pow2_between(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+// A GEMV input width the engine tiles: a power of two in [256, 4096] (rows of
+// <= 512 vectors) or a multiple of 256 up to 16384 (rows of up to 4 vectors per
+// thread).
+bool k_ok(int k) { return pow2_between(k, 256, 4096) || (k > 4096 && k <= 16384 && k % 256 == 0); }
+
+int attn_cmax(const kie_config& c) {
+  int m = kAttnUnits / c.n_kv_heads;
+  return m < 1 ? 1 : m;
+}
+
+int attn_cl_cap(const kie_config& c) {
+  const int cmax = attn_cmax(c);
+  int cl = (c.max_seq + cmax - 1) / cmax;
+  return cl < kClMin ? kClMin : cl;
+}
+
+XchLayout xch_layout(const kie_config& c) {
+  XchLayout x{};
+  const uint64_t L = c.n_layers, d = c.d_model, qd = (uint64_t)c.n_heads * c.head_dim, F = c.d_ffn;
+  uint64_t o = 0;
+  auto take = [&](uint64_t words) {
+    const uint64_t at = o;
+    o = align_up(o + words, 4);
+    return at;
+  };
+  x.xmid = take(L * d);
+  x.xout = take(L * d);
+  x.qkv = take(L * (qd + 2ull * c.n_kv_heads * c.head_dim));
+  x.a = take(L * qd);
+  x.h = take(L * F);
+  x.arg = take(2 * (uint64_t)kMaxWG);
+  x.dense = o;
+  x.att = take(L * c.n_heads * (uint64_t)attn_cmax(c) * (c.head_dim + 4));
+  x.words = align_up(o, 64);
+  return x;
+}
+
+struct Layout {
+  size_t params, rope, lw, kc, vc, xch, ctl, tok, forced, total;
+  size_t kv_plane_bytes;
+  XchLayout xl;
+};
+
+Layout make_layout(const kie_config& c) {
+  Layout y{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  y.kv_plane_bytes = (size_t)c.n_layers * c.n_kv_heads * c.max_seq * c.head_dim * 2;
+  y.xl = xch_layout(c);
+  y.params = take(sizeof(Params));
+  y.rope = take((size_t)c.max_seq * (c.head_dim / 2) * 2 * sizeof(float));
+  y.lw = take((size_t)c.n_layers * W_PER_LAYER * sizeof(void*));
+  y.kc = take(y.kv_plane_bytes);
+  y.vc = take(y.kv_plane_bytes);
+  y.xch = take((size_t)kRingSets * y.xl.words * 4);
+  y.ctl = take(CTL_WORDS * 4);
+  y.tok = take((size_t)c.max_seq * 4);
+  y.forced = take((size_t)c.max_seq * 4);
+  y.total = o;
+  return y;
+}
+
+struct LdsPlan {
+  int xres, xn, scr, misc, bytes;
+};
+
+LdsPlan lds_plan(const kie_config& c) {
+  LdsPlan p{};
+  const int qd = c.n_heads * c.head_dim;
+  int kmax = c.d_model;
+  if (qd > kmax) kmax = qd;
+  if (c.d_ffn > kmax) kmax = c.d_ffn;
+  const int G = c.n_heads / c.n_kv_heads;
+  const size_t gemv_scr = (size_t)(kRedCap + kYCap) * 4;
+  const size_t attn_scr = ((size_t)G * c.head_dim + 3 * (size_t)c.head_dim + (size_t)kWaves * G * c.head_dim + 16 +
+                           (size_t)G * attn_cl_cap(c)) * 4;
+  size_t o = 0;
+  p.xres = 0;
+  o = align_up((size_t)c.d_model * 4, 16);
+  p.xn = (int)o;
+  o = align_up(o + (size_t)kmax * 2, 16);
+  p.scr = (int)o;
+  o = align_up(o + (gemv_scr > attn_scr ? gemv_scr : attn_scr), 16);
+  p.misc = (int)o;
+  o += 128 * 4;
+  p.bytes = (int)o;
+  return p;
+}
+
+const void* monokernel_fn(const kie_config& c) {
+  const int G = c.n_heads / c.n_kv_heads;
+  return c.dtype == KIE_F16 ? monokernel_fn_f16(G) : monokernel_fn_bf16(G);
+}
+
+}  // namespace
+
+struct kie_engine {
+  kie_config cfg{};
+  Layout lay{};
+  LdsPlan lds{};
+  int device = 0;
+  int cu_count = 0;
+  int grid = 0;
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  bool have_weights = false;
+  const uint16_t* tok_emb = nullptr;
+  const uint16_t* final_norm = nullptr;
+  const uint16_t* lm_head = nullptr;
+  bool have_seq = false;
+  int pos = 0;
+  int pending = -1;
+  uint64_t timeout = kDefaultTimeout;
+  int abort_after = -1;
+  int withhold_wg = -1;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  float last_ms = 0.f;
+  int last_steps = 0;
+  Params params_host{};
+};
+
+extern "C" const char* kie_status_string(kie_status s) {
+  switch (s) {
+    case KIE_OK: return "ok";
+    case KIE_ERR_ARG: return "invalid argument";
+    case KIE_ERR_STATE: return "call out of order";
+    case KIE_ERR_CAPACITY: return "capacity exceeded";
+    case KIE_ERR_UNSUPPORTED: return "unsupported shape";
+    case KIE_ERR_HIP: return "HIP runtime error";
+    case KIE_ERR_TIMEOUT: return "device poll timed out";
+    case KIE_ERR_ABORTED: return "aborted on request";
+  }
+  return "unknown status";
+}
+
+extern "C" kie_status kie_config_validate(const kie_config* c) {
+  if (!c) return KIE_ERR_ARG;
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 1 ||
+      c->d_ffn < 1 || c->vocab < 1 || c->max_seq < 1)
+    return KIE_ERR_ARG;
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps) || !(c->rope_base > 1.f) || !std::isfinite(c->rope_base))
+    return KIE_ERR_ARG;
+  if (c->dtype != KIE_F16 && c->dtype != KIE_BF16) return KIE_ERR_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return KIE_ERR_UNSUPPORTED;
+  if (c->n_heads % c->n_kv_heads != 0) return KIE_ERR_UNSUPPORTED;
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KIE_ERR_UNSUPPORTED;
+  if (c->n_kv_heads > kAttnUnits) return KIE_ERR_UNSUPPORTED;
+  if (!k_ok(c->d_model) || !k_ok(c->n_heads * c->head_dim) || !k_ok(c->d_ffn)) return KIE_ERR_UNSUPPORTED;
+  if (attn_cl_cap(*c) > 2048) return KIE_ERR_UNSUPPORTED;  // split-KV chunk beyond the LDS score buffer
+  if ((long long)c->vocab * c->d_model >= (1ll << 40)) return KIE_ERR_UNSUPPORTED;
+  if (lds_plan(*c).bytes > 160 * 1024) return KIE_ERR_UNSUPPORTED;
+  return KIE_OK;
+}
+
+extern "C" size_t kie_workspace_bytes(const kie_config* c) {
+  if (kie_config_validate(c) != KIE_OK) return 0;
+  return make_layout(*c).total;
+}
+
+static kie_status hip_fail(hipError_t e, const char* what) {
+  if (getenv("KIE_VERBOSE")) fprintf(stderr, "kie: %s failed: %s\n", what, hipGetErrorString(e));
+  return KIE_ERR_HIP;
+}
+
+#define KIE_HIP(call)                                      \
+  do {                                                     \
+    hipError_t e_ = (call);                                \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);      \
+  } while (0)
+
+extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes, void* hip_stream,
+                                 kie_engine** out) {
+  if (!out) return KIE_ERR_ARG;
+  *out = nullptr;
+  const kie_status v = kie_config_validate(cfg);
+  if (v != KIE_OK) return v;
+  if (!workspace_dev || (reinterpret_cast<uintptr_t>(workspace_dev) & 255) != 0) return KIE_ERR_ARG;
+  const Layout lay = make_layout(*cfg);
+  if (ws_bytes < lay.total) return KIE_ERR_CAPACITY;
+
+  int dev = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  KIE_HIP(hipGetDeviceProperties(&prop, dev));
+  int coop = 0;
+  KIE_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+  if (!coop) return KIE_ERR_UNSUPPORTED;
+
+  kie_engine* e = new (std::nothrow) kie_engine();
+  if (!e) return KIE_ERR_ARG;
+  e->cfg = *cfg;
+  e->lay = lay;
+  e->lds = lds_plan(*cfg);
+  e->device = dev;
+  e->cu_count = prop.multiProcessorCount;
+  e->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  e->ws = reinterpret_cast<char*>(workspace_dev);
+
+  const void* fn = monokernel_fn(*cfg);
+  hipError_t he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, e->lds.bytes);
+  int per_cu = 0;
+  if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, e->lds.bytes);
+  if (he != hipSuccess || per_cu < 1) {
+    delete e;
+    return he != hipSuccess ? hip_fail(he, "occupancy") : KIE_ERR_UNSUPPORTED;
+  }
+  // One resident work-group per compute unit.
+  e->grid = e->cu_count < kMaxWG ? e->cu_count : kMaxWG;
+
+  // Rotary table, built in double precision: angle(p, i) = p * base^(-2i/hd).
+  const int half = cfg->head_dim / 2;
+  std::vector<float> rope((size_t)cfg->max_seq * half * 2);
+  for (int p = 0; p < cfg->max_seq; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)cfg->rope_base, -2.0 * i / cfg->head_dim);
+      rope[((size_t)p * half + i) * 2] = (float)std::cos(ang);
+      rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
+    }
+  he = hipMemcpyAsync(e->ws + lay.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice, e->stream);
+  if (he == hipSuccess) he = launch_fill(reinterpret_cast<uint32_t*>(e->ws + lay.ctl), CTL_WORDS, 0u, e->stream);
+  if (he == hipSuccess) he = hipEventCreate(&e->ev0);
+  if (he == hipSuccess) he = hipEventCreate(&e->ev1);
+  if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+  if (he != hipSuccess) {
+    kie_destroy(e);
+    return hip_fail(he, "create");
+  }
+  *out = e;
+  return KIE_OK;
+}
+
+extern "C" void kie_destroy(kie_engine* e) {
+  if (!e) return;
+  if (e->ev0) (void)hipEventDestroy(e->ev0);
+  if (e->ev1) (void)hipEventDestroy(e->ev1);
+  delete e;
+}
+
+extern "C" kie_status kie_load_weights(kie_engine* e, const kie_weights* w) {
+  if (!e || !w) return KIE_ERR_ARG;
+  const int L = e->cfg.n_layers;
+  if (!w->tok_emb || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->ffn_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return KIE_ERR_ARG;
+  std::vector<const void*> tab((size_t)L * W_PER_LAYER);
+  for (int l = 0; l < L; ++l) {
+    const void* p[W_PER_LAYER] = {w->attn_norm[l], w->wq[l], w->wk[l], w->wv[l], w->wo[l],
+                                  w->ffn_norm[l], w->w_gate[l], w->w_up[l], w->w_down[l]};
+    for (int k = 0; k < W_PER_LAYER; ++k) {
+      if (!p[k] || (reinterpret_cast<uintptr_t>(p[k]) & 15) != 0) return KIE_ERR_ARG;
+      tab[(size_t)l * W_PER_LAYER + k] = p[k];
+    }
+  }
+  for (const void* p : {w->tok_emb, w->final_norm, w->lm_head})
+    if ((reinterpret_cast<uintptr_t>(p) & 15) != 0) return KIE_ERR_ARG;
+  KIE_HIP(hipMemcpyAsync(e->ws + e->lay.lw, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice, e->stream));
+  KIE_HIP(hipStreamSynchronize(e->stream));
+  e->tok_emb = reinterpret_cast<const uint16_t*>(w->tok_emb);
+  e->final_norm = reinterpret_cast<const uint16_t*>(w->final_norm);
+  e->lm_head = reinterpret_cast<const uint16_t*>(w->lm_head);
+  e->have_weights = true;
+  e->have_seq = false;
+  e->pos = 0;
+  e->pending = -1;
+  return KIE_OK;
+}
+
+static Params base_params(const kie_engine* e) {
+  const kie_config& c = e->cfg;
+  Params P{};
+  P.L = c.n_layers; P.d = c.d_model; P.hq = c.n_heads; P.hkv = c.n_kv_heads; P.hd = c.head_dim;
+  P.F = c.d_ffn; P.V = c.vocab; P.max_seq = c.max_seq; P.eps = c.rms_eps;
+  P.cmax = attn_cmax(c); P.astride = c.head_dim + 4; P.cl_cap = attn_cl_cap(c);
+  P.tok_emb = e->tok_emb; P.final_norm = e->final_norm; P.lm_head = e->lm_head;
+  P.lw = reinterpret_cast<const uint16_t* const*>(e->ws + e->lay.lw);
+  P.kc = reinterpret_cast<uint16_t*>(e->ws + e->lay.kc);
+  P.vc = reinterpret_cast<uint16_t*>(e->ws + e->lay.vc);
+  P.rope = reinterpret_cast<const float*>(e->ws + e->lay.rope);
+  P.xch = reinterpret_cast<uint32_t*>(e->ws + e->lay.xch);
+  P.xl = e->lay.xl;
+  P.ctl = reinterpret_cast<uint32_t*>(e->ws + e->lay.ctl);
+  P.tok_out = reinterpret_cast<int*>(e->ws + e->lay.tok);
+  P.abort_after = -1;
+  P.withhold_wg = e->withhold_wg;
+  P.timeout = e->timeout;
+  P.lds_xres = e->lds.xres; P.lds_xn = e->lds.xn; P.lds_scr = e->lds.scr; P.lds_misc = e->lds.misc;
+  P.lds_bytes = e->lds.bytes;
+  return P;
+}
+
+// Reset control words and exchange sets, launch the persistent kernel, wait,
+// and read back status / steps done / last token.
+static kie_status run_persistent(kie_engine* e, Params& P, int* done, int* last) {
+  KIE_HIP(launch_fill(P.ctl, CTL_WORDS, 0u, e->stream));
+  KIE_HIP(launch_fill(P.xch, (uint64_t)kRingSets * P.xl.words, kSent, e->stream));
+  // The kernel reads its parameters from the workspace (scalar loads).
+  Params* dev_params = reinterpret_cast<Params*>(e->ws + e->lay.params);
+  e->params_host = P;  // stays valid until the copy below has run (the call synchronises)
+  KIE_HIP(hipMemcpyAsync(dev_params, &e->params_host, sizeof(Params), hipMemcpyHostToDevice, e->stream));
+  void* args[] = {&dev_params};
+  KIE_HIP(hipEventRecord(e->ev0, e->stream));
+  KIE_HIP(hipLaunchCooperativeKernel(monokernel_fn(e->cfg), dim3(e->grid), dim3(kThreads), args,
+                                     (unsigned)e->lds.bytes, e->stream));
+  KIE_HIP(hipEventRecord(e->ev1, e->stream));
+  uint32_t ctl[4] = {0, 0, 0, 0};
+  KIE_HIP(hipMemcpyAsync(ctl, P.ctl, sizeof(ctl), hipMemcpyDeviceToHost, e->stream));
+  KIE_HIP(hipStreamSynchronize(e->stream));
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, e->ev0, e->ev1) == hipSuccess) e->last_ms = ms;
+  *done = (int)ctl[CTL_DONE];
+  *last = (int)ctl[CTL_LAST];
+  e->last_steps = *done;
+  const int32_t st = (int32_t)ctl[CTL_STATUS];
+  if (st == 0) return KIE_OK;
+  if (st == KIE_ERR_ABORTED) return KIE_ERR_ABORTED;
+  return KIE_ERR_TIMEOUT;
+}
+
+extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prompt,
+                                  int32_t* next_token_host, float* logits_dev) {
+  if (!e || !prompt_host || !next_token_host) return KIE_ERR_ARG;
+  if (!e->have_weights) return KIE_ERR_STATE;
+  if (n_prompt < 1) return KIE_ERR_ARG;
+  if (n_prompt > e->cfg.max_seq) return KIE_ERR_CAPACITY;
+  for (int i = 0; i < n_prompt; ++i)
+    if (prompt_host[i] < 0 || prompt_host[i] >= e->cfg.vocab) return KIE_ERR_ARG;
+  e->have_seq = false;
+  Params P = base_params(e);
+  KIE_HIP(hipMemcpyAsync(e->ws + e->lay.forced, prompt_host, (size_t)n_prompt * 4, hipMemcpyHostToDevice, e->stream));
+  P.forced = reinterpret_cast<const int*>(e->ws + e->lay.forced);
+  P.pos0 = 0;
+  P.n_steps = n_prompt;
+  P.eos_id = -1;
+  P.in_tok = prompt_host[0];
+  P.lm_last_only = 1;
+  P.logits = logits_dev;
+  int done = 0, last = 0;
+  const kie_status st = run_persistent(e, P, &done, &last);
+  if (st != KIE_OK) return st;
+  if (done != n_prompt) return KIE_ERR_TIMEOUT;
+  e->pos = n_prompt;
+  e->pending = last;
+  e->have_seq = true;
+  *next_token_host = last;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id, int32_t* tokens_host,
+                                 int32_t* n_generated, float* logits_dev) {
+  if (!e || !n_generated || (n_steps > 0 && !tokens_host) || n_steps < 0) return KIE_ERR_ARG;
+  if (eos_id >= e->cfg.vocab) return KIE_ERR_ARG;
+  if (!e->have_weights || !e->have_seq) return KIE_ERR_STATE;
+  if ((long long)e->pos + n_steps > e->cfg.max_seq) return KIE_ERR_CAPACITY;
+  const int abort_after = e->abort_after;
+  e->abort_after = -1;
+  if (n_steps == 0) {
+    *n_generated = 0;
+    return KIE_OK;
+  }
+  Params P = base_params(e);
+  P.pos0 = e->pos;
+  P.n_steps = n_steps;
+  P.eos_id = eos_id < 0 ? -1 : eos_id;
+  P.in_tok = e->pending;
+  P.lm_last_only = 0;
+  P.logits = logits_dev;
+  P.abort_after = abort_after;
+  int done = 0, last = 0;
+  const kie_status st = run_persistent(e, P, &done, &last);
+  if (st == KIE_ERR_HIP) return st;
+  if (done > 0) {
+    KIE_HIP(hipMemcpy(tokens_host, P.tok_out, (size_t)done * 4, hipMemcpyDeviceToHost));
+  }
+  *n_generated = done;
+  if (st == KIE_OK || st == KIE_ERR_ABORTED) {
+    e->pos += done;
+    if (done > 0) e->pending = last;
+  } else {
+    e->have_seq = false;  // a poll expired mid-step: the cache row of that step may be partial
+  }
+  return st;
+}
+
+extern "C" kie_status kie_import_kv(kie_engine* e, const void* k_dev, const void* v_dev, int32_t n_pos,
+                                    int32_t pending_token) {
+  if (!e) return KIE_ERR_ARG;
+  if (!e->have_weights) return KIE_ERR_STATE;
+  if (n_pos < 0 || pending_token < 0 || pending_token >= e->cfg.vocab) return KIE_ERR_ARG;
+  if (n_pos >= e->cfg.max_seq) return KIE_ERR_CAPACITY;
+  if (n_pos > 0 && (!k_dev || !v_dev)) return KIE_ERR_ARG;
+  const kie_config& c = e->cfg;
+  uint16_t* kc = reinterpret_cast<uint16_t*>(e->ws + e->lay.kc);
+  uint16_t* vc = reinterpret_cast<uint16_t*>(e->ws + e->lay.vc);
+  if (n_pos > 0) {
+    const size_t row = (size_t)n_pos * c.head_dim * 2, pitch = (size_t)c.max_seq * c.head_dim * 2;
+    const size_t planes = (size_t)c.n_layers * c.n_kv_heads;
+    KIE_HIP(hipMemcpy2DAsync(kc, pitch, k_dev, row, row, planes, hipMemcpyDeviceToDevice, e->stream));
+    KIE_HIP(hipMemcpy2DAsync(vc, pitch, v_dev, row, row, planes, hipMemcpyDeviceToDevice, e->stream));
+  }
+  KIE_HIP(hipStreamSynchronize(e->stream));
+  e->pos = n_pos;
+  e->pending = pending_token;
+  e->have_seq = true;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_export_kv(kie_engine* e, void* k_dev, void* v_dev, int32_t* n_pos_io,
+                                    int32_t* pending_token) {
+  if (!e || !n_pos_io || !pending_token) return KIE_ERR_ARG;
+  if (!e->have_seq) return KIE_ERR_STATE;
+  if (*n_pos_io < e->pos) return KIE_ERR_CAPACITY;
+  if (e->pos > 0 && (!k_dev || !v_dev)) return KIE_ERR_ARG;
+  const kie_config& c = e->cfg;
+  if (e->pos > 0) {
+    const size_t row = (size_t)e->pos * c.head_dim * 2, pitch = (size_t)c.max_seq * c.head_dim * 2;
+    const size_t planes = (size_t)c.n_layers * c.n_kv_heads;
+    KIE_HIP(hipMemcpy2DAsync(k_dev, row, e->ws + e->lay.kc, pitch, row, planes, hipMemcpyDeviceToDevice, e->stream));
+    KIE_HIP(hipMemcpy2DAsync(v_dev, row, e->ws + e->lay.vc, pitch, row, planes, hipMemcpyDeviceToDevice, e->stream));
+    KIE_HIP(hipStreamSynchronize(e->stream));
+  }
+  *n_pos_io = e->pos;
+  *pending_token = e->pending;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_get_info(const kie_engine* e, kie_info* out) {
+  if (!e || !out) return KIE_ERR_ARG;
+  out->grid = e->grid;
+  out->block = kThreads;
+  out->lds_bytes = e->lds.bytes;
+  out->cu_count = e->cu_count;
+  out->attn_max_chunks = attn_cmax(e->cfg);
+  out->pos = e->pos;
+  out->last_kernel_ms = e->last_ms;
+  out->last_steps = e->last_steps;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_poll_timeout(kie_engine* e, uint64_t ticks) {
+  if (!e) return KIE_ERR_ARG;
+  e->timeout = ticks ? ticks : kDefaultTimeout;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_steps) {
+  if (!e || abort_after_steps < -1) return KIE_ERR_ARG;
+  e->abort_after = abort_after_steps;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_withhold(kie_engine* e, int32_t wg) {
+  if (!e || wg < -1) return KIE_ERR_ARG;
+  e->withhold_wg = wg;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
+                                     const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
+                                     void* hip_stream, float* kernel_ms) {
+  if (!W_dev || !x_dev || !y_dev || rows < 1 || n_copies < 1 || n_vec < 0) return KIE_ERR_ARG;
+  if (dtype != KIE_F16 && dtype != KIE_BF16) return KIE_ERR_ARG;
+  if (!k_ok(cols)) return KIE_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(W_dev) & 15) || (reinterpret_cast<uintptr_t>(x_dev) & 15)) return KIE_ERR_ARG;
+  if (n_vec == 0) {
+    if (kernel_ms) *kernel_ms = 0.f;
+    return KIE_OK;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  int dev = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  KIE_HIP(hipGetDeviceProperties(&prop, dev));
+  int grid = prop.multiProcessorCount;
+  if (grid > rows) grid = rows;
+  const size_t lds = (size_t)cols * 2 + (size_t)(kRedCap + kYCap) * 4;
+  const int max_rows = (rows + grid - 1) / grid;
+  const int vpr = cols / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
+  if ((long long)max_rows * nwr > kRedCap || max_rows > kYCap) return KIE_ERR_UNSUPPORTED;
+  const void* fn = gemv_probe_fn(dtype);
+  KIE_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  hipEvent_t a, b;
+  KIE_HIP(hipEventCreate(&a));
+  KIE_HIP(hipEventCreate(&b));
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(W_dev);
+  const uint16_t* x = reinterpret_cast<const uint16_t*>(x_dev);
+  int r = rows, c = cols, nc = n_copies, nv = n_vec;
+  void* args[] = {&W, &r, &c, &nc, &x, &y_dev, &nv};
+  hipError_t he = hipEventRecord(a, st);
+  if (he == hipSuccess) he = hipLaunchKernel(fn, dim3(grid), dim3(kThreads), args, lds, st);
+  if (he == hipSuccess) he = hipEventRecord(b, st);
+  if (he == hipSuccess) he = hipStreamSynchronize(st);
+  float ms = 0.f;
+  if (he == hipSuccess) he = hipEventElapsedTime(&ms, a, b);
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  if (he != hipSuccess) return hip_fail(he, "gemv probe");
+  if (kernel_ms) *kernel_ms = ms;
+  return KIE_OK;
+}

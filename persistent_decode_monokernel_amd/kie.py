@@ -1,0 +1,260 @@
+"""ctypes binding of libkie.so (include/kie.h): argument marshalling only.
+
+Every step of the decode path runs in the HIP library; PyTorch only provides
+device memory (weights, workspace, logits) and the stream.  Importing this
+module does not load the library; the first call does, and raises if the
+library is missing (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkie.so")
+
+KIE_OK = 0
+KIE_ERR_ARG = -1
+KIE_ERR_STATE = -2
+KIE_ERR_CAPACITY = -3
+KIE_ERR_UNSUPPORTED = -4
+KIE_ERR_HIP = -5
+KIE_ERR_TIMEOUT = -6
+KIE_ERR_ABORTED = -7
+KIE_F16 = 1
+KIE_BF16 = 2
+
+
+class KieError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+class kie_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ffn", ctypes.c_int32),
+        ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+        ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class kie_weights(ctypes.Structure):
+    _fields_ = [
+        ("tok_emb", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+        ("attn_norm", _PP), ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP),
+        ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP),
+    ]
+
+
+class kie_info(ctypes.Structure):
+    _fields_ = [
+        ("grid", ctypes.c_int32), ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+        ("cu_count", ctypes.c_int32), ("attn_max_chunks", ctypes.c_int32), ("pos", ctypes.c_int32),
+        ("last_kernel_ms", ctypes.c_float), ("last_steps", ctypes.c_int32),
+    ]
+
+
+# name -> (restype, argtypes); mirrors include/kie.h
+SIGNATURES = {
+    "kie_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "kie_config_validate": (ctypes.c_int, [ctypes.POINTER(kie_config)]),
+    "kie_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kie_config)]),
+    "kie_create": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.POINTER(ctypes.c_void_p)]),
+    "kie_load_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kie_weights)]),
+    "kie_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                   ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
+    "kie_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
+    "kie_destroy": (None, [ctypes.c_void_p]),
+    "kie_import_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.c_int32]),
+    "kie_export_kv": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]),
+    "kie_get_info": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kie_info)]),
+    "kie_set_poll_timeout": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64]),
+    "kie_set_abort_after": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_withhold": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_gemv_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libkie.so (once).  Raises if it was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m persistent_decode_monokernel_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().kie_status_string(int(s)).decode()
+
+
+def _check(status: int, what: str):
+    if status != KIE_OK:
+        raise KieError(status, what)
+
+
+def make_config(shape, max_seq: int) -> kie_config:
+    """kie_config from a ModelShape-like object (n_layers, d_model, ... dtype)."""
+    return kie_config(shape.n_layers, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
+                      shape.d_ffn, shape.vocab, max_seq, shape.rms_eps, shape.rope_base, shape.dtype)
+
+
+def validate(cfg: kie_config) -> int:
+    return lib().kie_config_validate(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg: kie_config) -> int:
+    return lib().kie_workspace_bytes(ctypes.byref(cfg))
+
+
+def _dptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+class Engine:
+    """One decode engine: workspace (torch uint8 tensor), borrowed weights.
+
+    Calls are synchronous on the engine stream (torch's current stream at
+    construction unless given).
+    """
+
+    def __init__(self, shape, max_seq: int, device="cuda", stream=None):
+        self.shape = shape
+        self.cfg = make_config(shape, max_seq)
+        self.device = torch.device(device)
+        nbytes = workspace_bytes(self.cfg)
+        if nbytes == 0:
+            raise KieError(validate(self.cfg), "kie_workspace_bytes")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib().kie_create(ctypes.byref(self.cfg), ctypes.c_void_p(_dptr(self.workspace)), nbytes,
+                                    ctypes.c_void_p(_stream_handle(self.stream)), ctypes.byref(h)), "kie_create")
+        self._h = h
+        self._weights = None
+
+    # ---- lifecycle
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().kie_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def load_weights(self, w: Dict[str, object]):
+        """w: dict from synth.make_weights (device tensors of the engine dtype)."""
+        layers = w["layers"]
+        L = len(layers)
+        arrs = {}
+        keep: List[torch.Tensor] = [w["tok_emb"], w["final_norm"], w["lm_head"]]
+        for key in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down"):
+            ts = [lw[key].contiguous() for lw in layers]
+            keep.extend(ts)
+            arrs[key] = (ctypes.c_void_p * L)(*[_dptr(t) for t in ts])
+        kw = kie_weights(_dptr(w["tok_emb"]), _dptr(w["final_norm"]), _dptr(w["lm_head"]),
+                         *[ctypes.cast(arrs[k], _PP) for k in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm",
+                                                               "w_gate", "w_up", "w_down")])
+        _check(lib().kie_load_weights(self._h, ctypes.byref(kw)), "kie_load_weights")
+        self._weights = keep  # borrowed by the library: keep alive
+
+    def prefill(self, prompt: Sequence[int], want_logits: bool = False) -> Tuple[int, Optional[torch.Tensor]]:
+        p = (ctypes.c_int32 * len(prompt))(*[int(x) for x in prompt])
+        tok = ctypes.c_int32(-1)
+        lg = torch.empty(self.cfg.vocab, dtype=torch.float32, device=self.device) if want_logits else None
+        st = lib().kie_prefill(self._h, p, len(prompt), ctypes.byref(tok),
+                               ctypes.c_void_p(_dptr(lg)) if lg is not None else None)
+        _check(st, "kie_prefill")
+        return tok.value, lg
+
+    def decode(self, n_steps: int, eos_id: int = -1, want_logits: bool = False, raise_on_error: bool = True):
+        """Returns (tokens, logits [n][V] or None, status)."""
+        toks = (ctypes.c_int32 * max(1, n_steps))()
+        n = ctypes.c_int32(0)
+        lg = (torch.empty((max(1, n_steps), self.cfg.vocab), dtype=torch.float32, device=self.device)
+              if want_logits else None)
+        st = lib().kie_decode(self._h, n_steps, eos_id, toks, ctypes.byref(n),
+                              ctypes.c_void_p(_dptr(lg)) if lg is not None else None)
+        if raise_on_error:
+            _check(st, "kie_decode")
+        out = [toks[i] for i in range(n.value)]
+        return out, (lg[: n.value] if lg is not None else None), st
+
+    def import_kv(self, k: torch.Tensor, v: torch.Tensor, pending: int):
+        n_pos = int(k.shape[2])
+        k = k.contiguous()
+        v = v.contiguous()
+        _check(lib().kie_import_kv(self._h, ctypes.c_void_p(_dptr(k)), ctypes.c_void_p(_dptr(v)), n_pos,
+                                   int(pending)), "kie_import_kv")
+
+    def export_kv(self):
+        s = self.shape
+        cap = self.info().pos
+        k = torch.empty((s.n_layers, s.n_kv_heads, max(cap, 1), s.head_dim), dtype=s.torch_dtype,
+                        device=self.device)
+        v = torch.empty_like(k)
+        n = ctypes.c_int32(max(cap, 1))
+        pend = ctypes.c_int32(-1)
+        _check(lib().kie_export_kv(self._h, ctypes.c_void_p(_dptr(k)), ctypes.c_void_p(_dptr(v)),
+                                   ctypes.byref(n), ctypes.byref(pend)), "kie_export_kv")
+        return k[:, :, : n.value], v[:, :, : n.value], pend.value
+
+    def info(self) -> kie_info:
+        i = kie_info()
+        _check(lib().kie_get_info(self._h, ctypes.byref(i)), "kie_get_info")
+        return i
+
+    def set_poll_timeout(self, ticks: int):
+        _check(lib().kie_set_poll_timeout(self._h, int(ticks)), "kie_set_poll_timeout")
+
+    def set_abort_after(self, steps: int):
+        _check(lib().kie_set_abort_after(self._h, int(steps)), "kie_set_abort_after")
+
+    def set_withhold(self, wg: int):
+        _check(lib().kie_set_withhold(self._h, int(wg)), "kie_set_withhold")
+
+
+def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None) -> Tuple[torch.Tensor, float]:
+    """y[i] = W[i % n_copies] @ x[i] in one persistent launch.  Returns (y fp32, kernel ms)."""
+    assert W.dim() == 3 and x.dim() == 2 and W.shape[2] == x.shape[1]
+    n_copies, rows, cols = W.shape
+    dtype = KIE_F16 if W.dtype == torch.float16 else KIE_BF16
+    y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=W.device)
+    ms = ctypes.c_float(0)
+    _check(lib().kie_gemv_probe(ctypes.c_void_p(_dptr(W)), rows, cols, n_copies, ctypes.c_void_p(_dptr(x)),
+                                ctypes.c_void_p(_dptr(y)), x.shape[0], dtype,
+                                ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(ms)), "kie_gemv_probe")
+    return y, ms.value

@@ -215,6 +215,30 @@ kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_steps);
  * the kernel.  -1 (default) disables it. */
 kie_status kie_set_withhold(kie_engine* e, int32_t wg);
 
+/* Per-token timeline.  kie_trace_words(e) = uint64 words a trace buffer
+ * needs: (n_layers*6 + 2) slots x grid work-groups x 3 stamps.  After
+ * kie_set_trace(e, buf, step), every persistent launch of the engine stamps
+ * loop iteration `step` (relative to the launch) into buf: for slot s (layer l
+ * stage k at s = 6*l + k with k = 0 QKV, 1 attention, 2 merge, 3 Wo,
+ * 4 gate/up, 5 down; then s = 6*L LM head, 6*L + 1 token gather) and
+ * work-group w, buf[(s*grid + w)*3 + j] holds the 100 MHz real-time counter at
+ * stage entry (j = 0), when the stage's input had arrived (j = 1; equals the
+ * exit stamp position for the merge stage, which has no separate wait) and at
+ * stage exit (j = 2).  Thread 0 of each work-group writes them; other entries
+ * are left untouched.  buf = NULL turns tracing off (the default). */
+size_t kie_trace_words(const kie_engine* e);
+kie_status kie_set_trace(kie_engine* e, uint64_t* trace_dev, int32_t step);
+
+/* Host-only self-check of the weight-stream tiling for cfg on `grid`
+ * work-groups (no GPU): every 16-byte vector each thread of each GEMV stage
+ * (QKV, Wo, gate/up, down, LM head) loads -- including the vectors the
+ * previous stage prefetches -- lies inside its weight matrix, in-range
+ * vectors are exactly the (row, column) the stage owns, and with full != 0
+ * every vector of every matrix is loaded exactly once by the grid (else a
+ * sample of work-groups is checked).  KIE_OK, or KIE_ERR_UNSUPPORTED on the
+ * first violation (described on stderr when KIE_VERBOSE is set). */
+kie_status kie_check_tiling(const kie_config* cfg, int32_t grid, int32_t full);
+
 /* ---- isolated GEMV probe -------------------------------------------------- */
 
 /* y[i] = W * x[i] for i < n_vec, in ONE persistent launch of the same GEMV

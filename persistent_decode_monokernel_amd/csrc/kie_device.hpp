@@ -197,8 +197,10 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
 
 // Weight stream load: one 16-byte vector per lane (global_load_dwordx4).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Non-temporal: streamed data (weights, KV rows) is not reused within a step,
+// and the streaming hint measurably raises read bandwidth on this GPU.
 __device__ __forceinline__ uint4 ldw(const uint16_t* p) {
-  const u32x4_t v = *(const KIE_GLOBAL u32x4_t*)p;
+  const u32x4_t v = __builtin_nontemporal_load((const KIE_GLOBAL u32x4_t*)p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 

@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include "kie_device.hpp"
+#include "kie_tiling.hpp"
 
 #define KIE_INLINE __attribute__((always_inline))
 
@@ -47,6 +48,11 @@ template <class T>
 __device__ __forceinline__ T* opaque_s(T* p) {
   asm volatile("" : "+s"(p));
   return p;
+}
+
+// Timeline stamp (thread 0 of the work-group; only on the traced step).
+__device__ __forceinline__ void stamp(uint64_t* tr, int slot, int k, int t) {
+  if (tr && t == 0) tr[((size_t)slot * gridDim.x + blockIdx.x) * 3 + k] = __builtin_amdgcn_s_memrealtime();
 }
 
 // ---------------------------------------------------------------------------
@@ -106,33 +112,68 @@ __device__ __forceinline__ float block_sum(float v, float* misc, int t) {
 // ---------------------------------------------------------------------------
 // Input preparation
 // ---------------------------------------------------------------------------
-// Poll n fp32 words (n even) of an exchange buffer into LDS as fp32.
-__device__ __forceinline__ bool poll_f32(const uint32_t* src, int n, float* dst, const Watch& w, int t) {
+// Batched poll of nw 8-byte exchange words src[2i..2i+1], i < nw, spread over
+// the work-group (word i on thread i % 512).  Each thread issues the loads of
+// up to kPollBatch words at once and waits once, then re-polls only the words
+// that were not written yet, so a vector costs about one memory round trip
+// instead of one per word.  store(i, v) receives every word once.  Ends with a
+// barrier; false if a poll expired.
+constexpr int kPollBatch = 8;
+template <class Ready, class Store>
+__device__ __forceinline__ bool poll_words(const uint32_t* src, int nw, const Watch& w, int t, Ready ready,
+                                           Store store) {
   bool ok = true;
-  for (int i = t; i < (n >> 1); i += kThreads) {
-    uint64_t v = 0;
-    if (ok && poll64(src + 2 * i, v, w, Ready32x2{})) {
-      dst[2 * i] = lo_f(v);
-      dst[2 * i + 1] = hi_f(v);
-    } else {
-      ok = false;
+  for (int base = t; base < nw && ok; base += kPollBatch * kThreads) {
+    uint64_t v[kPollBatch];
+    uint32_t pending = 0;
+#pragma unroll
+    for (int k = 0; k < kPollBatch; ++k) {
+      const int i = base + k * kThreads;
+      if (i < nw) {
+        v[k] = xld64(src + 2 * (size_t)i);
+        pending |= 1u << k;
+      }
+    }
+    uint64_t t0 = 0;
+    int n = 0;
+    for (;;) {
+      uint32_t again = 0;
+#pragma unroll
+      for (int k = 0; k < kPollBatch; ++k) {
+        if (pending & (1u << k)) {
+          if (ready(v[k])) store(base + k * kThreads, v[k]);
+          else again |= 1u << k;
+        }
+      }
+      if (!again) break;
+      if (t0 == 0) {
+        t0 = __builtin_amdgcn_s_memrealtime();
+      } else if (w.expired(t0, n)) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int k = 0; k < kPollBatch; ++k)
+        if (again & (1u << k)) v[k] = xld64(src + 2 * (size_t)(base + k * kThreads));
+      pending = again;
     }
   }
   return !any_failed(!ok);
 }
+// Poll n fp32 words (n even) of an exchange buffer into LDS as fp32.
+__device__ __forceinline__ bool poll_f32(const uint32_t* src, int n, float* dst, const Watch& w, int t) {
+  return poll_words(src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) {
+    dst[2 * i] = lo_f(v);
+    dst[2 * i + 1] = hi_f(v);
+  });
+}
 // Poll n fp32 words into LDS as 16-bit activations.
 template <int DT>
 __device__ __forceinline__ bool poll_to16(const uint32_t* src, int n, uint16_t* dst, const Watch& w, int t) {
-  bool ok = true;
-  for (int i = t; i < (n >> 1); i += kThreads) {
-    uint64_t v = 0;
-    if (ok && poll64(src + 2 * i, v, w, Ready32x2{})) {
-      reinterpret_cast<uint32_t*>(dst)[i] = pack16<DT>(lo_f(v), hi_f(v));
-    } else {
-      ok = false;
-    }
-  }
-  return !any_failed(!ok);
+  return poll_words(src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) {
+    reinterpret_cast<uint32_t*>(dst)[i] = pack16<DT>(lo_f(v), hi_f(v));
+  });
 }
 // xn = RMSNorm(x) * g, rounded to 16 bits.  Ends with a barrier.
 template <int DT>
@@ -149,7 +190,7 @@ __device__ __forceinline__ void rmsnorm_to16(const float* x, const uint16_t* g, 
 // ---------------------------------------------------------------------------
 // GEMV engine.
 //
-// A work-group owns `nrows` rows of K columns (row pointers from rowptr(r)).
+// A work-group owns `nrows` rows of K columns (StagePlan, kie_tiling.hpp).
 // The rows are read as 16-byte vectors (8 elements): lanes_per_row = min(K/8,
 // 512) consecutive threads read consecutive vectors of one row, so every wave
 // load is 1 KB of contiguous memory; rows_per_pass = 512 / lanes_per_row rows
@@ -160,39 +201,10 @@ __device__ __forceinline__ void rmsnorm_to16(const float* x, const uint16_t* g, 
 // (v_dot2c, fp32) are reduced across the lanes of a row on DPP and across
 // waves through LDS in a fixed order (deterministic).
 // ---------------------------------------------------------------------------
-struct Gv {
-  int nrows, vpr, lpr, rp, passes, J, sub, kl, nwr;
-};
-
-template <int VPT>
-__device__ __forceinline__ Gv gv_plan(int nrows, int K, int t) {
-  Gv g;
-  g.nrows = nrows;
-  g.vpr = K >> 3;
-  g.lpr = g.vpr < kThreads ? g.vpr : kThreads;
-  g.rp = kThreads / g.lpr;
-  g.passes = (nrows + g.rp - 1) / g.rp;
-  g.J = g.passes * VPT;
-  g.sub = t / g.lpr;
-  g.kl = t % g.lpr;
-  g.nwr = g.lpr >= 64 ? g.lpr / 64 : 1;
-  return g;
-}
-
-template <int VPT, class RowPtr>
-__device__ __forceinline__ const uint16_t* gv_addr(const Gv& g, RowPtr& rowptr, int j) {
-  const int p = j / VPT, i = j % VPT;
-  const int row = p * g.rp + g.sub;
-  const int kv = g.kl + i * g.lpr;
-  // out-of-range vectors re-read row 0 (a cache hit) and are discarded
-  const bool ok = row < g.nrows && kv < g.vpr;
-  return rowptr(ok ? row : 0) + (size_t)(ok ? kv : 0) * 8;
-}
-
 // Reduce one row-partial over the lanes of its row and park it in LDS.
 // WIDE: a row spans >= 64 lanes (K >= 512); else 32 lanes (K = 256).
 template <bool WIDE>
-__device__ __forceinline__ void gv_park(float acc, int p, const Gv& g, float* red, int t) {
+__device__ __forceinline__ void gv_park(float acc, int p, const StagePlan& g, float* red, int t) {
   const int row = p * g.rp + g.sub;
   if constexpr (WIDE) {
     acc = sum64_tail(acc);
@@ -212,17 +224,23 @@ __device__ __forceinline__ void gv_park(float acc, int p, const Gv& g, float* re
 // refilled unconditionally (padding vectors read row 0 again and are
 // discarded), which lets the compiler wait for exactly the oldest load
 // (vmcnt(kDepth-1)) instead of draining the queue.
-template <int DT, int VPT, bool WIDE, class RowPtr, class Prep>
-__device__ __forceinline__ bool gemv(int nrows, int K, RowPtr rowptr, Prep prep, const uint16_t* xs, float* red,
-                                     float* yv, int t) {
-  const Gv g = gv_plan<VPT>(nrows, K, t);
-  const int Jp = (g.J + kDepth - 1) / kDepth * kDepth;
-  uint4 ring[kDepth];
-  if (Jp > 0) {
+//
+// The ring is shared by consecutive GEMV stages: with `prefilled` the
+// previous stage already issued this stage's first kDepth vectors, and while
+// this stage drains its last block it issues the first kDepth vectors of the
+// next GEMV stage (next(i) = address of that stage's vector i, or nullptr when
+// there is none), so the weight stream does not stop at the hand-off.
+template <int DT, int VPT, bool WIDE, class Prep>
+__device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv, int t,
+                                     uint4 (&ring)[kDepth], bool prefilled, const StagePlan next) {
+  const int J = g.passes() * VPT;
+  const int Jp = (J + kDepth - 1) / kDepth * kDepth;
+  if (Jp > 0 && !prefilled) {
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(gv_addr<VPT>(g, rowptr, i));
+    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(g.addr<VPT>(i));
   }
   if (!prep()) return false;
+  const bool has_next = next.nrows > 0;
   if (Jp > 0) {
     uint4 xr[VPT];
 #pragma unroll
@@ -236,24 +254,39 @@ __device__ __forceinline__ bool gemv(int nrows, int K, RowPtr rowptr, Prep prep,
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {
         acc = dot8<DT>(ring[i], xr[i % VPT], acc);
-        ring[i] = ldw(gv_addr<VPT>(g, rowptr, j0 + i + kDepth));
+        ring[i] = ldw(g.addr<VPT>(j0 + i + kDepth));
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
           acc = 0.f;
         }
       }
     }
+    if (has_next) {
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) {  // last block: drain
-      acc = dot8<DT>(ring[i], xr[i % VPT], acc);
-      if (i % VPT == VPT - 1) {
-        gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
-        acc = 0.f;
+      for (int i = 0; i < kDepth; ++i) {  // last block: drain, refill with the next stage
+        acc = dot8<DT>(ring[i], xr[i % VPT], acc);
+        ring[i] = ldw(next.addr(i));
+        if (i % VPT == VPT - 1) {
+          gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
+          acc = 0.f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {  // last block: drain
+        acc = dot8<DT>(ring[i], xr[i % VPT], acc);
+        if (i % VPT == VPT - 1) {
+          gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
+          acc = 0.f;
+        }
       }
     }
+  } else if (has_next) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(next.addr(i));
   }
   __syncthreads();
-  for (int r = t; r < nrows; r += kThreads) {
+  for (int r = t; r < g.nrows; r += kThreads) {
     float y = 0.f;
     for (int w = 0; w < g.nwr; ++w) y += red[r * g.nwr + w];
     yv[r] = y;
@@ -262,17 +295,15 @@ __device__ __forceinline__ bool gemv(int nrows, int K, RowPtr rowptr, Prep prep,
   return true;
 }
 
-template <int DT, class RowPtr, class Prep>
-__device__ __forceinline__ bool gemv_any(int nrows, int K, RowPtr rowptr, Prep prep, const uint16_t* xs, float* red,
-                                         float* yv, int t) {
-  const int vpr = K >> 3;
-  if (vpr < 64) return gemv<DT, 1, false>(nrows, K, rowptr, prep, xs, red, yv, t);
-  if (vpr <= kThreads) return gemv<DT, 1, true>(nrows, K, rowptr, prep, xs, red, yv, t);
-  if (vpr <= 2 * kThreads) return gemv<DT, 2, true>(nrows, K, rowptr, prep, xs, red, yv, t);
-  return gemv<DT, 4, true>(nrows, K, rowptr, prep, xs, red, yv, t);
+template <int DT, class Prep>
+__device__ __forceinline__ bool gemv_any(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv,
+                                         int t, uint4 (&ring)[kDepth], bool prefilled, const StagePlan next) {
+  if (g.vpr < 64) return gemv<DT, 1, false>(g, prep, xs, red, yv, t, ring, prefilled, next);
+  if (g.vpt == 1) return gemv<DT, 1, true>(g, prep, xs, red, yv, t, ring, prefilled, next);
+  if (g.vpt == 2) return gemv<DT, 2, true>(g, prep, xs, red, yv, t, ring, prefilled, next);
+  return gemv<DT, 4, true>(g, prep, xs, red, yv, t, ring, prefilled, next);
 }
 
-__device__ __forceinline__ int split_lo(int n, int parts, int i) { return (int)(((long long)n * i) / parts); }
 
 __device__ __forceinline__ const uint16_t* lw_ptr(const Params& P, int l, int k) {
   return P.lw[l * W_PER_LAYER + k];
@@ -282,33 +313,40 @@ __device__ __forceinline__ const uint16_t* lw_ptr(const Params& P, int l, int k)
 // Stages
 // ---------------------------------------------------------------------------
 
+// The plan of GEMV stage `st` of layer l for this thread (tiling in
+// kie_tiling.hpp; matrix bases from the weight-pointer table).
+__device__ __forceinline__ StagePlan plan_stage(const Params& P, int l, int st, int t, int wg, int nb) {
+  const TileDims D{P.d, P.hq, P.hkv, P.hd, P.F, P.V};
+  const uint16_t* mats[M_COUNT] = {lw_ptr(P, l, W_Q),    lw_ptr(P, l, W_K),    lw_ptr(P, l, W_V),
+                                   lw_ptr(P, l, W_O),    lw_ptr(P, l, W_GATE), lw_ptr(P, l, W_UP),
+                                   lw_ptr(P, l, W_DOWN), P.lm_head};
+  return make_stage_plan(D, st, wg, nb, t, mats);
+}
+
 // QKV projection: rows [r0, r1) of the stacked [Wq; Wk; Wv] (contiguous row
 // segments of the three matrices), published unrotated in fp32.  Input x_l:
 // LDS xres (layer 0: the embedding) or polled from the previous layer's xout.
 template <int DT>
-__device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t* X) {
+__device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  const int slot = l * kStagesPerLayer + 0;
+  stamp(tr, slot, 0, c.t);
   const Params& P = c.P;
   const int hd = P.hd, d = P.d;
   const int nq = P.hq * hd, nk = P.hkv * hd;
   const int N = nq + 2 * nk;
   const int r0 = split_lo(N, c.nb, c.wg), r1 = split_lo(N, c.nb, c.wg + 1);
-  const uint16_t* wq = lw_ptr(P, l, W_Q);
-  const uint16_t* wk = lw_ptr(P, l, W_K);
-  const uint16_t* wv = lw_ptr(P, l, W_V);
-  auto rowptr = [&](int r) -> const uint16_t* {
-    const int row = r0 + r;
-    return row < nq ? wq + (size_t)row * d
-         : row < nq + nk ? wk + (size_t)(row - nq) * d : wv + (size_t)(row - nq - nk) * d;
-  };
+  const StagePlan pl = plan_stage(P, l, GS_QKV, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
     if (l > 0 && !poll_f32(X + P.xl.xout + (size_t)(l - 1) * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_ATTN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
+    stamp(tr, slot, 1, c.t);
     return true;
   };
-  if (!gemv_any<DT>(r1 - r0, d, rowptr, prep, c.s.xn, c.s.red, c.s.yv, c.t)) return false;
+  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, l > 0, StagePlan{})) return false;
   uint32_t* dst = X + P.xl.qkv + (size_t)l * N;
   for (int r = c.t; r < r1 - r0; r += kThreads) xst32(dst + r0 + r, __float_as_uint(c.s.yv[r]));
+  stamp(tr, slot, 2, c.t);
   return true;
 }
 
@@ -318,32 +356,27 @@ __device__ __forceinline__ void attn_chunking(const Params& P, int n, int& CL, i
   nch = (n + CL - 1) / CL;
 }
 
-// Rotary embedding in place on LDS vectors: nvec vectors of hd floats, pair
-// (i, i + hd/2) turned by the angle of `pos` (table built on the host in
-// double precision).  Ends with a barrier.
-__device__ __forceinline__ void rope_lds(float* v, int nvec, int hd, const float* rope, int pos, int t) {
-  const int half = hd >> 1;
-  for (int k = t; k < nvec * half; k += kThreads) {
-    const int h = k / half, i = k % half;
-    const float cs = rope[((size_t)pos * half + i) * 2], sn = rope[((size_t)pos * half + i) * 2 + 1];
-    const float a = v[h * hd + i], b = v[h * hd + i + half];
-    v[h * hd + i] = a * cs - b * sn;
-    v[h * hd + i + half] = a * sn + b * cs;
-  }
-  __syncthreads();
-}
+// Online-softmax state update with one more score s and value row v:
+// (m, l, o) -> (max(m, s), l e^(m-m') + e^(s-m'), o e^(m-m') + e^(s-m') v).
+__device__ __forceinline__ float safe_exp_diff(float a, float m) { return a == -INFINITY ? 0.f : expf(a - m); }
 
 // Split-KV attention (flash-decoding): unit (KV head g, chunk c) computes, for
 // the G query heads that read head g, the partial softmax statistics over the
 // chunk's positions: m = max score, l = sum exp(s - m), o = sum exp(s - m) v.
-// Rotary embedding of q and of the new k is fused here; the unit whose chunk
-// holds the current position also appends (rotated k, v) to the KV cache.
+// Rotary embedding of q and of the new k happens in registers right after the
+// poll; the unit whose chunk holds the current position also appends the
+// (rotated k, v) row to the KV cache.  Positions are spread over lane groups
+// of hd/8 lanes; each group keeps an online softmax state, groups are merged
+// with shuffles inside a wave and through LDS across waves.
 template <int DT, int G>
-__device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos, uint32_t* X) {
+__device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
   const Params& P = c.P;
+  const int slot = l * kStagesPerLayer + 1;
+  stamp(tr, slot, 0, c.t);
   const int t = c.t;
   const int hd = P.hd, hkv = P.hkv, hq = P.hq;
+  const int half = hd >> 1, qd4 = hd >> 2;
   const int N = (hq + 2 * hkv) * hd;
   const int n = pos + 1;
   int CL, nch;
@@ -351,195 +384,176 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
   const int units = hkv * nch;
   const int LPP = hd >> 3;                // lanes per position row
   const int PP = kThreads / LPP;          // positions per pass
-  const int pp = t / LPP, e8 = (t % LPP) * 8;
-  const float scale = 1.0f / sqrtf((float)hd);
-  float* qs = c.s.scr;                    // [G][hd]
-  float* kn = qs + G * hd;                // [hd] new key (fp32, rotated); must follow qs
-  float* vn = kn + hd;                    // [hd] new value
-  uint16_t* kv16 = reinterpret_cast<uint16_t*>(vn + hd);  // [2][hd] new row as stored
-  float* ored = vn + 2 * hd;              // [kWaves][G][hd]
-  float* ml = ored + kWaves * G * hd;     // [G][2] (padded to 16 floats)
-  float* sc = ml + 16;                    // [G][cl_cap]
-  constexpr int APF = 8;                  // passes prefetched into registers
-  const uint32_t* src = X + P.xl.qkv + (size_t)l * N;
+  const int grp = t / LPP, e8 = (t % LPP) * 8;
   const int wave = t >> 6, lane = t & 63;
+  const float scale = 1.0f / sqrtf((float)hd);
+  float* qs = c.s.scr;                                    // [G][hd] rotated queries
+  uint16_t* kv16 = reinterpret_cast<uint16_t*>(qs + G * hd);  // [2][hd] new row as stored
+  float* wml = qs + G * hd + hd;                          // [kWaves][G][2] per-wave (m, l)
+  float* wo = wml + kWaves * G * 2;                       // [kWaves][G][hd] per-wave o
+  constexpr int APF = 4;                                  // passes prefetched into registers
+  const uint32_t* src = X + P.xl.qkv + (size_t)l * N;
   for (int u = c.wg; u < units; u += c.nb) {
     const int g = u % hkv, ch = u / hkv;
-    const int j0 = ch * CL, j1 = min(n, j0 + CL), len = j1 - j0;
+    const int j0 = ch * CL, j1 = min(n, j0 + CL);
     const bool has_new = pos >= j0 && pos < j1;
-    const int npass = (len + PP - 1) / PP;
+    const int npass = (j1 - j0 + PP - 1) / PP;
     const size_t plane = ((size_t)l * hkv + g) * P.max_seq * hd;
     uint16_t* kb = P.kc + plane;
     uint16_t* vb = P.vc + plane;
-    // cached rows (written by earlier steps) are independent of this step:
+    // cached rows (written by earlier steps) do not depend on this step:
     // start streaming them before waiting for q
     uint4 kr[APF], vr[APF];
 #pragma unroll
     for (int a = 0; a < APF; ++a) {
-      const int j = j0 + a * PP + pp;
+      const int j = j0 + a * PP + grp;
       if (a < npass && j < j1 && j != pos) {
         kr[a] = ldw(kb + (size_t)j * hd + e8);
         vr[a] = ldw(vb + (size_t)j * hd + e8);
       }
     }
+    // poll roles: q of the G heads (pairs 2m, 2m+1 and their rotary partners
+    // 2m+hd/2, 2m+1+hd/2), then the new k and v of head g
+    const int nq = G * qd4, nkv = has_new ? qd4 : 0;
+    const int role = t < nq ? 0 : t < nq + nkv ? 1 : t < nq + 2 * nkv ? 2 : 3;
+    const int h = role == 0 ? t / qd4 : 0;
+    const int m = role == 0 ? t % qd4 : role == 1 ? t - nq : role == 2 ? t - nq - nkv : 0;
+    float4 rot = make_float4(1.f, 0.f, 1.f, 0.f);
+    if (role <= 1) {
+      const uint4 rw = ldw(reinterpret_cast<const uint16_t*>(P.rope + ((size_t)pos * half + 2 * m) * 2));
+      rot = make_float4(__uint_as_float(rw.x), __uint_as_float(rw.y), __uint_as_float(rw.z), __uint_as_float(rw.w));
+    }
     bool ok = true;
-    // queries of the G heads sharing KV head g (+ the new k, v of head g)
-    const int nq2 = (G * hd) >> 1;
-    const int nw2 = nq2 + (has_new ? hd : 0);
-    for (int i = t; i < nw2; i += kThreads) {
-      const uint32_t* sp;
-      float* dp;
-      if (i < nq2) {
-        sp = src + (size_t)g * G * hd + 2 * i;
-        dp = qs + 2 * i;
-      } else if (i < nq2 + (hd >> 1)) {
-        const int k = i - nq2;
-        sp = src + (size_t)hq * hd + (size_t)g * hd + 2 * k;
-        dp = kn + 2 * k;
-      } else {
-        const int k = i - nq2 - (hd >> 1);
-        sp = src + (size_t)(hq + hkv) * hd + (size_t)g * hd + 2 * k;
-        dp = vn + 2 * k;
+    if (role < 3) {
+      const uint32_t* sp = role == 0 ? src + (size_t)(g * G + h) * hd
+                         : role == 1 ? src + (size_t)hq * hd + (size_t)g * hd
+                                     : src + (size_t)(hq + hkv) * hd + (size_t)g * hd;
+      uint64_t va = xld64(sp + 2 * m), vb2 = xld64(sp + 2 * m + half);  // both in flight, one wait
+      if (!(Ready32x2{}(va) && Ready32x2{}(vb2)))
+        ok = poll64(sp + 2 * m, va, c.w, Ready32x2{}) && poll64(sp + 2 * m + half, vb2, c.w, Ready32x2{});
+      float a0 = lo_f(va), a1 = hi_f(va), b0 = lo_f(vb2), b1 = hi_f(vb2);
+      if (role <= 1) {  // rotate pairs (2m, 2m+hd/2) and (2m+1, 2m+1+hd/2)
+        const float ra0 = a0 * rot.x - b0 * rot.y, rb0 = a0 * rot.y + b0 * rot.x;
+        const float ra1 = a1 * rot.z - b1 * rot.w, rb1 = a1 * rot.w + b1 * rot.z;
+        a0 = ra0; b0 = rb0; a1 = ra1; b1 = rb1;
       }
-      uint64_t v = 0;
-      if (ok && poll64(sp, v, c.w, Ready32x2{})) {
-        dp[0] = lo_f(v);
-        dp[1] = hi_f(v);
-      } else {
-        ok = false;
+      if (role == 0) {
+        float* qh = qs + h * hd;
+        qh[2 * m] = a0; qh[2 * m + 1] = a1; qh[2 * m + half] = b0; qh[2 * m + 1 + half] = b1;
+      } else if (ok) {
+        // append to the cache for later steps; keep the stored values for now
+        const uint32_t wa = pack16<DT>(a0, a1), wb = pack16<DT>(b0, b1);
+        uint32_t* dst = reinterpret_cast<uint32_t*>((role == 1 ? kb : vb) + (size_t)pos * hd);
+        xst32(dst + m, wa);
+        xst32(dst + m + (half >> 1), wb);
+        uint32_t* kv32 = reinterpret_cast<uint32_t*>(kv16) + (role == 1 ? 0 : half);
+        kv32[m] = wa;
+        kv32[m + (half >> 1)] = wb;
       }
     }
     if (any_failed(!ok)) return false;
-    rope_lds(qs, has_new ? G + 1 : G, hd, P.rope, pos, t);  // kn follows qs: rotated too
+    stamp(tr, slot, 1, t);
     if (has_new) {
-      // append the new row to the cache (read by later steps) and keep the
-      // stored 16-bit values for this step's own use
-      uint32_t* kd = reinterpret_cast<uint32_t*>(kb + (size_t)pos * hd);
-      uint32_t* vd = reinterpret_cast<uint32_t*>(vb + (size_t)pos * hd);
-      for (int i = t; i < hd; i += kThreads) {  // i < hd/2: key pairs, else value pairs
-        const bool isk = i < (hd >> 1);
-        const int k = isk ? i : i - (hd >> 1);
-        const float* f = isk ? kn : vn;
-        const uint32_t wv = pack16<DT>(f[2 * k], f[2 * k + 1]);
-        xst32((isk ? kd : vd) + k, wv);
-        reinterpret_cast<uint32_t*>(kv16)[(isk ? 0 : (hd >> 1)) + k] = wv;
-      }
-      __syncthreads();
 #pragma unroll
-      for (int a = 0; a < APF; ++a) {
-        const int j = j0 + a * PP + pp;
-        if (a < npass && j == pos) {
+      for (int a = 0; a < APF; ++a)
+        if (a < npass && j0 + a * PP + grp == pos) {
           kr[a] = *reinterpret_cast<const uint4*>(kv16 + e8);
           vr[a] = *reinterpret_cast<const uint4*>(kv16 + hd + e8);
         }
-      }
     }
-    // scores
-    for (int a = 0; a < npass; ++a) {
-      const int j = j0 + a * PP + pp;
-      const bool valid = j < j1;
-      uint4 kv4 = make_uint4(0, 0, 0, 0);
-      if (a < APF) {
+    // online softmax over this lane group's positions, one head at a time
+    // (keeps one head's state live: bounded register use for any G)
+#pragma unroll 1
+    for (int hh = 0; hh < G; ++hh) {
+      float q8[8];
 #pragma unroll
-        for (int b = 0; b < APF; ++b)
-          if (b == a) kv4 = kr[b];
-      } else if (valid) {
-        kv4 = j == pos ? *reinterpret_cast<const uint4*>(kv16 + e8) : ldw(kb + (size_t)j * hd + e8);
+      for (int e = 0; e < 8; ++e) q8[e] = qs[hh * hd + e8 + e];
+      float mx = -INFINITY, ls = 0.f, o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = 0.f;
+      for (int a = 0; a < npass; ++a) {
+        const int j = j0 + a * PP + grp;
+        if (j >= j1) break;  // uniform per lane group
+        uint4 k4, v4;
+        if (a < APF) {
+          k4 = kr[0];
+          v4 = vr[0];
+#pragma unroll
+          for (int b = 1; b < APF; ++b)
+            if (b == a) { k4 = kr[b]; v4 = vr[b]; }
+        } else if (j == pos) {
+          k4 = *reinterpret_cast<const uint4*>(kv16 + e8);
+          v4 = *reinterpret_cast<const uint4*>(kv16 + hd + e8);
+        } else {
+          k4 = ldw(kb + (size_t)j * hd + e8);
+          v4 = ldw(vb + (size_t)j * hd + e8);
+        }
+        float kf[8], vf[8];
+        unpack8<DT>(k4, kf);
+        unpack8<DT>(v4, vf);
+        float sd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sd += q8[e] * kf[e];
+        sd = ((LPP == 16) ? sum16(sd) : sum8(sd)) * scale;
+        const float mn = fmaxf(mx, sd);
+        const float fo = safe_exp_diff(mx, mn), fp = expf(sd - mn);
+        ls = ls * fo + fp;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = o[e] * fo + fp * vf[e];
+        mx = mn;
       }
-      float kf[8];
-      unpack8<DT>(kv4, kf);
+      // merge the lane groups of the wave (lanes that differ in bits >= log2(LPP))
+      for (int msk = LPP; msk < 64; msk <<= 1) {
+        const float mo = __shfl_xor(mx, msk), lo = __shfl_xor(ls, msk);
+        const float mn = fmaxf(mx, mo);
+        const float fa = safe_exp_diff(mx, mn), fb = safe_exp_diff(mo, mn);
+        ls = ls * fa + lo * fb;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* qh = qs + h * hd + e8;
-        float sdot = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sdot += qh[e] * kf[e];
-        sdot = (LPP == 16) ? sum16(sdot) : sum8(sdot);
-        if ((t % LPP) == 0 && valid) sc[h * P.cl_cap + (j - j0)] = sdot * scale;
+        for (int e = 0; e < 8; ++e) o[e] = o[e] * fa + __shfl_xor(o[e], msk) * fb;
+        mx = mn;
       }
-    }
-    __syncthreads();
-    // softmax statistics: wave h handles head h
-    for (int h = wave; h < G; h += kWaves) {
-      float* sh = sc + h * P.cl_cap;
-      float m = -INFINITY;
-      for (int j = lane; j < len; j += 64) m = fmaxf(m, sh[j]);
-      m = wave_max(m);
-      float sum = 0.f;
-      for (int j = lane; j < len; j += 64) {
-        const float pj = expf(sh[j] - m);
-        sh[j] = pj;
-        sum += pj;
+      if (lane < LPP) {
+        float* dst = wo + (wave * G + hh) * hd + e8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = o[e];
+        if (lane == 0) {
+          wml[(wave * G + hh) * 2] = mx;
+          wml[(wave * G + hh) * 2 + 1] = ls;
+        }
       }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        ml[2 * h] = m;
-        ml[2 * h + 1] = sum;
-      }
-    }
-    __syncthreads();
-    // o = sum_j p_j v_j
-    float o[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-    for (int a = 0; a < npass; ++a) {
-      const int j = j0 + a * PP + pp;
-      if (j >= j1) continue;
-      uint4 vv4 = make_uint4(0, 0, 0, 0);
-      if (a < APF) {
-#pragma unroll
-        for (int b = 0; b < APF; ++b)
-          if (b == a) vv4 = vr[b];
-      } else {
-        vv4 = j == pos ? *reinterpret_cast<const uint4*>(kv16 + hd + e8) : ldw(vb + (size_t)j * hd + e8);
-      }
-      float vf[8];
-      unpack8<DT>(vv4, vf);
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pj = sc[h * P.cl_cap + (j - j0)];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] += pj * vf[e];
-      }
-    }
-    // reduce over the position groups of the wave (lanes with equal t % LPP)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = o[h][e];
-        for (int msk = LPP; msk < 64; msk <<= 1) v += __shfl_xor(v, msk);
-        o[h][e] = v;
-      }
-    if (lane < LPP) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ored[(wave * G + h) * hd + e8 + e] = o[h][e];
     }
     __syncthreads();
+    // merge the waves and publish (m, l, o) of each head for this chunk
     uint32_t* att = X + P.xl.att;
     for (int idx = t; idx < G * hd; idx += kThreads) {
-      const int h = idx / hd, e = idx % hd;
-      float acc = 0.f;
+      const int hh = idx / hd, e = idx % hd;
+      float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) acc += ored[(w * G + h) * hd + e];
-      uint32_t* rowp = att + (((size_t)l * hq + (size_t)g * G + h) * P.cmax + ch) * P.astride;
-      xst32(rowp + 4 + e, __float_as_uint(acc));
-      if (e == 0) xst64(rowp, pack2f(ml[2 * h], ml[2 * h + 1]));
+      for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, wml[(w2 * G + hh) * 2]);
+      float Ls = 0.f, Os = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < kWaves; ++w2) {
+        const float f = safe_exp_diff(wml[(w2 * G + hh) * 2], M);
+        Ls += wml[(w2 * G + hh) * 2 + 1] * f;
+        Os += wo[(w2 * G + hh) * hd + e] * f;
+      }
+      uint32_t* rowp = att + (((size_t)l * hq + (size_t)g * G + hh) * P.cmax + ch) * P.astride;
+      xst32(rowp + 4 + e, __float_as_uint(Os));
+      if (e == 0) xst64(rowp, pack2f(M, Ls));
     }
     __syncthreads();
   }
+  stamp(tr, slot, 2, t);
   return true;
 }
 
 // Merge of the split-KV partials.  Unit (head h, dims 8s..8s+7) runs on one
 // wave; lanes walk the chunks with an online rescaling, then the wave combines.
 template <int DT>
-__device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos, uint32_t* X) {
+__device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
+  const int slot = l * kStagesPerLayer + 2;
+  stamp(tr, slot, 0, c.t);
   const Params& P = c.P;
   const int hd = P.hd, hq = P.hq;
   int CL, nch;
@@ -555,12 +569,15 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
     for (int ch = lane; ch < nch && ok; ch += 64) {
       const uint32_t* rowp = X + P.xl.att + (((size_t)l * hq + h) * P.cmax + ch) * P.astride;
-      uint64_t mlv = 0, o01 = 0, o23 = 0, o45 = 0, o67 = 0;
       const uint32_t* op = rowp + 4 + sl * 8;
-      ok = poll64(rowp, mlv, c.w, Ready32x2{}) && poll64(op, o01, c.w, Ready32x2{}) &&
-           poll64(op + 2, o23, c.w, Ready32x2{}) && poll64(op + 4, o45, c.w, Ready32x2{}) &&
-           poll64(op + 6, o67, c.w, Ready32x2{});
-      if (!ok) break;
+      // issue all five loads, then wait once
+      uint64_t mlv = xld64(rowp), o01 = xld64(op), o23 = xld64(op + 2), o45 = xld64(op + 4), o67 = xld64(op + 6);
+      const Ready32x2 rd{};
+      if (!(rd(mlv) && rd(o01) && rd(o23) && rd(o45) && rd(o67))) {
+        ok = poll64(rowp, mlv, c.w, rd) && poll64(op, o01, c.w, rd) && poll64(op + 2, o23, c.w, rd) &&
+             poll64(op + 4, o45, c.w, rd) && poll64(op + 6, o67, c.w, rd);
+        if (!ok) break;
+      }
       const float mc = lo_f(mlv), lc = hi_f(mlv);
       const float mn = fmaxf(m, mc);
       const float a = expf(m - mn), b = expf(mc - mn);
@@ -584,67 +601,85 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
       xst64(dst + 6, pack2f(o[6] * inv, o[7] * inv));
     }
   }
-  return !any_failed(!ok);
+  const bool failed = any_failed(!ok);
+  stamp(tr, slot, 2, c.t);
+  return !failed;
 }
 
 // x_mid = x_l + Wo a  (rows split over work-groups)
 template <int DT>
-__device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* X) {
+__device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  const int slot = l * kStagesPerLayer + 3;
+  stamp(tr, slot, 0, c.t);
   const Params& P = c.P;
   const int d = P.d, K = P.hq * P.hd;
   const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
-  const uint16_t* W = lw_ptr(P, l, W_O);
-  auto rowptr = [&](int r) -> const uint16_t* { return W + (size_t)(r0 + r) * K; };
-  auto prep = [&]() -> bool { return poll_to16<DT>(X + P.xl.a + (size_t)l * K, K, c.s.xn, c.w, c.t); };
-  if (!gemv_any<DT>(r1 - r0, K, rowptr, prep, c.s.xn, c.s.red, c.s.yv, c.t)) return false;
+  const StagePlan pl = plan_stage(P, l, GS_WO, c.t, c.wg, c.nb);
+  auto prep = [&]() -> bool {
+    const bool r = poll_to16<DT>(X + P.xl.a + (size_t)l * K, K, c.s.xn, c.w, c.t);
+    stamp(tr, slot, 1, c.t);
+    return r;
+  };
+  const StagePlan np = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
+  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, false, np)) return false;
   uint32_t* dst = X + P.xl.xmid + (size_t)l * d;
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
+  stamp(tr, slot, 2, c.t);
   return true;
 }
 
 // h = silu(Wg n) * (Wu n), n = RMSNorm(x_mid) * g_ffn
 template <int DT>
-__device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32_t* X) {
+__device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  const int slot = l * kStagesPerLayer + 4;
+  stamp(tr, slot, 0, c.t);
   const Params& P = c.P;
   const int d = P.d, F = P.F;
   const int f0 = split_lo(F, c.nb, c.wg), f1 = split_lo(F, c.nb, c.wg + 1);
   const int nf = f1 - f0;
-  const uint16_t* Wg = lw_ptr(P, l, W_GATE);
-  const uint16_t* Wu = lw_ptr(P, l, W_UP);
-  auto rowptr = [&](int r) -> const uint16_t* {
-    return r < nf ? Wg + (size_t)(f0 + r) * d : Wu + (size_t)(f0 + r - nf) * d;
-  };
+  const StagePlan pl = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
     if (!poll_f32(X + P.xl.xmid + (size_t)l * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_FFN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
+    stamp(tr, slot, 1, c.t);
     return true;
   };
-  if (!gemv_any<DT>(2 * nf, d, rowptr, prep, c.s.xn, c.s.red, c.s.yv, c.t)) return false;
+  const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
+  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, np)) return false;
   uint32_t* dst = X + P.xl.h + (size_t)l * F;
   for (int f = c.t; f < nf; f += kThreads) {
     const float gt = c.s.yv[f], up = c.s.yv[nf + f];
     xst32(dst + f0 + f, __float_as_uint(gt / (1.0f + expf(-gt)) * up));
   }
+  stamp(tr, slot, 2, c.t);
   return true;
 }
 
 // x_next = x_mid + Wd h
 template <int DT>
-__device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t* X) {
+__device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  const int slot = l * kStagesPerLayer + 5;
+  stamp(tr, slot, 0, c.t);
   const Params& P = c.P;
   const int d = P.d, F = P.F;
   const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
-  const uint16_t* W = lw_ptr(P, l, W_DOWN);
-  auto rowptr = [&](int r) -> const uint16_t* { return W + (size_t)(r0 + r) * F; };
-  auto prep = [&]() -> bool { return poll_to16<DT>(X + P.xl.h + (size_t)l * F, F, c.s.xn, c.w, c.t); };
-  if (!gemv_any<DT>(r1 - r0, F, rowptr, prep, c.s.xn, c.s.red, c.s.yv, c.t)) return false;
+  const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
+  auto prep = [&]() -> bool {
+    const bool r = poll_to16<DT>(X + P.xl.h + (size_t)l * F, F, c.s.xn, c.w, c.t);
+    stamp(tr, slot, 1, c.t);
+    return r;
+  };
+  const StagePlan np = l + 1 < P.L ? plan_stage(P, l + 1, GS_QKV, c.t, c.wg, c.nb)
+                                   : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
+  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, np)) return false;
   uint32_t* dst = X + P.xl.xout + (size_t)l * d;
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
+  stamp(tr, slot, 2, c.t);
   return true;
 }
 
@@ -683,81 +718,82 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, const Lds& s, int
 }
 
 // LM head on this work-group's vocabulary rows; logits optionally written.
+// The host guarantees ceil(V / grid) rows fit the LDS partial-sum buffers.
 template <int DT>
 __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, float* logits, float& best_v,
-                                     int& best_i) {
+                                     int& best_i, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   const Params& P = c.P;
+  const int slot = P.L * kStagesPerLayer;
+  stamp(tr, slot, 0, c.t);
   const int d = P.d, V = P.V;
   const int v0 = split_lo(V, c.nb, c.wg), v1 = split_lo(V, c.nb, c.wg + 1);
-  const int vpr = d >> 3;
-  const int nwr = vpr >= 64 ? (vpr < kThreads ? vpr : kThreads) / 64 : 1;
-  int cap = kRedCap / nwr;
-  if (cap > kYCap) cap = kYCap;
+  const StagePlan pl = plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
+  auto prep = [&]() -> bool {
+    if (!poll_f32(X + P.xl.xout + (size_t)(P.L - 1) * d, d, c.s.xres, c.w, c.t)) return false;
+    rmsnorm_to16<DT>(c.s.xres, P.final_norm, d, P.eps, c.s.xn, c.s.misc, c.t);
+    stamp(tr, slot, 1, c.t);
+    return true;
+  };
+  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, StagePlan{})) return false;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
-  for (int b0 = v0; b0 < v1 || b0 == v0; b0 += cap) {
-    const int rows = min(cap, v1 - b0);
-    auto rowptr = [&](int r) -> const uint16_t* { return P.lm_head + (size_t)(b0 + r) * d; };
-    auto prep = [&]() -> bool {
-      if (b0 != v0) return true;
-      if (!poll_f32(X + P.xl.xout + (size_t)(P.L - 1) * d, d, c.s.xres, c.w, c.t)) return false;
-      rmsnorm_to16<DT>(c.s.xres, P.final_norm, d, P.eps, c.s.xn, c.s.misc, c.t);
-      return true;
-    };
-    if (!gemv_any<DT>(rows, d, rowptr, prep, c.s.xn, c.s.red, c.s.yv, c.t)) return false;
-    for (int r = c.t; r < rows; r += kThreads) {
-      const float y = c.s.yv[r];
-      if (logits) logits[b0 + r] = y;
-      if (arg_better(y, b0 + r, bv, bi)) {
-        bv = y;
-        bi = b0 + r;
-      }
+  for (int r = c.t; r < v1 - v0; r += kThreads) {
+    const float y = c.s.yv[r];
+    if (logits) logits[v0 + r] = y;
+    if (arg_better(y, v0 + r, bv, bi)) {
+      bv = y;
+      bi = v0 + r;
     }
-    __syncthreads();
-    if (rows <= 0) break;
   }
   block_argmax(bv, bi, c.s, c.t);
   best_v = bv;
   best_i = bi;
+  stamp(tr, slot, 2, c.t);
   return true;
 }
 
-// Reset this work-group's share of exchange set `Xr` to the NaN pattern.
-// Set Xr was last used two steps ago; every work-group finished reading it
-// before publishing its partial of the previous step, which this work-group
-// has already consumed.
-__device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr, int nch_prev) {
+// Reset this work-group's share of exchange set `Xr` to the NaN pattern, with
+// threads [t_lo, kThreads).  Xr is the set of the previous step: every
+// work-group finished reading it before publishing its partial of that step,
+// and this work-group has consumed all those partials.  The next writes into
+// Xr happen two steps later, by work-groups that have seen this work-group's
+// next partial, which is published after a release fence that covers these
+// stores.
+__device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr, int nch_prev, int t_lo) {
   const Sc c = stage_ctx(Pp, smem);
   const Params& P = c.P;
+  if (c.t < t_lo) return;
+  const uint32_t tt = c.t - t_lo, nt = kThreads - t_lo;
   const uint64_t sent2 = ~0ull;
-  const uint64_t dense2 = P.xl.dense >> 1;  // in 8-byte units
-  {
-    const uint64_t a = dense2 * c.wg / c.nb, b = dense2 * (c.wg + 1) / c.nb;
-    for (uint64_t k = a + c.t; k < b; k += kThreads) xst64(Xr + 2 * k, sent2);
+  {  // dense part, 8-byte units (the host keeps every count below 2^32 / grid)
+    const uint32_t dense2 = (uint32_t)(P.xl.dense >> 1);
+    const uint32_t a = split_lo(dense2, c.nb, c.wg), b = split_lo(dense2, c.nb, c.wg + 1);
+    for (uint32_t k = a + tt; k < b; k += nt) xst64(Xr + 2 * (size_t)k, sent2);
   }
-  if (nch_prev > 0) {
-    const uint64_t per = (uint64_t)nch_prev * P.astride / 2;  // 8-byte units per (layer, head)
-    const uint64_t blocks = (uint64_t)P.L * P.hq;
-    const uint64_t tot = per * blocks;
-    const uint64_t a = tot * c.wg / c.nb, b = tot * (c.wg + 1) / c.nb;
+  if (nch_prev > 0) {  // the chunks of every (layer, head) block that were in use
+    const uint32_t per = (uint32_t)(nch_prev * P.astride / 2);  // 8-byte units per block
+    const uint32_t blocks = (uint32_t)(P.L * P.hq);
+    const uint32_t b0 = split_lo(blocks, c.nb, c.wg), b1 = split_lo(blocks, c.nb, c.wg + 1);
     uint32_t* att = Xr + P.xl.att;
-    for (uint64_t k = a + c.t; k < b; k += kThreads) {
-      const uint64_t blk = k / per, off = k % per;
-      xst64(att + blk * (uint64_t)P.cmax * P.astride + 2 * off, sent2);
+    for (uint32_t blk = b0; blk < b1; ++blk) {
+      uint32_t* base = att + (size_t)blk * P.cmax * P.astride;
+      for (uint32_t k = tt; k < per; k += nt) xst64(base + 2 * (size_t)k, sent2);
     }
   }
 }
 
 // Gather the per-work-group (max, index) partials -> the greedy token.  Every
 // work-group reduces the same values in the same order, so all agree.
-__device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* X, int& tok) {
+__device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* X, int& tok, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
+  const int slot = c.P.L * kStagesPerLayer + 1;
+  stamp(tr, slot, 0, c.t);
   const Params& P = c.P;
   float gv = -INFINITY;
   int gi = 0x7FFFFFFF;
   bool ok = true;
-  for (int w = c.t; w < c.nb; w += kThreads) {
+  for (int w = c.t; w < c.nb && c.t < kThreads / 2; w += kThreads / 2) {
     uint64_t v = 0;
     if (ok && poll64(X + P.xl.arg + 2 * w, v, c.w, Ready32x2{})) {
       const float vv = lo_f(v);
@@ -771,9 +807,11 @@ __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* 
     }
   }
   if (any_failed(!ok)) return false;
+  stamp(tr, slot, 1, c.t);
   block_argmax(gv, gi, c.s, c.t);
   // NaN logits never win a comparison: keep the index inside the vocabulary
   tok = (gi >= 0 && gi < P.V) ? gi : 0;
+  stamp(tr, slot, 2, c.t);
   return true;
 }
 
@@ -788,11 +826,13 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
   int tok = Pp->in_tok;
   int done = 0;
   bool ok = true;
+  uint4 ring[kDepth];  // weight-stream ring shared by consecutive GEMV stages
   for (int s = 0; s < n_steps && ok; ++s) {
     const Params& P = *opaque_s(Pp);
     const int pos = P.pos0 + s;
     if (P.forced) tok = P.forced[s];
     uint32_t* X = P.xch + (size_t)(s % kRingSets) * P.xl.words;
+    uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace : nullptr;
     {  // embedding row -> residual stream
       const Sc c = stage_ctx(Pp, smem);
       const uint16_t* er = c.P.tok_emb + (size_t)tok * c.P.d;
@@ -800,9 +840,9 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       __syncthreads();
     }
     for (int l = 0; l < L && ok; ++l) {
-      ok = st_qkv<DT>(Pp, smem, l, X) && st_attn<DT, G>(Pp, smem, l, pos, X) &&
-           st_merge<DT>(Pp, smem, l, pos, X) && st_wo<DT>(Pp, smem, l, X) && st_gateup<DT>(Pp, smem, l, X) &&
-           st_down<DT>(Pp, smem, l, X);
+      ok = st_qkv<DT>(Pp, smem, l, X, tr, ring) && st_attn<DT, G>(Pp, smem, l, pos, X, tr) &&
+           st_merge<DT>(Pp, smem, l, pos, X, tr) && st_wo<DT>(Pp, smem, l, X, tr, ring) &&
+           st_gateup<DT>(Pp, smem, l, X, tr, ring) && st_down<DT>(Pp, smem, l, X, tr, ring);
     }
     if (!ok) break;
     float bv = 0.f;
@@ -811,22 +851,24 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       const Params& Q = *opaque_s(Pp);
       if (!Q.lm_last_only || s == Q.n_steps - 1) {
         float* lg = Q.logits ? Q.logits + (size_t)(Q.lm_last_only ? 0 : s) * Q.V : nullptr;
-        if (!st_lmhead<DT>(Pp, smem, X, lg, bv, bi)) {
+        if (!st_lmhead<DT>(Pp, smem, X, lg, bv, bi, tr, ring)) {
           ok = false;
           break;
         }
       }
     }
-    // recycle the set used two steps ago, then publish this step's partial
-    if (s >= 2) {
-      int CL, nch;
-      attn_chunking(*Pp, pos - 1, CL, nch);
-      reset_set(Pp, smem, Pp->xch + (size_t)((s + 1) % kRingSets) * Pp->xl.words, nch);
-    }
+    // publish this step's partial after a release of everything this step wrote
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     if (t == 0 && wg != Pp->withhold_wg) xst64(X + Pp->xl.arg + 2 * wg, pack2f(bv, __int_as_float(bi)));
-    if (!gather_token(Pp, smem, X, tok)) {
+    // the upper half of the work-group recycles the previous step's exchange
+    // set while the lower half gathers the partials (grid <= kThreads / 2)
+    if (s >= 1) {
+      int CL, nch;
+      attn_chunking(*Pp, pos, CL, nch);
+      reset_set(Pp, smem, Pp->xch + (size_t)((s + 2) % kRingSets) * Pp->xl.words, nch, kThreads / 2);
+    }
+    if (!gather_token(Pp, smem, X, tok, tr)) {
       ok = false;
       break;
     }
@@ -861,14 +903,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
   for (int iv = 0; iv < nvec; ++iv) {
     const int t = opaque_v((int)threadIdx.x);
     const uint16_t* Wc = W + (size_t)(iv % ncopy) * rows * cols;
-    auto rowptr = [&](int r) -> const uint16_t* { return Wc + (size_t)(r0 + r) * cols; };
+    StagePlan pl = plan_rows(r1 - r0, cols, t);
+    pl.seg0 = Wc + (size_t)r0 * cols;
     auto prep = [&]() -> bool {
       const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
       for (int i = t; i < (cols >> 3); i += kThreads) reinterpret_cast<uint4*>(xs)[i] = src[i];
       __syncthreads();
       return true;
     };
-    gemv_any<DT>(r1 - r0, cols, rowptr, prep, xs, red, yv, t);
+    uint4 ring[kDepth];
+    gemv_any<DT>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
     for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
     __syncthreads();
   }

@@ -11,6 +11,7 @@
 
 #include "kie.h"
 #include "kie_params.hpp"
+#include "kie_tiling.hpp"
 
 namespace kie {
 const void* monokernel_fn_f16(int group);
@@ -107,8 +108,8 @@ LdsPlan lds_plan(const kie_config& c) {
   if (c.d_ffn > kmax) kmax = c.d_ffn;
   const int G = c.n_heads / c.n_kv_heads;
   const size_t gemv_scr = (size_t)(kRedCap + kYCap) * 4;
-  const size_t attn_scr = ((size_t)G * c.head_dim + 3 * (size_t)c.head_dim + (size_t)kWaves * G * c.head_dim + 16 +
-                           (size_t)G * attn_cl_cap(c)) * 4;
+  const size_t attn_scr = ((size_t)G * c.head_dim + (size_t)c.head_dim + (size_t)kWaves * G * 2 +
+                           (size_t)kWaves * G * c.head_dim) * 4;
   size_t o = 0;
   p.xres = 0;
   o = align_up((size_t)c.d_model * 4, 16);
@@ -152,6 +153,8 @@ struct kie_engine {
   float last_ms = 0.f;
   int last_steps = 0;
   Params params_host{};
+  uint64_t* trace = nullptr;
+  int trace_step = 0;
 };
 
 extern "C" const char* kie_status_string(kie_status s) {
@@ -182,7 +185,6 @@ extern "C" kie_status kie_config_validate(const kie_config* c) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return KIE_ERR_UNSUPPORTED;
   if (c->n_kv_heads > kAttnUnits) return KIE_ERR_UNSUPPORTED;
   if (!k_ok(c->d_model) || !k_ok(c->n_heads * c->head_dim) || !k_ok(c->d_ffn)) return KIE_ERR_UNSUPPORTED;
-  if (attn_cl_cap(*c) > 2048) return KIE_ERR_UNSUPPORTED;  // split-KV chunk beyond the LDS score buffer
   if ((long long)c->vocab * c->d_model >= (1ll << 40)) return KIE_ERR_UNSUPPORTED;
   if (lds_plan(*c).bytes > 160 * 1024) return KIE_ERR_UNSUPPORTED;
   return KIE_OK;
@@ -242,6 +244,23 @@ extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, siz
   }
   // One resident work-group per compute unit.
   e->grid = e->cu_count < kMaxWG ? e->cu_count : kMaxWG;
+  // every GEMV stage's rows per work-group must fit the LDS partial sums
+  {
+    const kie_config& c = *cfg;
+    auto fits = [&](long long rows, int K) {
+      const int vpr = K / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
+      return rows <= kYCap && rows * nwr <= kRedCap;
+    };
+    auto per = [&](long long n) { return (n + e->grid - 1) / e->grid; };
+    const long long qkv = (long long)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+    if (!fits(per(qkv), c.d_model) || !fits(per(c.d_model), c.n_heads * c.head_dim) ||
+        !fits(2 * per(c.d_ffn), c.d_model) || !fits(per(c.d_model), c.d_ffn) || !fits(per(c.vocab), c.d_model) ||
+        e->grid > kThreads / 2 || (uint64_t)c.vocab * e->grid >= (1ull << 32) ||
+        (lay.xl.dense / 2) * e->grid >= (1ull << 32) || (uint64_t)c.d_ffn * e->grid >= (1ull << 32)) {
+      delete e;
+      return KIE_ERR_UNSUPPORTED;
+    }
+  }
 
   // Rotary table, built in double precision: angle(p, i) = p * base^(-2i/hd).
   const int half = cfg->head_dim / 2;
@@ -319,6 +338,8 @@ static Params base_params(const kie_engine* e) {
   P.abort_after = -1;
   P.withhold_wg = e->withhold_wg;
   P.timeout = e->timeout;
+  P.trace = e->trace;
+  P.trace_step = e->trace_step;
   P.lds_xres = e->lds.xres; P.lds_xn = e->lds.xn; P.lds_scr = e->lds.scr; P.lds_misc = e->lds.misc;
   P.lds_bytes = e->lds.bytes;
   return P;
@@ -531,5 +552,104 @@ extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t co
   (void)hipEventDestroy(b);
   if (he != hipSuccess) return hip_fail(he, "gemv probe");
   if (kernel_ms) *kernel_ms = ms;
+  return KIE_OK;
+}
+
+extern "C" size_t kie_trace_words(const kie_engine* e) {
+  if (!e) return 0;
+  return (size_t)(e->cfg.n_layers * kStagesPerLayer + 2) * e->grid * 3;
+}
+
+extern "C" kie_status kie_set_trace(kie_engine* e, uint64_t* trace_dev, int32_t step) {
+  if (!e || step < 0) return KIE_ERR_ARG;
+  if (trace_dev && (reinterpret_cast<uintptr_t>(trace_dev) & 7)) return KIE_ERR_ARG;
+  e->trace = trace_dev;
+  e->trace_step = step;
+  return KIE_OK;
+}
+
+// Host check of the GEMV tiling (kie_tiling.hpp) for cfg on `grid`
+// work-groups: every vector a thread loads lies inside its weight matrix and
+// on a row boundary grid; every in-range vector is the (row, column) the stage
+// definition assigns to it; with `full`, every vector of every matrix is
+// loaded exactly once by the grid (sampled work-groups otherwise).
+extern "C" kie_status kie_check_tiling(const kie_config* cfg, int32_t grid, int32_t full) {
+  const kie_status v = kie_config_validate(cfg);
+  if (v != KIE_OK) return v;
+  if (grid < 1 || grid > kMaxWG) return KIE_ERR_ARG;
+  const kie_config& c = *cfg;
+  const TileDims D{c.d_model, c.n_heads, c.n_kv_heads, c.head_dim, c.d_ffn, c.vocab};
+  const uintptr_t kSpan = (uintptr_t)1 << 40;  // fake, disjoint matrix bases
+  const uint16_t* mats[M_COUNT];
+  for (int m = 0; m < M_COUNT; ++m) mats[m] = reinterpret_cast<const uint16_t*>((uintptr_t)(m + 1) * kSpan);
+  const bool verbose = getenv("KIE_VERBOSE") != nullptr;
+  auto fail = [&](const char* what, int st, int wg, int t, int j) {
+    if (verbose) fprintf(stderr, "kie_check_tiling: %s (stage %d wg %d thread %d vector %d)\n", what, st, wg, t, j);
+    return KIE_ERR_UNSUPPORTED;
+  };
+  std::vector<std::vector<uint8_t>> seen;
+  if (full) {
+    seen.resize(M_COUNT);
+    for (int m = 0; m < M_COUNT; ++m) {
+      int N, K;
+      stage_dims(D, m == M_Q || m == M_K || m == M_V ? GS_QKV : m == M_O ? GS_WO
+                      : m == M_GATE || m == M_UP ? GS_GATEUP : m == M_DOWN ? GS_DOWN : GS_LM, N, K);
+      seen[m].assign((size_t)matrix_rows(D, m) * (K / 8), 0);
+    }
+  }
+  std::vector<int> wgs;
+  if (full) {
+    for (int w = 0; w < grid; ++w) wgs.push_back(w);
+  } else {
+    for (int w : {0, 1, grid / 2, grid - 2, grid - 1})
+      if (w >= 0 && w < grid && (wgs.empty() || wgs.back() != w)) wgs.push_back(w);
+  }
+  for (int st = 0; st < GS_COUNT; ++st) {
+    int N, K;
+    stage_dims(D, st, N, K);
+    for (int wg : wgs) {
+      const int r0 = split_lo(N, grid, wg), r1 = split_lo(N, grid, wg + 1), n = r1 - r0;
+      for (int t = 0; t < kThreads; ++t) {
+        const StagePlan g = make_stage_plan(D, st, wg, grid, t, mats);
+        if (g.nrows > kYCap || (long long)g.nrows * g.nwr > kRedCap) return fail("rows exceed LDS", st, wg, t, -1);
+        if (g.nrows == 0) continue;
+        const int J = g.passes() * g.vpt, Jp = (J + kDepth - 1) / kDepth * kDepth;
+        for (int j = 0; j < Jp + kDepth; ++j) {  // + the prefetch reach of the previous stage
+          const uintptr_t a = reinterpret_cast<uintptr_t>(g.addr(j));
+          const int m = (int)(a / kSpan) - 1;
+          if (m < 0 || m >= M_COUNT) return fail("address outside every matrix", st, wg, t, j);
+          const uint64_t e = (a - (uintptr_t)(m + 1) * kSpan) / 2;
+          if ((a & 15) != 0 || e % 8 != 0) return fail("misaligned vector", st, wg, t, j);
+          if (e + 8 > (uint64_t)matrix_rows(D, m) * K) return fail("vector beyond its matrix", st, wg, t, j);
+          const int p = j / g.vpt, i = j % g.vpt;
+          const int row = p * g.rp + g.sub, kv = g.kl + i * g.lpr;
+          if (row >= g.nrows || kv >= g.vpr || j >= J) continue;  // padding: any in-bounds vector
+          int em, erow;
+          switch (st) {
+            case GS_QKV: {
+              const int gr = r0 + row, nq = D.hq * D.hd, nk = D.hkv * D.hd;
+              em = gr < nq ? M_Q : gr < nq + nk ? M_K : M_V;
+              erow = gr < nq ? gr : gr < nq + nk ? gr - nq : gr - nq - nk;
+              break;
+            }
+            case GS_WO: em = M_O; erow = r0 + row; break;
+            case GS_GATEUP: em = row < n ? M_GATE : M_UP; erow = r0 + (row < n ? row : row - n); break;
+            case GS_DOWN: em = M_DOWN; erow = r0 + row; break;
+            default: em = M_LM; erow = r0 + row; break;
+          }
+          if (m != em || e != (uint64_t)erow * K + (uint64_t)kv * 8) return fail("wrong vector", st, wg, t, j);
+          if (full) {
+            uint8_t& s = seen[m][(size_t)erow * (K / 8) + kv];
+            if (s) return fail("vector loaded twice", st, wg, t, j);
+            s = 1;
+          }
+        }
+      }
+    }
+  }
+  if (full)
+    for (int m = 0; m < M_COUNT; ++m)
+      for (uint8_t s : seen[m])
+        if (!s) return fail("vector never loaded", -1, -1, -1, m);
   return KIE_OK;
 }

@@ -83,6 +83,9 @@ SIGNATURES = {
     "kie_set_poll_timeout": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64]),
     "kie_set_abort_after": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_withhold": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_trace_words": (ctypes.c_size_t, [ctypes.c_void_p]),
+    "kie_set_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
+    "kie_check_tiling": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_int32, ctypes.c_int32]),
     "kie_gemv_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
@@ -124,6 +127,10 @@ def make_config(shape, max_seq: int) -> kie_config:
 
 def validate(cfg: kie_config) -> int:
     return lib().kie_config_validate(ctypes.byref(cfg))
+
+
+def check_tiling(cfg: kie_config, grid: int, full: bool) -> int:
+    return lib().kie_check_tiling(ctypes.byref(cfg), int(grid), 1 if full else 0)
 
 
 def workspace_bytes(cfg: kie_config) -> int:
@@ -242,6 +249,15 @@ class Engine:
 
     def set_abort_after(self, steps: int):
         _check(lib().kie_set_abort_after(self._h, int(steps)), "kie_set_abort_after")
+
+    def trace_words(self) -> int:
+        return int(lib().kie_trace_words(self._h))
+
+    def set_trace(self, buf: Optional[torch.Tensor], step: int = 0):
+        """buf: int64 device tensor of trace_words() entries, or None to stop."""
+        _check(lib().kie_set_trace(self._h, ctypes.c_void_p(_dptr(buf)) if buf is not None else None, int(step)),
+               "kie_set_trace")
+        self._trace_buf = buf
 
     def set_withhold(self, wg: int):
         _check(lib().kie_set_withhold(self._h, int(wg)), "kie_set_withhold")

@@ -216,16 +216,18 @@ kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_steps);
 kie_status kie_set_withhold(kie_engine* e, int32_t wg);
 
 /* Per-token timeline.  kie_trace_words(e) = uint64 words a trace buffer
- * needs: (n_layers*6 + 2) slots x grid work-groups x 3 stamps.  After
+ * needs: (n_layers*6 + 2) slots x grid work-groups x 4 stamps.  After
  * kie_set_trace(e, buf, step), every persistent launch of the engine stamps
  * loop iteration `step` (relative to the launch) into buf: for slot s (layer l
  * stage k at s = 6*l + k with k = 0 QKV, 1 attention, 2 merge, 3 Wo,
- * 4 gate/up, 5 down; then s = 6*L LM head, 6*L + 1 token gather) and
- * work-group w, buf[(s*grid + w)*3 + j] holds the 100 MHz real-time counter at
- * stage entry (j = 0), when the stage's input had arrived (j = 1; equals the
- * exit stamp position for the merge stage, which has no separate wait) and at
- * stage exit (j = 2).  Thread 0 of each work-group writes them; other entries
- * are left untouched.  buf = NULL turns tracing off (the default). */
+ * 4 gate/up, 5 down; then s = 6*L LM head, 6*L + 1 step tail: partial
+ * published / partials gathered / exchange set recycled / token known) and
+ * work-group w, buf[(s*grid + w)*4 + j] holds the 100 MHz real-time counter at
+ * stage entry (j = 0), when the stage's input had arrived (j = 1), when its
+ * arithmetic was done (j = 2) and at stage exit (j = 3).  Thread 0 of each
+ * work-group writes them (the recycling stamp: thread 256); entries a
+ * work-group does not reach are left untouched.  buf = NULL turns tracing off
+ * (the default). */
 size_t kie_trace_words(const kie_engine* e);
 kie_status kie_set_trace(kie_engine* e, uint64_t* trace_dev, int32_t step);
 

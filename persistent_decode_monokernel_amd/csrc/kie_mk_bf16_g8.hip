@@ -1,0 +1,12 @@
+// Instantiations of the persistent decode kernel: bf16, 8 query heads per KV head.
+#include "kie_monokernel.hpp"
+
+namespace kie {
+const void* monokernel_fn_bf16_g8(int vd, int vf) {
+  if (vd == 0 && vf == 1) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 8, 0, 1>);
+  if (vd == 1 && vf == 1) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 8, 1, 1>);
+  if (vd == 1 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 8, 1, 2>);
+  if (vd == 1 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 8, 1, 4>);
+  return nullptr;
+}
+}  // namespace kie

@@ -50,10 +50,26 @@ __device__ __forceinline__ T* opaque_s(T* p) {
   return p;
 }
 
-// Timeline stamp (thread 0 of the work-group; only on the traced step).
-__device__ __forceinline__ void stamp(uint64_t* tr, int slot, int k, int t) {
-  if (tr && t == 0) tr[((size_t)slot * gridDim.x + blockIdx.x) * 3 + k] = __builtin_amdgcn_s_memrealtime();
+// Timeline stamp k of a slot, by thread `who` of the work-group (only on the
+// traced step).  k: 0 entry, 1 input arrived, 2 compute done, 3 exit.
+__device__ __forceinline__ void stamp(uint64_t* tr, int slot, int k, int t, int who = 0) {
+  if (tr && t == who)
+    tr[((size_t)slot * gridDim.x + blockIdx.x) * kTraceStamps + k] = __builtin_amdgcn_s_memrealtime();
 }
+
+// Wait until every store this thread issued has been performed.  Exchange and
+// KV-cache stores are agent-scope (sc1, written through to memory), so once
+// they are acknowledged any later publication is ordered after them for every
+// other work-group; no cache write-back is needed (a release fence would write
+// back this XCD's whole L2).
+__device__ __forceinline__ void drain_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt unconstrained
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Issue the first kDepth vectors of the next GEMV stage into the ring.
+__device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np);
 
 // ---------------------------------------------------------------------------
 // LDS view
@@ -232,7 +248,8 @@ __device__ __forceinline__ void gv_park(float acc, int p, const StagePlan& g, fl
 // there is none), so the weight stream does not stop at the hand-off.
 template <int DT, int VPT, bool WIDE, class Prep>
 __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv, int t,
-                                     uint4 (&ring)[kDepth], bool prefilled, const StagePlan next) {
+                                     uint4 (&ring)[kDepth], bool prefilled, const StagePlan next, uint64_t* tr,
+                                     int slot) {
   const int J = g.passes() * VPT;
   const int Jp = (J + kDepth - 1) / kDepth * kDepth;
   if (Jp > 0 && !prefilled) {
@@ -285,6 +302,7 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
 #pragma unroll
     for (int i = 0; i < kDepth; ++i) ring[i] = ldw(next.addr(i));
   }
+  stamp(tr, slot, 2, t);
   __syncthreads();
   for (int r = t; r < g.nrows; r += kThreads) {
     float y = 0.f;
@@ -295,13 +313,29 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
   return true;
 }
 
+__device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np) {
+  if (np.nrows > 0) {
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(np.addr(i));
+  }
+}
+
+// GEMV of a width class fixed at compile time: VC = 0 for K < 512 (rows of
+// 32 lanes), else the vectors per thread per row (1, 2 or 4).
+template <int DT, int VC, class Prep>
+__device__ __forceinline__ bool gemv_cls(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv,
+                                         int t, uint4 (&ring)[kDepth], bool prefilled, uint64_t* tr, int slot) {
+  return gemv<DT, (VC > 0 ? VC : 1), (VC > 0)>(g, prep, xs, red, yv, t, ring, prefilled, StagePlan{}, tr, slot);
+}
+
 template <int DT, class Prep>
 __device__ __forceinline__ bool gemv_any(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv,
-                                         int t, uint4 (&ring)[kDepth], bool prefilled, const StagePlan next) {
-  if (g.vpr < 64) return gemv<DT, 1, false>(g, prep, xs, red, yv, t, ring, prefilled, next);
-  if (g.vpt == 1) return gemv<DT, 1, true>(g, prep, xs, red, yv, t, ring, prefilled, next);
-  if (g.vpt == 2) return gemv<DT, 2, true>(g, prep, xs, red, yv, t, ring, prefilled, next);
-  return gemv<DT, 4, true>(g, prep, xs, red, yv, t, ring, prefilled, next);
+                                         int t, uint4 (&ring)[kDepth], bool prefilled, const StagePlan next,
+                                         uint64_t* tr = nullptr, int slot = 0) {
+  if (g.vpr < 64) return gemv<DT, 1, false>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpt == 1) return gemv<DT, 1, true>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpt == 2) return gemv<DT, 2, true>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  return gemv<DT, 4, true>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
 }
 
 
@@ -326,7 +360,7 @@ __device__ __forceinline__ StagePlan plan_stage(const Params& P, int l, int st, 
 // QKV projection: rows [r0, r1) of the stacked [Wq; Wk; Wv] (contiguous row
 // segments of the three matrices), published unrotated in fp32.  Input x_l:
 // LDS xres (layer 0: the embedding) or polled from the previous layer's xout.
-template <int DT>
+template <int DT, int VD>
 __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 0;
@@ -343,10 +377,10 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
     stamp(tr, slot, 1, c.t);
     return true;
   };
-  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, l > 0, StagePlan{})) return false;
+  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, l > 0, tr, slot)) return false;
   uint32_t* dst = X + P.xl.qkv + (size_t)l * N;
   for (int r = c.t; r < r1 - r0; r += kThreads) xst32(dst + r0 + r, __float_as_uint(c.s.yv[r]));
-  stamp(tr, slot, 2, c.t);
+  stamp(tr, slot, 3, c.t);
   return true;
 }
 
@@ -358,11 +392,15 @@ __device__ __forceinline__ void attn_chunking(const Params& P, int n, int& CL, i
 
 // Online-softmax state update with one more score s and value row v:
 // (m, l, o) -> (max(m, s), l e^(m-m') + e^(s-m'), o e^(m-m') + e^(s-m') v).
-__device__ __forceinline__ float safe_exp_diff(float a, float m) { return a == -INFINITY ? 0.f : expf(a - m); }
+// Softmax statistics are kept in base 2: scores are scaled by log2(e)/sqrt(hd)
+// so that exp(s - m) = exp2(s' - m'), one v_exp_f32 (about 1 ulp).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float safe_exp_diff(float a, float m) { return a == -INFINITY ? 0.f : fast_exp2(a - m); }
 
 // Split-KV attention (flash-decoding): unit (KV head g, chunk c) computes, for
 // the G query heads that read head g, the partial softmax statistics over the
-// chunk's positions: m = max score, l = sum exp(s - m), o = sum exp(s - m) v.
+// chunk's positions: m = max score, l = sum exp(s - m), o = sum exp(s - m) v
+// (m kept in base-2 units, see fast_exp2).
 // Rotary embedding of q and of the new k happens in registers right after the
 // poll; the unit whose chunk holds the current position also appends the
 // (rotated k, v) row to the KV cache.  Positions are spread over lane groups
@@ -386,7 +424,7 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
   const int PP = kThreads / LPP;          // positions per pass
   const int grp = t / LPP, e8 = (t % LPP) * 8;
   const int wave = t >> 6, lane = t & 63;
-  const float scale = 1.0f / sqrtf((float)hd);
+  const float scale = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
   float* qs = c.s.scr;                                    // [G][hd] rotated queries
   uint16_t* kv16 = reinterpret_cast<uint16_t*>(qs + G * hd);  // [2][hd] new row as stored
   float* wml = qs + G * hd + hd;                          // [kWaves][G][2] per-wave (m, l)
@@ -494,9 +532,9 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
         float sd = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) sd += q8[e] * kf[e];
-        sd = ((LPP == 16) ? sum16(sd) : sum8(sd)) * scale;
+        sd = (hd == 128 ? sum16(sd) : sum8(sd)) * scale;
         const float mn = fmaxf(mx, sd);
-        const float fo = safe_exp_diff(mx, mn), fp = expf(sd - mn);
+        const float fo = safe_exp_diff(mx, mn), fp = fast_exp2(sd - mn);
         ls = ls * fo + fp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = o[e] * fo + fp * vf[e];
@@ -522,6 +560,7 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
         }
       }
     }
+    stamp(tr, slot, 2, t);
     __syncthreads();
     // merge the waves and publish (m, l, o) of each head for this chunk
     uint32_t* att = X + P.xl.att;
@@ -543,7 +582,7 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
     }
     __syncthreads();
   }
-  stamp(tr, slot, 2, t);
+  stamp(tr, slot, 3, t);
   return true;
 }
 
@@ -580,15 +619,16 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
       }
       const float mc = lo_f(mlv), lc = hi_f(mlv);
       const float mn = fmaxf(m, mc);
-      const float a = expf(m - mn), b = expf(mc - mn);
+      const float a = safe_exp_diff(m, mn), b = fast_exp2(mc - mn);
       ls = ls * a + lc * b;
       const float oc[8] = {lo_f(o01), hi_f(o01), lo_f(o23), hi_f(o23), lo_f(o45), hi_f(o45), lo_f(o67), hi_f(o67)};
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = o[e] * a + oc[e] * b;
       m = mn;
     }
+    stamp(tr, slot, 1, c.t);
     const float M = wave_max(m);
-    const float f = (m == -INFINITY) ? 0.f : expf(m - M);
+    const float f = safe_exp_diff(m, M);
     ls = sum64_tail(ls * f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = sum64_tail(o[e] * f);
@@ -602,12 +642,12 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
     }
   }
   const bool failed = any_failed(!ok);
-  stamp(tr, slot, 2, c.t);
+  stamp(tr, slot, 3, c.t);
   return !failed;
 }
 
 // x_mid = x_l + Wo a  (rows split over work-groups)
-template <int DT>
+template <int DT, int VD>
 __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 3;
@@ -622,16 +662,17 @@ __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* 
     return r;
   };
   const StagePlan np = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
-  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, false, np)) return false;
+  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, false, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xmid + (size_t)l * d;
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
-  stamp(tr, slot, 2, c.t);
+  ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
+  stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // h = silu(Wg n) * (Wu n), n = RMSNorm(x_mid) * g_ffn
-template <int DT>
+template <int DT, int VD>
 __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 4;
@@ -648,18 +689,19 @@ __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32
     return true;
   };
   const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
-  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, np)) return false;
+  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.h + (size_t)l * F;
   for (int f = c.t; f < nf; f += kThreads) {
     const float gt = c.s.yv[f], up = c.s.yv[nf + f];
     xst32(dst + f0 + f, __float_as_uint(gt / (1.0f + expf(-gt)) * up));
   }
-  stamp(tr, slot, 2, c.t);
+  ring_prefetch(ring, np);
+  stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // x_next = x_mid + Wd h
-template <int DT>
+template <int DT, int VF>
 __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 5;
@@ -675,11 +717,12 @@ __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t
   };
   const StagePlan np = l + 1 < P.L ? plan_stage(P, l + 1, GS_QKV, c.t, c.wg, c.nb)
                                    : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
-  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, np)) return false;
+  if (!gemv_cls<DT, VF>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xout + (size_t)l * d;
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
-  stamp(tr, slot, 2, c.t);
+  ring_prefetch(ring, np);
+  stamp(tr, slot, 3, c.t);
   return true;
 }
 
@@ -719,7 +762,7 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, const Lds& s, int
 
 // LM head on this work-group's vocabulary rows; logits optionally written.
 // The host guarantees ceil(V / grid) rows fit the LDS partial-sum buffers.
-template <int DT>
+template <int DT, int VD>
 __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, float* logits, float& best_v,
                                      int& best_i, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
@@ -735,7 +778,7 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
     stamp(tr, slot, 1, c.t);
     return true;
   };
-  if (!gemv_any<DT>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, StagePlan{})) return false;
+  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   float bv = -INFINITY;
   int bi = 0x7FFFFFFF;
   for (int r = c.t; r < v1 - v0; r += kThreads) {
@@ -749,7 +792,7 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
   block_argmax(bv, bi, c.s, c.t);
   best_v = bv;
   best_i = bi;
-  stamp(tr, slot, 2, c.t);
+  stamp(tr, slot, 3, c.t);
   return true;
 }
 
@@ -758,9 +801,10 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
 // work-group finished reading it before publishing its partial of that step,
 // and this work-group has consumed all those partials.  The next writes into
 // Xr happen two steps later, by work-groups that have seen this work-group's
-// next partial, which is published after a release fence that covers these
+// next partial, which is published only after these stores were performed
 // stores.
-__device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr, int nch_prev, int t_lo) {
+__device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr, int nch_prev, int t_lo,
+                                     uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
   const Params& P = c.P;
   if (c.t < t_lo) return;
@@ -781,6 +825,7 @@ __device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr,
       for (uint32_t k = tt; k < per; k += nt) xst64(base + 2 * (size_t)k, sent2);
     }
   }
+  stamp(tr, P.L * kStagesPerLayer + 1, 2, c.t, t_lo);
 }
 
 // Gather the per-work-group (max, index) partials -> the greedy token.  Every
@@ -811,14 +856,14 @@ __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* 
   block_argmax(gv, gi, c.s, c.t);
   // NaN logits never win a comparison: keep the index inside the vocabulary
   tok = (gi >= 0 && gi < P.V) ? gi : 0;
-  stamp(tr, slot, 2, c.t);
+  stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // ---------------------------------------------------------------------------
 // The persistent kernel
 // ---------------------------------------------------------------------------
-template <int DT, int G>
+template <int DT, int G, int VD, int VF>
 __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restrict__ Pp) {
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x, wg = blockIdx.x;
@@ -840,9 +885,9 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       __syncthreads();
     }
     for (int l = 0; l < L && ok; ++l) {
-      ok = st_qkv<DT>(Pp, smem, l, X, tr, ring) && st_attn<DT, G>(Pp, smem, l, pos, X, tr) &&
-           st_merge<DT>(Pp, smem, l, pos, X, tr) && st_wo<DT>(Pp, smem, l, X, tr, ring) &&
-           st_gateup<DT>(Pp, smem, l, X, tr, ring) && st_down<DT>(Pp, smem, l, X, tr, ring);
+      ok = st_qkv<DT, VD>(Pp, smem, l, X, tr, ring) && st_attn<DT, G>(Pp, smem, l, pos, X, tr) &&
+           st_merge<DT>(Pp, smem, l, pos, X, tr) && st_wo<DT, VD>(Pp, smem, l, X, tr, ring) &&
+           st_gateup<DT, VD>(Pp, smem, l, X, tr, ring) && st_down<DT, VF>(Pp, smem, l, X, tr, ring);
     }
     if (!ok) break;
     float bv = 0.f;
@@ -851,14 +896,14 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       const Params& Q = *opaque_s(Pp);
       if (!Q.lm_last_only || s == Q.n_steps - 1) {
         float* lg = Q.logits ? Q.logits + (size_t)(Q.lm_last_only ? 0 : s) * Q.V : nullptr;
-        if (!st_lmhead<DT>(Pp, smem, X, lg, bv, bi, tr, ring)) {
+        if (!st_lmhead<DT, VD>(Pp, smem, X, lg, bv, bi, tr, ring)) {
           ok = false;
           break;
         }
       }
     }
-    // publish this step's partial after a release of everything this step wrote
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // publish this step's partial once everything this step wrote is performed
+    drain_stores();
     __syncthreads();
     if (t == 0 && wg != Pp->withhold_wg) xst64(X + Pp->xl.arg + 2 * wg, pack2f(bv, __int_as_float(bi)));
     // the upper half of the work-group recycles the previous step's exchange
@@ -866,13 +911,12 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     if (s >= 1) {
       int CL, nch;
       attn_chunking(*Pp, pos, CL, nch);
-      reset_set(Pp, smem, Pp->xch + (size_t)((s + 2) % kRingSets) * Pp->xl.words, nch, kThreads / 2);
+      reset_set(Pp, smem, Pp->xch + (size_t)((s + 2) % kRingSets) * Pp->xl.words, nch, kThreads / 2, tr);
     }
     if (!gather_token(Pp, smem, X, tok, tr)) {
       ok = false;
       break;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (wg == 0 && t == 0) Pp->tok_out[s] = tok;
     done = s + 1;
     if (Pp->eos_id >= 0 && tok == Pp->eos_id) break;

@@ -9,13 +9,14 @@ constexpr int kThreads = 512;            // threads per work-group (8 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxWG = 1024;             // upper bound on the persistent grid
 constexpr int kRingSets = 3;             // exchange sets rotating over decode steps
-constexpr int kClMin = 64;               // shortest split-KV chunk (positions)
+constexpr int kClMin = 16;               // shortest split-KV chunk (positions)
 constexpr int kAttnUnits = 256;          // target (KV head, chunk) units per layer
 constexpr int kRedCap = 8192;            // LDS floats for per-wave GEMV partial sums
 constexpr int kYCap = 1024;              // LDS floats for finished GEMV rows
 constexpr int kDepth = 16;               // weight vectors in flight per thread
 constexpr uint32_t kSent = 0xFFFFFFFFu;  // NaN pattern that marks "not written yet"
 constexpr int kStagesPerLayer = 6;       // qkv, attn, merge, wo, gate/up, down
+constexpr int kTraceStamps = 4;          // per (slot, work-group): entry, input, compute done, exit
 
 // per-layer weight slots in the device pointer table
 enum : int {
@@ -61,9 +62,10 @@ struct Params {
   // launch
   int pos0, n_steps, eos_id, in_tok, abort_after, lm_last_only, withhold_wg;
   // per-token timeline: step `trace_step` of the launch is stamped into
-  // trace[((slot) * grid + wg) * 3 + k], slot = layer * kStagesPerLayer + stage
-  // (then kStagesPerLayer*L + {0: LM head, 1: token gather}); k = 0 entry,
-  // 1 input ready, 2 exit; 100 MHz real-time counter ticks.
+  // trace[((slot) * grid + wg) * kTraceStamps + k], slot = layer *
+  // kStagesPerLayer + stage (then kStagesPerLayer*L + {0: LM head, 1: step
+  // tail}); k = 0 entry, 1 input arrived, 2 compute done, 3 exit; ticks of the
+  // 100 MHz real-time counter.
   uint64_t* trace;
   int trace_step;
   uint64_t timeout;           // poll deadline, ticks of the 100 MHz counter

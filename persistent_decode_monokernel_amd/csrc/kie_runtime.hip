@@ -14,8 +14,14 @@
 #include "kie_tiling.hpp"
 
 namespace kie {
-const void* monokernel_fn_f16(int group);
-const void* monokernel_fn_bf16(int group);
+const void* monokernel_fn_f16_g1(int vd, int vf);
+const void* monokernel_fn_f16_g2(int vd, int vf);
+const void* monokernel_fn_f16_g4(int vd, int vf);
+const void* monokernel_fn_f16_g8(int vd, int vf);
+const void* monokernel_fn_bf16_g1(int vd, int vf);
+const void* monokernel_fn_bf16_g2(int vd, int vf);
+const void* monokernel_fn_bf16_g4(int vd, int vf);
+const void* monokernel_fn_bf16_g8(int vd, int vf);
 const void* gemv_probe_fn(int dtype);
 hipError_t launch_fill(uint32_t* p, uint64_t n, uint32_t v, hipStream_t st);
 }  // namespace kie
@@ -123,9 +129,25 @@ LdsPlan lds_plan(const kie_config& c) {
   return p;
 }
 
+// GEMV width class of an input width K: 0 for K < 512 (32 lanes per row),
+// else the vectors each thread reads per row (1, 2 or 4).
+int width_class(int K) {
+  const int vpr = K / 8;
+  return vpr < 64 ? 0 : vpr <= kThreads ? 1 : vpr <= 2 * kThreads ? 2 : 4;
+}
+
+// The kernel instance for a shape: dtype, query heads per KV head, width class
+// of d_model (= that of n_heads*head_dim) and of d_ffn.
 const void* monokernel_fn(const kie_config& c) {
-  const int G = c.n_heads / c.n_kv_heads;
-  return c.dtype == KIE_F16 ? monokernel_fn_f16(G) : monokernel_fn_bf16(G);
+  const int G = c.n_heads / c.n_kv_heads, vd = width_class(c.d_model), vf = width_class(c.d_ffn);
+  const bool f16 = c.dtype == KIE_F16;
+  switch (G) {
+    case 1: return f16 ? monokernel_fn_f16_g1(vd, vf) : monokernel_fn_bf16_g1(vd, vf);
+    case 2: return f16 ? monokernel_fn_f16_g2(vd, vf) : monokernel_fn_bf16_g2(vd, vf);
+    case 4: return f16 ? monokernel_fn_f16_g4(vd, vf) : monokernel_fn_bf16_g4(vd, vf);
+    case 8: return f16 ? monokernel_fn_f16_g8(vd, vf) : monokernel_fn_bf16_g8(vd, vf);
+  }
+  return nullptr;
 }
 
 }  // namespace
@@ -185,6 +207,11 @@ extern "C" kie_status kie_config_validate(const kie_config* c) {
   if (G != 1 && G != 2 && G != 4 && G != 8) return KIE_ERR_UNSUPPORTED;
   if (c->n_kv_heads > kAttnUnits) return KIE_ERR_UNSUPPORTED;
   if (!k_ok(c->d_model) || !k_ok(c->n_heads * c->head_dim) || !k_ok(c->d_ffn)) return KIE_ERR_UNSUPPORTED;
+  // compiled kernel instances: d_model <= 4096 with n_heads*head_dim in the
+  // same width class, d_ffn >= 512
+  if (width_class(c->d_model) > 1 || width_class(c->n_heads * c->head_dim) != width_class(c->d_model) ||
+      width_class(c->d_ffn) == 0 || (width_class(c->d_model) == 0 && width_class(c->d_ffn) != 1))
+    return KIE_ERR_UNSUPPORTED;
   if ((long long)c->vocab * c->d_model >= (1ll << 40)) return KIE_ERR_UNSUPPORTED;
   if (lds_plan(*c).bytes > 160 * 1024) return KIE_ERR_UNSUPPORTED;
   return KIE_OK;
@@ -557,7 +584,7 @@ extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t co
 
 extern "C" size_t kie_trace_words(const kie_engine* e) {
   if (!e) return 0;
-  return (size_t)(e->cfg.n_layers * kStagesPerLayer + 2) * e->grid * 3;
+  return (size_t)(e->cfg.n_layers * kStagesPerLayer + 2) * e->grid * kTraceStamps;
 }
 
 extern "C" kie_status kie_set_trace(kie_engine* e, uint64_t* trace_dev, int32_t step) {

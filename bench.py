@@ -57,6 +57,102 @@ def bytes_per_launch(s, pos0: int, n_steps: int) -> int:
     return tot
 
 
+# --------------------------------------------------------------------------
+# Counter-measured HBM traffic of the timed launch.
+#
+# Filled from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE) over the
+# default 2b command, each scaled by the same counter's reading for a plain
+# device-to-device copy of known size (--copy-probe).  Reported only while the
+# kernel sources hash to the value they were taken at.
+MEASURED_TRAFFIC = {
+    # kie_decode(1024) after a 512-token prefill, FETCH_SIZE x 2.0, WRITE_SIZE x 1.0
+    "2b": {"src_sha": "966ccaec1ef66885", "steps": 1024,
+           "fetch_bytes": 1850975564 * 1024 * 2, "write_bytes": 32315766 * 1024},
+}
+
+KERNEL_SRC_DIR = os.path.join(ROOT, "persistent_decode_monokernel_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SRC_DIR)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(ROOT, "include", "kie.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, steps: int):
+    m = MEASURED_TRAFFIC.get(workload)
+    if not m or m["steps"] != steps or m["src_sha"] != kernel_source_hash():
+        return None
+    return m["fetch_bytes"] + m["write_bytes"]
+
+
+def copy_probe(mib: int, reps: int = 3):
+    """Plain device-to-device copies of `mib` MiB (calibration for --pmc)."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n // 2, dtype=torch.float16, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)  # the runtime's device-to-device copy kernel
+        torch.neg(src, out=dst)  # an elementwise kernel: n bytes read, n written
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "reps": reps}), flush=True)
+
+
+def rocpd_summary(db: str, pattern: str = "monokernel"):
+    """Kernel statistics and the per-dispatch durations of the kernels matching
+    `pattern` from a rocprofv3 --kernel-trace database."""
+    import sqlite3
+
+    c = sqlite3.connect(db)
+    print("kernel statistics (all dispatches of the run):")
+    print(f"{'calls':>6} {'total ms':>12} {'avg ms':>12} {'pct':>6}  kernel")
+    for name, calls, tot_ns, avg_ns, pct in c.execute(
+            "select name, count(*), sum(end-start), avg(end-start), "
+            "100.0*sum(end-start)/(select sum(end-start) from kernels) from kernels "
+            "group by name order by sum(end-start) desc limit 8"):
+        print(f"{calls:>6} {tot_ns / 1e6:>12.3f} {avg_ns / 1e6:>12.3f} {pct:>6.2f}  {name[:90]}")
+    print(f"\ndispatches of kernels matching '{pattern}' in launch order:")
+    print(f"{'#':>3} {'dispatch':>8} {'grid':>8} {'block':>6} {'lds':>6} {'vgpr':>5} {'sgpr':>5} {'ms':>12}  kernel")
+    rows = list(c.execute(
+        "select dispatch_id, grid_x, workgroup_x, lds_size, vgpr_count, sgpr_count, end-start, name "
+        "from kernels where name like ? order by start", (f"%{pattern}%",)))
+    for i, (did, gx, wx, lds, vg, sg, dur, name) in enumerate(rows):
+        print(f"{i:>3} {did:>8} {gx:>8} {wx:>6} {lds:>6} {vg:>5} {sg:>5} {dur / 1e6:>12.3f}  {name[:60]}")
+    return rows
+
+
+def pmc_summary(csvs, pattern: str = "monokernel", copy_pattern: str = "copyBuffer|neg_kernel", copy_bytes: int = 0):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) from rocprofv3 --pmc CSVs, and
+    the byte factor implied by a copy dispatch of `copy_bytes` read + written."""
+    import csv
+
+    vals = {}
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+                vals.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    for (name, did), cv in sorted(vals.items(), key=lambda kv: kv[0][1]):
+        if pattern in name or any(p in name for p in copy_pattern.split("|")):
+            line = " ".join(f"{k}={v:.0f}" + ("KiB" if k.endswith("_SIZE") else "") for k, v in sorted(cv.items()))
+            if pattern not in name and copy_bytes:
+                fac = {k: copy_bytes / (v * 1024.0) for k, v in cv.items() if k.endswith("_SIZE") and v > 0}
+                line += "  bytes per counted byte: " + " ".join(f"{k}={f:.4f}" for k, f in fac.items())
+            print(f"dispatch {did:>6}  {name[:50]:<50} {line}")
+    return vals
+
+
 def cpu_baseline(shape, w_gpu, n_prompt: int, budget_s: float = 15.0):
     """Time the CPU oracle's incremental decode (as it stands) on a bounded sample."""
     import torch
@@ -96,11 +192,28 @@ def main():
     ap.add_argument("--workload", default="2b", choices=["tiny", "2b", "2b_long", "8b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--rocpd-summary", default=None, metavar="DB",
+                    help="only summarise a rocprofv3 kernel-trace database")
+    ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="CSV",
+                    help="only summarise rocprofv3 --pmc counter CSVs")
+    ap.add_argument("--copy-bytes", type=int, default=0, help="bytes read (= written) by the copy probe")
     args = ap.parse_args()
+    if args.rocpd_summary:
+        rocpd_summary(args.rocpd_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, copy_bytes=args.copy_bytes)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not an implemented path", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
 
@@ -171,7 +284,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, n_done),
         },
         "kernel": {
             "name": "kie::monokernel (persistent decode)",

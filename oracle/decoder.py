@@ -34,6 +34,13 @@ float64 at use; every sum, product, exp and square root is float64.  Matrix
 products use torch's float64 matmul (a library primitive) with no blocking or
 reordering beyond what the definition states.
 
+KV cache storage: exact float64 by default.  A cache may instead be given the
+model's 16-bit storage dtype (KVCache(store_dtype=...)): every appended key and
+value row is then rounded to that format once, as a model run at 16-bit
+precision keeps it (the pages state the 2B model's precision as FP16 as a
+whole: remio.ai, section "Dlaczego Kog idzie glebiej w wnioskowanie GPU").
+Everything else stays float64.
+
 Pins (tests/test_oracle_pins.py): brute-force scalar loops on tiny shapes,
 closed forms (RMSNorm energy, RoPE rotation values, softmax of known scores,
 silu values), invariants (RoPE norm preservation and relative-position
@@ -112,21 +119,32 @@ def matvec(W: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
 
 
 class KVCache:
-    """Per-layer float64 keys (already rotated) and values, [Hkv][n][hd] each."""
+    """Per-layer keys (already rotated) and values, [Hkv][n][hd] each, held as
+    float64.  store_dtype None keeps appended rows exact; a 16-bit dtype rounds
+    each appended row to it (the cache's storage format)."""
 
-    def __init__(self, n_layers: int, n_kv_heads: int, head_dim: int):
+    def __init__(self, n_layers: int, n_kv_heads: int, head_dim: int, store_dtype: Optional[torch.dtype] = None):
         self.k: List[torch.Tensor] = [torch.zeros((n_kv_heads, 0, head_dim), dtype=F64) for _ in range(n_layers)]
         self.v: List[torch.Tensor] = [torch.zeros((n_kv_heads, 0, head_dim), dtype=F64) for _ in range(n_layers)]
+        self.store_dtype = store_dtype
 
     @property
     def length(self) -> int:
         return int(self.k[0].shape[1])
 
+    def append(self, l: int, k: torch.Tensor, v: torch.Tensor):
+        """Append rows k, v [Hkv][n][hd] to layer l."""
+        if self.store_dtype is not None:
+            k = k.to(self.store_dtype).to(F64)
+            v = v.to(self.store_dtype).to(F64)
+        self.k[l] = torch.cat([self.k[l], k], dim=1)
+        self.v[l] = torch.cat([self.v[l], v], dim=1)
+
     @classmethod
-    def from_tensors(cls, k: torch.Tensor, v: torch.Tensor) -> "KVCache":
+    def from_tensors(cls, k: torch.Tensor, v: torch.Tensor, store_dtype: Optional[torch.dtype] = None) -> "KVCache":
         """From stored K, V arrays [n_layers][Hkv][n][hd] (converted exactly)."""
         L, hkv, _, hd = k.shape
-        c = cls(L, hkv, hd)
+        c = cls(L, hkv, hd, store_dtype)
         c.k = [to64(k[l]) for l in range(L)]
         c.v = [to64(v[l]) for l in range(L)]
         return c
@@ -178,8 +196,7 @@ def forward(w: Dict[str, object], shape, tokens: Sequence[int], cache: Optional[
         v = (xn @ to64(lw["wv"]).T).reshape(n, s.n_kv_heads, s.head_dim)
         q = apply_rope(q, cos, sin)
         k = apply_rope(k, cos, sin)
-        cache.k[l] = torch.cat([cache.k[l], k.transpose(0, 1)], dim=1)
-        cache.v[l] = torch.cat([cache.v[l], v.transpose(0, 1)], dim=1)
+        cache.append(l, k.transpose(0, 1), v.transpose(0, 1))
         o = attention(q, cache.k[l], cache.v[l], p0).reshape(n, s.n_heads * s.head_dim)
         x = x + o @ to64(lw["wo"]).T
         xn = rmsnorm(x, to64(lw["ffn_norm"]), s.rms_eps)

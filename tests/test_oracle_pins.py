@@ -213,6 +213,33 @@ def test_incremental_decode_equals_full_forward():
         assert oracle.greedy_token(full[len(prompt) - 1 + i]) == seq[i]
 
 
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_cache_storage_dtype_rounds_each_appended_row(dt):
+    """A cache stored in a 16-bit format holds exactly the rounded rows: layer 0's
+    keys and values depend on no attention output, so they must equal the
+    exact cache's layer-0 rows rounded to that format; incremental decode must
+    still equal the full causal pass under the same storage."""
+    shape = synth.small_shape(n_layers=2, d_model=32, n_heads=4, n_kv_heads=2, head_dim=8, d_ffn=64, vocab=61)
+    w = synth.make_weights(shape, 12, std=0.2)
+    prompt = synth.make_prompt(shape, 7, 13).tolist()
+    exact = oracle.KVCache(shape.n_layers, shape.n_kv_heads, shape.head_dim)
+    stored = oracle.KVCache(shape.n_layers, shape.n_kv_heads, shape.head_dim, store_dtype=dt)
+    oracle.forward(w, shape, prompt, exact)
+    oracle.forward(w, shape, prompt, stored)
+    assert torch.equal(stored.k[0], exact.k[0].to(dt).to(torch.float64))
+    assert torch.equal(stored.v[0], exact.v[0].to(dt).to(torch.float64))
+    assert not torch.equal(stored.k[0], exact.k[0])  # the rounding did happen
+    # later layers see rounded keys: close to, not equal to, the exact ones
+    assert torch.allclose(stored.k[1], exact.k[1], rtol=0, atol=0.05)
+    tok0, lg0, c = oracle.prefill(w, shape, prompt,
+                                  oracle.KVCache(shape.n_layers, shape.n_kv_heads, shape.head_dim, store_dtype=dt))
+    toks, lgs = oracle.greedy_decode(w, shape, c, tok0, 6)
+    full = oracle.forward(w, shape, prompt + [tok0] + toks[:-1],
+                          oracle.KVCache(shape.n_layers, shape.n_kv_heads, shape.head_dim, store_dtype=dt))
+    assert torch.allclose(full[len(prompt) - 1], lg0, atol=1e-12)
+    assert torch.allclose(full[len(prompt):], lgs, atol=1e-12)
+
+
 def test_teacher_forced_from_imported_cache():
     shape = synth.small_shape(n_layers=2, d_model=32, n_heads=4, n_kv_heads=4, head_dim=8, d_ffn=64, vocab=50)
     w = synth.make_weights(shape, 8, std=0.2)

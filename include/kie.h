@@ -66,9 +66,15 @@ typedef enum {
 
 typedef enum { KIE_F16 = 1, KIE_BF16 = 2 } kie_dtype;
 
-/* Model shape.  Supported: head_dim in {64, 128}; n_heads a multiple of
- * n_kv_heads; n_heads / n_kv_heads <= 8; d_model, n_heads*head_dim and d_ffn
- * multiples of 256; vocab >= 1; max_seq >= 1. */
+/* Model shape.  Supported (kie_config_validate() reports anything else as
+ * KIE_ERR_UNSUPPORTED):
+ *   head_dim in {64, 128}; n_heads / n_kv_heads in {1, 2, 4, 8}; n_kv_heads <= 256;
+ *   d_model and n_heads*head_dim powers of two in [256, 4096], both below 512
+ *   or both at least 512;
+ *   d_ffn a power of two in [512, 4096] or a multiple of 256 in (4096, 16384],
+ *   and at most 4096 when d_model is 256;
+ *   vocab * d_model < 2^40; the kernel's LDS plan within 160 KiB;
+ *   vocab >= 1; max_seq >= 1. */
 typedef struct {
   int32_t n_layers;
   int32_t d_model;
@@ -155,9 +161,12 @@ kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prom
  *   every executed step (parity mode; costs extra writes).
  * Requires a prefilled sequence and pos + n_steps <= max_seq (else
  * KIE_ERR_CAPACITY before any launch).  Repeated calls continue the sequence.
- * On KIE_ERR_TIMEOUT or KIE_ERR_ABORTED, tokens_host and n_generated hold the
- * steps that completed, and the sequence must be restarted by kie_prefill()
- * or kie_import_kv(). */
+ * On KIE_ERR_ABORTED (see kie_set_abort_after) tokens_host and n_generated
+ * hold the steps that completed and the sequence stays valid: pos advanced by
+ * n_generated and the last emitted token is pending, so decoding can go on.
+ * On KIE_ERR_TIMEOUT they hold the completed steps too, but the step that
+ * timed out may have left a partial KV-cache row: the sequence must be
+ * restarted by kie_prefill() or kie_import_kv() (KIE_ERR_STATE until then). */
 kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id, int32_t* tokens_host,
                       int32_t* n_generated, float* logits_dev);
 

@@ -187,6 +187,49 @@ __device__ __forceinline__ float dot8(const uint4& w, const uint4& x, float acc)
   }
   return acc;
 }
+// Activations fed to the dot2 unit sit in LDS as 16-byte vectors of 8
+// elements.  fp16: vector k holds inputs 8k..8k+7.  bf16 keeps only 8
+// significant bits, so an input x is stored as three bf16 terms
+// x = b0 + b1 + b2 (b0 = bf16(x), b1 = bf16(x - b0), b2 = bf16(x - b0 - b1);
+// each difference is exact in fp32): vector 3k holds the b0 of inputs
+// 8k..8k+7, 3k+1 their b1, 3k+2 their b2.  Three dot2 passes then see every
+// input to fp32 precision (the weights are exact), so a bf16 model's GEMVs
+// are as accurate as fp32 ones.
+template <int DT>
+constexpr int kActWords = DT == KIE_BF16 ? 3 : 1;  // 16-byte vectors per 8 inputs
+
+template <int DT>
+__device__ __forceinline__ void act_terms(float v, uint16_t (&b)[kActWords<DT>]) {
+  b[0] = to_16<DT>(v);
+  if constexpr (kActWords<DT> > 1) {
+    const float r1 = v - to_f32<DT>(b[0]);
+    b[1] = to_16<DT>(r1);
+    b[2] = to_16<DT>(r1 - to_f32<DT>(b[1]));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void act_store(uint16_t* xs, int i, float v) {
+  constexpr int AW = kActWords<DT>;
+  uint16_t b[AW];
+  act_terms<DT>(v, b);
+  const int o = (i >> 3) * 8 * AW + (i & 7);
+#pragma unroll
+  for (int a = 0; a < AW; ++a) xs[o + 8 * a] = b[a];
+}
+// Inputs 2p and 2p+1.
+template <int DT>
+__device__ __forceinline__ void act_store2(uint16_t* xs, int p, float x0, float x1) {
+  constexpr int AW = kActWords<DT>;
+  uint16_t b0[AW], b1[AW];
+  act_terms<DT>(x0, b0);
+  act_terms<DT>(x1, b1);
+  uint32_t* u = reinterpret_cast<uint32_t*>(xs);
+  const int o = (p >> 2) * 4 * AW + (p & 3);
+#pragma unroll
+  for (int a = 0; a < AW; ++a) u[o + 4 * a] = (uint32_t)b0[a] | ((uint32_t)b1[a] << 16);
+}
+
 template <int DT>
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   f[0] = to_f32<DT>(v.x & 0xFFFF); f[1] = to_f32<DT>(v.x >> 16);

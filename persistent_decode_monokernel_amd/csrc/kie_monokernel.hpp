@@ -76,7 +76,7 @@ __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const Stage
 // ---------------------------------------------------------------------------
 struct Lds {
   float* xres;     // fp32 residual stream copy [d]
-  uint16_t* xn;    // 16-bit activation fed to dot2 [Kmax]
+  uint16_t* xn;    // 16-bit activation fed to dot2 [Kmax] (bf16: three terms, see act_store)
   float* red;      // GEMV per-wave partial sums [kRedCap]
   float* yv;       // GEMV finished rows [kYCap]
   float* scr;      // attention scratch (aliases red/yv)
@@ -187,9 +187,7 @@ __device__ __forceinline__ bool poll_f32(const uint32_t* src, int n, float* dst,
 // Poll n fp32 words into LDS as 16-bit activations.
 template <int DT>
 __device__ __forceinline__ bool poll_to16(const uint32_t* src, int n, uint16_t* dst, const Watch& w, int t) {
-  return poll_words(src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) {
-    reinterpret_cast<uint32_t*>(dst)[i] = pack16<DT>(lo_f(v), hi_f(v));
-  });
+  return poll_words(src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) { act_store2<DT>(dst, i, lo_f(v), hi_f(v)); });
 }
 // xn = RMSNorm(x) * g, rounded to 16 bits.  Ends with a barrier.
 template <int DT>
@@ -199,7 +197,7 @@ __device__ __forceinline__ void rmsnorm_to16(const float* x, const uint16_t* g, 
   for (int i = t; i < n; i += kThreads) ss += x[i] * x[i];
   ss = block_sum(ss, misc, t);
   const float r = 1.0f / sqrtf(ss / (float)n + eps);
-  for (int i = t; i < n; i += kThreads) xn[i] = to_16<DT>(x[i] * r * to_f32<DT>(g[i]));
+  for (int i = t; i < n; i += kThreads) act_store<DT>(xn, i, x[i] * r * to_f32<DT>(g[i]));
   __syncthreads();
 }
 
@@ -259,18 +257,26 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
   if (!prep()) return false;
   const bool has_next = next.nrows > 0;
   if (Jp > 0) {
-    uint4 xr[VPT];
+    constexpr int AW = kActWords<DT>;
+    uint4 xr[AW][VPT];  // the input vectors (bf16: all three terms) this thread multiplies
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int kv = g.kl + i * g.lpr;
-      xr[i] = kv < g.vpr ? *reinterpret_cast<const uint4*>(xs + kv * 8) : make_uint4(0, 0, 0, 0);
+      const uint4* v = reinterpret_cast<const uint4*>(xs) + kv * AW;
+#pragma unroll
+      for (int a = 0; a < AW; ++a) xr[a][i] = kv < g.vpr ? v[a] : make_uint4(0, 0, 0, 0);
     }
+    auto dot = [&](const uint4& w, int i, float acc) {
+#pragma unroll
+      for (int a = AW - 1; a >= 0; --a) acc = dot8<DT>(w, xr[a][i % VPT], acc);  // small terms first
+      return acc;
+    };
     float acc = 0.f;
     int j0 = 0;
     for (; j0 + kDepth < Jp; j0 += kDepth) {
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {
-        acc = dot8<DT>(ring[i], xr[i % VPT], acc);
+        acc = dot(ring[i], i, acc);
         ring[i] = ldw(g.addr<VPT>(j0 + i + kDepth));
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
@@ -281,7 +287,7 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
     if (has_next) {
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {  // last block: drain, refill with the next stage
-        acc = dot8<DT>(ring[i], xr[i % VPT], acc);
+        acc = dot(ring[i], i, acc);
         ring[i] = ldw(next.addr(i));
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
@@ -291,7 +297,7 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
     } else {
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {  // last block: drain
-        acc = dot8<DT>(ring[i], xr[i % VPT], acc);
+        acc = dot(ring[i], i, acc);
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
           acc = 0.f;
@@ -940,7 +946,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
                                                           const uint16_t* x, float* y, int nvec) {
   extern __shared__ __align__(16) char smem[];
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* red = reinterpret_cast<float*>(smem + (size_t)cols * 2);
+  float* red = reinterpret_cast<float*>(smem + (size_t)cols * 2 * kActWords<DT>);
   float* yv = red + kRedCap;
   const int nb = gridDim.x, wg = blockIdx.x;
   const int r0 = split_lo(rows, nb, wg), r1 = split_lo(rows, nb, wg + 1);
@@ -949,9 +955,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
     const uint16_t* Wc = W + (size_t)(iv % ncopy) * rows * cols;
     StagePlan pl = plan_rows(r1 - r0, cols, t);
     pl.seg0 = Wc + (size_t)r0 * cols;
-    auto prep = [&]() -> bool {
+    auto prep = [&]() -> bool {  // the probe's input is 16-bit already: bf16 residuals are zero
       const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
-      for (int i = t; i < (cols >> 3); i += kThreads) reinterpret_cast<uint4*>(xs)[i] = src[i];
+      constexpr int AW = kActWords<DT>;
+      for (int i = t; i < (cols >> 3); i += kThreads) {
+        reinterpret_cast<uint4*>(xs)[i * AW] = src[i];
+        for (int a = 1; a < AW; ++a) reinterpret_cast<uint4*>(xs)[i * AW + a] = make_uint4(0, 0, 0, 0);
+      }
       __syncthreads();
       return true;
     };

@@ -120,7 +120,7 @@ LdsPlan lds_plan(const kie_config& c) {
   p.xres = 0;
   o = align_up((size_t)c.d_model * 4, 16);
   p.xn = (int)o;
-  o = align_up(o + (size_t)kmax * 2, 16);
+  o = align_up(o + (size_t)kmax * 2 * (c.dtype == KIE_BF16 ? 3 : 1), 16);  // bf16: three terms per input
   p.scr = (int)o;
   o = align_up(o + (gemv_scr > attn_scr ? gemv_scr : attn_scr), 16);
   p.misc = (int)o;
@@ -437,9 +437,9 @@ extern "C" kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id,
   if ((long long)e->pos + n_steps > e->cfg.max_seq) return KIE_ERR_CAPACITY;
   const int abort_after = e->abort_after;
   e->abort_after = -1;
-  if (n_steps == 0) {
+  if (n_steps == 0 || abort_after == 0) {  // nothing to run; the sequence is unchanged
     *n_generated = 0;
-    return KIE_OK;
+    return n_steps > 0 ? KIE_ERR_ABORTED : KIE_OK;
   }
   Params P = base_params(e);
   P.pos0 = e->pos;
@@ -556,7 +556,7 @@ extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t co
   KIE_HIP(hipGetDeviceProperties(&prop, dev));
   int grid = prop.multiProcessorCount;
   if (grid > rows) grid = rows;
-  const size_t lds = (size_t)cols * 2 + (size_t)(kRedCap + kYCap) * 4;
+  const size_t lds = (size_t)cols * 2 * (dtype == KIE_BF16 ? 3 : 1) + (size_t)(kRedCap + kYCap) * 4;
   const int max_rows = (rows + grid - 1) / grid;
   const int vpr = cols / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
   if ((long long)max_rows * nwr > kRedCap || max_rows > kYCap) return KIE_ERR_UNSUPPORTED;

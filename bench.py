@@ -151,6 +151,95 @@ def pmc_summary(csvs, pattern: str = "monokernel", copy_pattern: str = "copyBuff
     return vals
 
 
+def gemv_probe_bench(n_copies: int = 16):
+    """Isolated weight-streaming GEMV: each fp16 shape of the probe workload,
+    1000 fresh vectors in ONE persistent launch of the same GEMV engine the
+    decode stages use, over n_copies rotating weight copies (16 x 32 MiB = 512
+    MiB, beyond the 256 MB Infinity Cache) or one copy (cache-resident).
+    Algorithmic bytes per vector: the matrix, the input vector, the output."""
+    import torch
+
+    from persistent_decode_monokernel_amd import kie, synth
+
+    for (rows, cols), seed in zip(synth.GEMV_SHAPES, synth.GEMV_SEEDS):
+        for nc in (n_copies, 1):
+            W, x = synth.make_gemv(rows, cols, synth.GEMV_N_VEC, seed, n_copies=nc, device="cuda")
+            kie.gemv_probe(W, x[:8])  # warm-up
+            _, ms = kie.gemv_probe(W, x)
+            per = rows * cols * 2 + cols * 2 + rows * 4
+            gbs = per * synth.GEMV_N_VEC / (ms / 1e3) / 1e9
+            print(json.dumps({"gemv": f"{rows}x{cols} fp16", "copies": nc, "vectors": synth.GEMV_N_VEC,
+                              "kernel_ms": ms, "us_per_gemv": ms * 1e3 / synth.GEMV_N_VEC, "GB/s": gbs,
+                              "frac_of_8000": gbs / HBM_PEAK_GBS,
+                              "note": "HBM stream" if nc > 1 else "Infinity-Cache resident"}), flush=True)
+            del W, x
+            torch.cuda.empty_cache()
+
+
+STAGES = ("qkv", "attention", "merge", "wo", "gate/up", "down")
+
+
+def timeline(wl, step: int = 10, n_decode: int = 32):
+    """Per-token timeline of one decode step (the step-th of a kie_decode(n_decode)
+    launch after the workload's prompt): for every stage, the median over
+    work-groups of the time from stage entry until its input had arrived (the
+    hand-off wait), of the arithmetic, and of the tail (output stores, next
+    stage's prefetch), plus the stage's span on the critical path (last
+    work-group's exit minus the previous stage's last exit), averaged over the
+    layers.  Stamps come from the kernel's 100 MHz real-time counter."""
+    import numpy as np
+    import torch
+
+    from persistent_decode_monokernel_amd import kie, synth
+
+    s = wl.shape
+    dev = torch.device("cuda:0")
+    w = synth.make_weights(s, wl.weight_seed, device=dev)
+    P = wl.n_prompt
+    eng = kie.Engine(s, max_seq=P + n_decode, device=dev)
+    eng.load_weights(w)
+    eng.prefill(synth.make_prompt(s, P, wl.prompt_seed).tolist())
+    buf = torch.zeros(eng.trace_words(), dtype=torch.int64, device=dev)
+    eng.set_trace(buf, step)
+    eng.decode(n_decode)
+    ms = eng.info().last_kernel_ms
+    G = eng.info().grid
+    tr = buf.cpu().numpy().astype(np.float64).reshape(-1, G, 4) / 100.0  # microseconds
+    L = s.n_layers
+    print(f"workload {wl.name}: kie_decode({n_decode}) after {P} prompt positions, {ms:.2f} ms "
+          f"({ms / n_decode * 1e3:.1f} us/token); timeline of step {step}, grid {G}")
+    t0 = tr[0, :, 0].min()
+    t_end = tr[6 * L + 1, :, 3].max()
+    print(f"step span {t_end - t0:.1f} us")
+    print(f"{'stage':10s} {'busy WGs':>8s} {'wait':>7s} {'compute':>8s} {'tail':>7s} {'critical span':>14s}   (us, median over "
+          f"work-groups, mean over layers 1..{L - 1})")
+    tot_wait = tot_span = 0.0
+    for k in range(6):
+        waits, comps, tails, spans, busy = [], [], [], [], []
+        for l in range(1, L):
+            x = tr[6 * l + k]
+            ok = (x[:, 3] - x[:, 0]) > (0.5 if k in (1, 2) else -1.0)  # attention/merge: work-groups with units
+            x = x[ok]
+            busy.append(len(x))
+            done = x[:, 2] if k != 2 else x[:, 3]  # the merge stamps no separate "arithmetic done"
+            waits.append(np.median(x[:, 1] - x[:, 0]))
+            comps.append(np.median(done - x[:, 1]))
+            tails.append(np.median(x[:, 3] - done))
+            spans.append(tr[6 * l + k, :, 3].max() - tr[6 * l + k - 1, :, 3].max())
+        tot_wait += np.mean(waits)
+        tot_span += np.mean(spans)
+        print(f"{STAGES[k]:10s} {np.mean(busy):8.0f} {np.mean(waits):7.2f} {np.mean(comps):8.2f} {np.mean(tails):7.2f} "
+              f"{np.mean(spans):14.2f}")
+    x = tr[6 * L]
+    print(f"{'lm head':10s} {G:8d} {np.median(x[:, 1] - x[:, 0]):7.2f} {np.median(x[:, 2] - x[:, 1]):8.2f} "
+          f"{np.median(x[:, 3] - x[:, 2]):7.2f} {x[:, 3].max() - tr[6 * L - 1, :, 3].max():14.2f}")
+    x = tr[6 * L + 1]  # gather: entry, partials gathered, (recycling done), token known
+    print(f"{'step tail':10s} {G:8d} {np.median(x[:, 1] - x[:, 0]):7.2f} {np.median(x[:, 3] - x[:, 1]):8.2f} "
+          f"{0.0:7.2f} {x[:, 3].max() - tr[6 * L, :, 3].max():14.2f}   (wait = all argmax partials gathered)")
+    print(f"per layer: critical span {tot_span:.2f} us, of which hand-off waits (sum of stage medians) {tot_wait:.2f} us "
+          f"= {tot_wait / tot_span:.0%}")
+
+
 def cpu_baseline(shape, w_gpu, n_prompt: int, budget_s: float = 15.0):
     """Time the CPU oracle's incremental decode (as it stands) on a bounded sample."""
     import torch
@@ -197,6 +286,9 @@ def main():
     ap.add_argument("--pmc-summary", nargs="+", default=None, metavar="CSV",
                     help="only summarise rocprofv3 --pmc counter CSVs")
     ap.add_argument("--copy-bytes", type=int, default=0, help="bytes read (= written) by the copy probe")
+    ap.add_argument("--gemv", action="store_true", help="only run the isolated GEMV probe workload")
+    ap.add_argument("--timeline", type=int, default=None, metavar="STEP",
+                    help="only print the per-stage timeline of decode step STEP of a 32-step launch")
     args = ap.parse_args()
     if args.rocpd_summary:
         rocpd_summary(args.rocpd_summary)
@@ -211,6 +303,14 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.gemv:
+        gemv_probe_bench()
+        return
+    if args.timeline is not None:
+        from persistent_decode_monokernel_amd import synth
+
+        timeline(synth.WORKLOADS[args.workload], step=args.timeline)
         return
 
     import torch

@@ -229,6 +229,75 @@ __device__ __forceinline__ void gv_park(float acc, int p, const StagePlan& g, fl
   }
 }
 
+// Weight-vector addressing for tilings whose rows span whole waves (K >= 512):
+// the row a wave reads is wave-uniform, so the row's address (segment select,
+// row * K) is scalar arithmetic and each lane only adds its fixed byte offset
+// within the row -- no per-vector vector-ALU address work.  Same mapping as
+// StagePlan::addr (the host checks that one).
+struct WideRows {
+  // Row r (local) of the work-group lives at b0 + r * rb, plus d1 once r >=
+  // n0 and d2 once r >= n01 (the later segments' bases, shifted by their first
+  // local row; plain integers, so the select stays arithmetic on registers).
+  uint64_t b0, d1, d2;
+  int n0, n01, nrows, rp, sub, vsh;
+  uint32_t rb;      // bytes per row
+  uint32_t lo[4];   // this lane's byte offset of its vector i of a row (padding columns: 0)
+  __device__ __forceinline__ const char* row(int r) const {
+    r = r < nrows ? r : 0;
+    const uint64_t m1 = r >= n0 ? ~0ull : 0ull, m2 = r >= n01 ? ~0ull : 0ull;
+    return reinterpret_cast<const char*>(b0 + (m1 & d1) + (m2 & d2) + (uint64_t)(uint32_t)r * rb);
+  }
+  // vector i of the row read in pass p
+  __device__ __forceinline__ uint4 load(int p, int i) const {
+    return ldw(reinterpret_cast<const uint16_t*>(row(p * rp + sub) + lo[i]));
+  }
+  // j-th vector with the vectors-per-row of the plan (runtime)
+  __device__ __forceinline__ uint4 load_j(int j) const {
+    const int i = j & ((1 << vsh) - 1);
+    const uint32_t o = i == 0 ? lo[0] : i == 1 ? lo[1] : i == 2 ? lo[2] : lo[3];
+    return ldw(reinterpret_cast<const uint16_t*>(row((j >> vsh) * rp + sub) + o));
+  }
+};
+
+// The plan's row fields are work-group uniform, but part of them comes out of
+// vector-ALU integer division; reading them back with readfirstlane keeps the
+// row arithmetic on the scalar unit.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const char* uni(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>((hi << 32) | lo);
+}
+
+__device__ __forceinline__ WideRows wide_rows(const StagePlan& g) {
+  WideRows w;
+  w.n0 = uni(g.n0);
+  w.n01 = uni(g.n01);
+  w.nrows = uni(g.nrows);
+  w.rp = uni(g.rp);
+  w.sub = uni(g.sub);  // lanes_per_row >= 64: uniform over the wave
+  w.vsh = uni(g.vpt == 1 ? 0 : g.vpt == 2 ? 1 : 2);
+  w.rb = (uint32_t)uni(g.K * 2);
+  const uint64_t b0 = reinterpret_cast<uint64_t>(uni(g.seg0));
+  const uint64_t b1 = reinterpret_cast<uint64_t>(uni(g.seg1)) - (uint64_t)(uint32_t)w.n0 * w.rb;
+  const uint64_t b2 = reinterpret_cast<uint64_t>(uni(g.seg2)) - (uint64_t)(uint32_t)w.n01 * w.rb;
+  w.b0 = b0;
+  w.d1 = b1 - b0;
+  w.d2 = b2 - b1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kv = g.kl + i * g.lpr;
+    w.lo[i] = (i < g.vpt && kv < g.vpr) ? (uint32_t)kv * 16u : 0u;
+  }
+  return w;
+}
+
+// j-th vector of any plan (the next stage's prefetch)
+__device__ __forceinline__ uint4 plan_load(const StagePlan& g, const WideRows& w, int j) {
+  return g.lpr >= 64 ? w.load_j(j) : ldw(g.addr(j));
+}
+
 // Runs prep() (poll + normalisation; must end with a barrier and leave the
 // 16-bit input in xs) between the ring prologue and the main loop.  On return
 // yv[r] holds row r's dot product for r < nrows (after a barrier).
@@ -250,9 +319,16 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
                                      int slot) {
   const int J = g.passes() * VPT;
   const int Jp = (J + kDepth - 1) / kDepth * kDepth;
+  static_assert(kDepth % VPT == 0, "ring blocks hold whole rows");
+  const WideRows wr = WIDE ? wide_rows(g) : WideRows{};
+  // vector j = pj * VPT + i of this stage
+  auto wload = [&](int pj, int i) -> uint4 {
+    if constexpr (WIDE) return wr.load(pj, i);
+    else return ldw(g.addr<VPT>(pj * VPT + i));
+  };
   if (Jp > 0 && !prefilled) {
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(g.addr<VPT>(i));
+    for (int i = 0; i < kDepth; ++i) ring[i] = wload(i / VPT, i % VPT);
   }
   if (!prep()) return false;
   const bool has_next = next.nrows > 0;
@@ -274,10 +350,11 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
     float acc = 0.f;
     int j0 = 0;
     for (; j0 + kDepth < Jp; j0 += kDepth) {
+      const int p0 = (j0 + kDepth) / VPT;
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {
         acc = dot(ring[i], i, acc);
-        ring[i] = ldw(g.addr<VPT>(j0 + i + kDepth));
+        ring[i] = wload(p0 + i / VPT, i % VPT);
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
           acc = 0.f;
@@ -285,10 +362,11 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
       }
     }
     if (has_next) {
+      const WideRows nw = next.lpr >= 64 ? wide_rows(next) : WideRows{};
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {  // last block: drain, refill with the next stage
         acc = dot(ring[i], i, acc);
-        ring[i] = ldw(next.addr(i));
+        ring[i] = plan_load(next, nw, i);
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
           acc = 0.f;
@@ -305,8 +383,9 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
       }
     }
   } else if (has_next) {
+    const WideRows nw = next.lpr >= 64 ? wide_rows(next) : WideRows{};
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(next.addr(i));
+    for (int i = 0; i < kDepth; ++i) ring[i] = plan_load(next, nw, i);
   }
   stamp(tr, slot, 2, t);
   __syncthreads();
@@ -321,8 +400,9 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
 
 __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np) {
   if (np.nrows > 0) {
+    const WideRows nw = np.lpr >= 64 ? wide_rows(np) : WideRows{};
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = ldw(np.addr(i));
+    for (int i = 0; i < kDepth; ++i) ring[i] = plan_load(np, nw, i);
   }
 }
 

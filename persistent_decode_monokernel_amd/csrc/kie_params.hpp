@@ -13,7 +13,7 @@ constexpr int kClMin = 16;               // shortest split-KV chunk (positions)
 constexpr int kAttnUnits = 256;          // target (KV head, chunk) units per layer
 constexpr int kRedCap = 8192;            // LDS floats for per-wave GEMV partial sums
 constexpr int kYCap = 1024;              // LDS floats for finished GEMV rows
-constexpr int kDepth = 16;               // weight vectors in flight per thread
+constexpr int kDepth = 8;               // weight vectors in flight per thread
 constexpr uint32_t kSent = 0xFFFFFFFFu;  // NaN pattern that marks "not written yet"
 constexpr int kStagesPerLayer = 6;       // qkv, attn, merge, wo, gate/up, down
 constexpr int kTraceStamps = 4;          // per (slot, work-group): entry, input, compute done, exit

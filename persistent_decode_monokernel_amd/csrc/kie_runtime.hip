@@ -133,7 +133,7 @@ LdsPlan lds_plan(const kie_config& c) {
 // else the vectors each thread reads per row (1, 2 or 4).
 int width_class(int K) {
   const int vpr = K / 8;
-  return vpr < 64 ? 0 : vpr <= kThreads ? 1 : vpr <= 2 * kThreads ? 2 : 4;
+  return vpr < 64 ? 0 : vectors_per_lane(vpr);
 }
 
 // The kernel instance for a shape: dtype, query heads per KV head, width class
@@ -208,10 +208,12 @@ extern "C" kie_status kie_config_validate(const kie_config* c) {
   if (c->n_kv_heads > kAttnUnits) return KIE_ERR_UNSUPPORTED;
   if (!k_ok(c->d_model) || !k_ok(c->n_heads * c->head_dim) || !k_ok(c->d_ffn)) return KIE_ERR_UNSUPPORTED;
   // compiled kernel instances: d_model <= 4096 with n_heads*head_dim in the
-  // same width class, d_ffn >= 512
-  if (width_class(c->d_model) > 1 || width_class(c->n_heads * c->head_dim) != width_class(c->d_model) ||
-      width_class(c->d_ffn) == 0 || (width_class(c->d_model) == 0 && width_class(c->d_ffn) != 1))
-    return KIE_ERR_UNSUPPORTED;
+  // same width class, d_ffn >= 512 in a class at least d_model's
+  {
+    const int vd = width_class(c->d_model), vf = width_class(c->d_ffn);
+    if (c->d_model > 4096 || width_class(c->n_heads * c->head_dim) != vd || vf == 0 || vf < vd)
+      return KIE_ERR_UNSUPPORTED;
+  }
   if ((long long)c->vocab * c->d_model >= (1ll << 40)) return KIE_ERR_UNSUPPORTED;
   if (lds_plan(*c).bytes > 160 * 1024) return KIE_ERR_UNSUPPORTED;
   return KIE_OK;

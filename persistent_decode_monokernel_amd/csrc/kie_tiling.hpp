@@ -54,18 +54,37 @@ __host__ __device__ __forceinline__ int matrix_rows(const TileDims& D, int m) {
   }
 }
 
+// Lanes that read one row of vpr 16-byte vectors.  Rows of at least 64
+// vectors are read by whole waves: the smallest multiple of 64 lanes (a power
+// of two, at most the 512 threads) that leaves each lane at most 4 vectors of
+// the row, so one lane reduction serves up to 4 vectors and the row a wave
+// reads is wave-uniform.  Shorter rows (K = 256) take vpr lanes, two rows per
+// wave.
+__host__ __device__ __forceinline__ int lanes_per_row(int vpr) {
+  if (vpr < 64) return vpr;
+  int l = 64;
+  while (l < kThreads && 4 * l < vpr) l <<= 1;
+  return l;
+}
+// Vectors each lane reads per row, rounded up to 1, 2 or 4 (the GEMV width
+// class; columns beyond the row are padding).
+__host__ __device__ __forceinline__ int vectors_per_lane(int vpr) {
+  const int l = lanes_per_row(vpr), v = (vpr + l - 1) / l;
+  return v <= 1 ? 1 : v <= 2 ? 2 : 4;
+}
+
 // One thread's view of a work-group's rows in a GEMV stage.
 //
 // The work-group owns nrows local rows, made of up to three contiguous
 // segments of weight matrices: local rows [0, n0) start at seg0, [n0, n01) at
 // seg1, [n01, nrows) at seg2 (row stride K elements).  A row is read as K/8
-// vectors of 8 elements; lpr = min(K/8, 512) consecutive threads read
-// consecutive vectors of one row, rp = 512 / lpr rows are read per pass, and a
-// row of more than 512 vectors gives each thread vpt vectors (1, 2 or 4).
-// Thread t reads, for its j-th vector, local row (j / vpt) * rp + t / lpr and
-// vector t % lpr + (j % vpt) * lpr of that row.  Vectors beyond the rows (the
-// padding of the last pass / of the ring) re-read local row 0, vector 0 and
-// are discarded by the caller.
+// vectors of 8 elements by lpr = lanes_per_row(K/8) consecutive threads, each
+// taking vpt = vectors_per_lane(K/8) vectors of it; rp = 512 / lpr rows are
+// read per pass.  Thread t reads, for its j-th vector, local row
+// (j / vpt) * rp + t / lpr and vector t % lpr + (j % vpt) * lpr of that row.
+// Padding (rows beyond nrows, vectors beyond the row: the last pass, the ring
+// and the column tail) reads row 0 and/or vector 0 instead; the caller
+// discards it.
 struct StagePlan {
   const uint16_t* seg0;
   const uint16_t* seg1;
@@ -75,10 +94,8 @@ struct StagePlan {
   __host__ __device__ __forceinline__ int passes() const { return (nrows + rp - 1) / rp; }
 
   __host__ __device__ __forceinline__ const uint16_t* row_vec(int row, int kv) const {
-    if (row >= nrows || kv >= vpr) {
-      row = 0;
-      kv = 0;
-    }
+    if (row >= nrows) row = 0;
+    if (kv >= vpr) kv = 0;
     const uint16_t* b = row < n0 ? seg0 + (size_t)row * K
                       : row < n01 ? seg1 + (size_t)(row - n0) * K : seg2 + (size_t)(row - n01) * K;
     return b + (size_t)kv * 8;
@@ -100,9 +117,9 @@ __host__ __device__ __forceinline__ StagePlan plan_rows(int nrows, int K, int t)
   g.nrows = nrows;
   g.K = K;
   g.vpr = K >> 3;
-  g.lpr = g.vpr < kThreads ? g.vpr : kThreads;
+  g.lpr = lanes_per_row(g.vpr);
   g.rp = kThreads / g.lpr;
-  g.vpt = g.vpr <= kThreads ? 1 : g.vpr <= 2 * kThreads ? 2 : 4;
+  g.vpt = vectors_per_lane(g.vpr);
   g.sub = t / g.lpr;
   g.kl = t % g.lpr;
   g.nwr = g.lpr >= 64 ? g.lpr / 64 : 1;

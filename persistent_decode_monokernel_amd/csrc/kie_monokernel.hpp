@@ -79,7 +79,9 @@ struct Lds {
   uint16_t* xn;    // 16-bit activation fed to dot2 [Kmax] (bf16: three terms, see act_store)
   float* red;      // GEMV per-wave partial sums [kRedCap]
   float* yv;       // GEMV finished rows [kYCap]
-  float* scr;      // attention scratch (aliases red/yv)
+  float* scr;      // aliases red/yv
+  float* att;      // attention scratch: aliases xn and red/yv (both idle from the end of the
+                   // QKV GEMV to the Wo poll)
   float* misc;     // 64 floats: block reductions
   int* imisc;      // 64 ints
 };
@@ -91,6 +93,7 @@ __device__ __forceinline__ Lds lds_view(char* smem, const Params& P) {
   s.red = reinterpret_cast<float*>(smem + P.lds_scr);
   s.yv = s.red + kRedCap;
   s.scr = s.red;
+  s.att = reinterpret_cast<float*>(smem + P.lds_xn);
   s.misc = reinterpret_cast<float*>(smem + P.lds_misc);
   s.imisc = reinterpret_cast<int*>(s.misc + 64);
   return s;
@@ -490,8 +493,10 @@ __device__ __forceinline__ float safe_exp_diff(float a, float m) { return a == -
 // Rotary embedding of q and of the new k happens in registers right after the
 // poll; the unit whose chunk holds the current position also appends the
 // (rotated k, v) row to the KV cache.  Positions are spread over lane groups
-// of hd/8 lanes; each group keeps an online softmax state, groups are merged
-// with shuffles inside a wave and through LDS across waves.
+// of hd/8 lanes (8 dimensions per lane, one position per group and pass).
+// Each group keeps the online-softmax state of up to four heads at once, so a
+// K/V row is read once for all of them; the groups' states then meet once in
+// LDS, one thread per (head, dimension) folding them.
 template <int DT, int G>
 __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
@@ -506,16 +511,16 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
   int CL, nch;
   attn_chunking(P, n, CL, nch);
   const int units = hkv * nch;
+  constexpr int HB = G < 4 ? G : G == 8 ? 2 : 4;  // heads whose state a lane group keeps at once
   const int LPP = hd >> 3;                // lanes per position row
-  const int PP = kThreads / LPP;          // positions per pass
+  const int PP = kThreads / LPP;          // lane groups = positions per pass
   const int grp = t / LPP, e8 = (t % LPP) * 8;
-  const int wave = t >> 6, lane = t & 63;
   const float scale = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
-  float* qs = c.s.scr;                                    // [G][hd] rotated queries
+  float* qs = c.s.att;                                    // [G][hd] rotated queries
   uint16_t* kv16 = reinterpret_cast<uint16_t*>(qs + G * hd);  // [2][hd] new row as stored
-  float* wml = qs + G * hd + hd;                          // [kWaves][G][2] per-wave (m, l)
-  float* wo = wml + kWaves * G * 2;                       // [kWaves][G][hd] per-wave o
-  constexpr int APF = 4;                                  // passes prefetched into registers
+  float* gml = qs + G * hd + hd;                          // [PP][HB][2] per-group (m, l)
+  float* go = gml + PP * HB * 2;                          // [PP][HB][hd] per-group o
+  constexpr int APF = 2;                                  // passes prefetched into registers
   const uint32_t* src = X + P.xl.qkv + (size_t)l * N;
   for (int u = c.wg; u < units; u += c.nb) {
     const int g = u % hkv, ch = u / hkv;
@@ -585,16 +590,20 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
           vr[a] = *reinterpret_cast<const uint4*>(kv16 + hd + e8);
         }
     }
-    // online softmax over this lane group's positions, one head at a time
-    // (keeps one head's state live: bounded register use for any G)
+    const int ngrp = min(PP, j1 - j0);  // lane groups holding at least one position
 #pragma unroll 1
-    for (int hh = 0; hh < G; ++hh) {
-      float q8[8];
+    for (int hb = 0; hb < G; hb += HB) {
+      float q[HB][8], mx[HB], ls[HB], o[HB][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q8[e] = qs[hh * hd + e8 + e];
-      float mx = -INFINITY, ls = 0.f, o[8];
+      for (int h = 0; h < HB; ++h) {
+        mx[h] = -INFINITY;
+        ls[h] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          q[h][e] = qs[(hb + h) * hd + e8 + e];
+          o[h][e] = 0.f;
+        }
+      }
       for (int a = 0; a < npass; ++a) {
         const int j = j0 + a * PP + grp;
         if (j >= j1) break;  // uniform per lane group
@@ -615,58 +624,54 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
         float kf[8], vf[8];
         unpack8<DT>(k4, kf);
         unpack8<DT>(v4, vf);
-        float sd = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sd += q8[e] * kf[e];
-        sd = (hd == 128 ? sum16(sd) : sum8(sd)) * scale;
-        const float mn = fmaxf(mx, sd);
-        const float fo = safe_exp_diff(mx, mn), fp = fast_exp2(sd - mn);
-        ls = ls * fo + fp;
+        for (int h = 0; h < HB; ++h) {
+          float sd = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = o[e] * fo + fp * vf[e];
-        mx = mn;
-      }
-      // merge the lane groups of the wave (lanes that differ in bits >= log2(LPP))
-      for (int msk = LPP; msk < 64; msk <<= 1) {
-        const float mo = __shfl_xor(mx, msk), lo = __shfl_xor(ls, msk);
-        const float mn = fmaxf(mx, mo);
-        const float fa = safe_exp_diff(mx, mn), fb = safe_exp_diff(mo, mn);
-        ls = ls * fa + lo * fb;
+          for (int e = 0; e < 8; ++e) sd += q[h][e] * kf[e];
+          sd = (hd == 128 ? sum16(sd) : sum8(sd)) * scale;
+          const float mn = fmaxf(mx[h], sd);
+          const float fo = safe_exp_diff(mx[h], mn), fp = fast_exp2(sd - mn);
+          ls[h] = ls[h] * fo + fp;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = o[e] * fa + __shfl_xor(o[e], msk) * fb;
-        mx = mn;
-      }
-      if (lane < LPP) {
-        float* dst = wo + (wave * G + hh) * hd + e8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = o[e];
-        if (lane == 0) {
-          wml[(wave * G + hh) * 2] = mx;
-          wml[(wave * G + hh) * 2 + 1] = ls;
+          for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * fo + fp * vf[e];
+          mx[h] = mn;
         }
       }
-    }
-    stamp(tr, slot, 2, t);
-    __syncthreads();
-    // merge the waves and publish (m, l, o) of each head for this chunk
-    uint32_t* att = X + P.xl.att;
-    for (int idx = t; idx < G * hd; idx += kThreads) {
-      const int hh = idx / hd, e = idx % hd;
-      float M = -INFINITY;
+      if (grp < ngrp) {
 #pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, wml[(w2 * G + hh) * 2]);
-      float Ls = 0.f, Os = 0.f;
+        for (int h = 0; h < HB; ++h) {
+          float* dst = go + (grp * HB + h) * hd + e8;
 #pragma unroll
-      for (int w2 = 0; w2 < kWaves; ++w2) {
-        const float f = safe_exp_diff(wml[(w2 * G + hh) * 2], M);
-        Ls += wml[(w2 * G + hh) * 2 + 1] * f;
-        Os += wo[(w2 * G + hh) * hd + e] * f;
+          for (int e = 0; e < 8; ++e) dst[e] = o[h][e];
+          if (e8 == 0) {
+            gml[(grp * HB + h) * 2] = mx[h];
+            gml[(grp * HB + h) * 2 + 1] = ls[h];
+          }
+        }
       }
-      uint32_t* rowp = att + (((size_t)l * hq + (size_t)g * G + hh) * P.cmax + ch) * P.astride;
-      xst32(rowp + 4 + e, __float_as_uint(Os));
-      if (e == 0) xst64(rowp, pack2f(M, Ls));
+      stamp(tr, slot, 2, t);
+      __syncthreads();
+      // fold the groups and publish (m, l, o) of heads hb .. hb+HB-1 for this chunk
+      uint32_t* att = X + P.xl.att;
+      for (int idx = t; idx < HB * hd; idx += kThreads) {
+        const int h = idx / hd, e = idx % hd;
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int g2 = 0; g2 < ngrp; ++g2) M = fmaxf(M, gml[(g2 * HB + h) * 2]);
+        float Ls = 0.f, Os = 0.f;
+#pragma unroll 8
+        for (int g2 = 0; g2 < ngrp; ++g2) {
+          const float f = safe_exp_diff(gml[(g2 * HB + h) * 2], M);
+          Ls += gml[(g2 * HB + h) * 2 + 1] * f;
+          Os += go[(g2 * HB + h) * hd + e] * f;
+        }
+        uint32_t* rowp = att + (((size_t)l * hq + (size_t)g * G + hb + h) * P.cmax + ch) * P.astride;
+        xst32(rowp + 4 + e, __float_as_uint(Os));
+        if (e == 0) xst64(rowp, pack2f(M, Ls));
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   stamp(tr, slot, 3, t);
   return true;

@@ -114,15 +114,21 @@ LdsPlan lds_plan(const kie_config& c) {
   if (c.d_ffn > kmax) kmax = c.d_ffn;
   const int G = c.n_heads / c.n_kv_heads;
   const size_t gemv_scr = (size_t)(kRedCap + kYCap) * 4;
-  const size_t attn_scr = ((size_t)G * c.head_dim + (size_t)c.head_dim + (size_t)kWaves * G * 2 +
-                           (size_t)kWaves * G * c.head_dim) * 4;
+  // attention scratch, from the xn offset over xn and scr: rotated queries
+  // [G][hd], the new row [2][hd] 16-bit, per lane group (m, l) and o for up
+  // to 4 heads at once (2 when 8 query heads share a KV head), lane groups = 512 / (hd / 8)
+  const size_t hb = G < 4 ? G : G == 8 ? 2 : 4, groups = (size_t)kThreads / (c.head_dim / 8);
+  const size_t attn_scr = ((size_t)G * c.head_dim + (size_t)c.head_dim + groups * hb * 2 +
+                           groups * hb * c.head_dim) * 4;
   size_t o = 0;
   p.xres = 0;
   o = align_up((size_t)c.d_model * 4, 16);
   p.xn = (int)o;
-  o = align_up(o + (size_t)kmax * 2 * (c.dtype == KIE_BF16 ? 3 : 1), 16);  // bf16: three terms per input
+  const size_t xn_bytes = align_up((size_t)kmax * 2 * (c.dtype == KIE_BF16 ? 3 : 1), 16);  // bf16: three terms
+  o += xn_bytes;
   p.scr = (int)o;
-  o = align_up(o + (gemv_scr > attn_scr ? gemv_scr : attn_scr), 16);
+  const size_t scr_bytes = attn_scr > xn_bytes + gemv_scr ? attn_scr - xn_bytes : gemv_scr;
+  o = align_up(o + scr_bytes, 16);
   p.misc = (int)o;
   o += 128 * 4;
   p.bytes = (int)o;

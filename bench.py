@@ -175,6 +175,34 @@ def gemv_probe_bench(n_copies: int = 16):
             torch.cuda.empty_cache()
 
 
+def ttft_bench(name: str, modes=("auto", "decode_loop")):
+    """Time to first token: wall time of kie_prefill (prompt already on the
+    host, weights resident) for the workload's prompt, per prefill mode."""
+    import torch
+
+    from persistent_decode_monokernel_amd import kie, synth
+
+    wl = synth.WORKLOADS[name]
+    s = wl.shape
+    w = synth.make_weights(s, wl.weight_seed, device="cuda")
+    prompt = synth.make_prompt(s, wl.n_prompt, wl.prompt_seed).tolist()
+    for mode in modes:
+        eng = kie.Engine(s, max_seq=wl.n_prompt + 8)
+        eng.load_weights(w)
+        eng.set_prefill_mode(kie.KIE_PREFILL_AUTO if mode == "auto" else kie.KIE_PREFILL_DECODE_LOOP)
+        eng.prefill(prompt[:64])  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tok, _ = eng.prefill(prompt)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        flops = 2.0 * synth.param_count(s) * wl.n_prompt
+        print(json.dumps({"ttft_ms": dt * 1e3, "workload": name, "prompt": wl.n_prompt, "mode": mode,
+                          "prompt_tokens_per_s": wl.n_prompt / dt, "dense_TFLOP_per_s": flops / dt / 1e12,
+                          "first_token": tok}), flush=True)
+        eng.close()
+
+
 STAGES = ("qkv", "attention", "merge", "wo", "gate/up", "down")
 
 
@@ -286,6 +314,7 @@ def main():
                     help="only summarise rocprofv3 --pmc counter CSVs")
     ap.add_argument("--copy-bytes", type=int, default=0, help="bytes read (= written) by the copy probe")
     ap.add_argument("--gemv", action="store_true", help="only run the isolated GEMV probe workload")
+    ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")
     ap.add_argument("--timeline", type=int, default=None, metavar="STEP",
                     help="only print the per-stage timeline of decode step STEP of a 32-step launch")
     args = ap.parse_args()
@@ -305,6 +334,9 @@ def main():
         return
     if args.gemv:
         gemv_probe_bench()
+        return
+    if args.ttft:
+        ttft_bench(args.workload)
         return
     if args.timeline is not None:
         from persistent_decode_monokernel_amd import synth

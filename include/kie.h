@@ -140,8 +140,10 @@ kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_byte
  * sequence: a kie_prefill() or kie_import_kv() must follow before decoding. */
 kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
 
-/* Run the prompt through the model inside the persistent kernel, one position
- * per loop iteration with the prompt tokens fed instead of sampled ones.
+/* Run the prompt through the model (see kie_set_prefill_mode for how): the
+ * last prompt position, and by default only it, is a step of the persistent
+ * decode kernel with the prompt token fed instead of a sampled one; earlier
+ * positions run as dense matrix-core products where the shape allows.
  * Starts a new sequence: the KV cache is rewritten from position 0.
  *   prompt_host[n_prompt]: token ids in [0, vocab), 1 <= n_prompt <= max_seq.
  *   next_token_host: receives the greedy token after the last prompt position.
@@ -150,6 +152,18 @@ kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
  * After success the engine holds pos = n_prompt and the new token pending. */
 kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prompt,
                        int32_t* next_token_host, float* logits_dev);
+
+/* How kie_prefill() runs the prompt.  KIE_PREFILL_AUTO (default): positions
+ * 0 .. n_prompt-2 as dense products on the matrix cores (fp16 models whose
+ * projection widths are multiples of 128; others fall back), then the last
+ * position as one forced step of the persistent decode kernel, which yields
+ * the logits and the first token.  KIE_PREFILL_DECODE_LOOP: every prompt
+ * position as a forced step of the persistent decode kernel.  The pages put
+ * prompt processing inside the resident program (revietech.ru page, section
+ * "Chto takoye monokernel"); both modes leave the same sequence state (up to
+ * rounding order). */
+typedef enum { KIE_PREFILL_AUTO = 0, KIE_PREFILL_DECODE_LOOP = 1 } kie_prefill_mode;
+kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode);
 
 /* Greedy decode of up to n_steps tokens in ONE persistent kernel launch.
  * Step i feeds the pending token at position pos+i and emits token i.  If

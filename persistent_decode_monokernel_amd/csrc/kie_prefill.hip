@@ -1,0 +1,282 @@
+// Prompt processing as dense GEMMs on the matrix cores (MFMA), for the
+// positions before the last prompt token: the work of a prompt of P tokens is
+// a [P x d] x [d x N] product per projection, which is what the matrix cores
+// are for (the per-token decode path stays on the dot2 vector ALU).
+//
+// The prompt is processed in chunks of up to kPfChunk positions, layer by
+// layer, with one launch per operation on the engine's stream:
+//   X = E[tokens]                                   (fp32 residual, [M][d])
+//   per layer:  Xn = RMSNorm(X) * g_attn            (16-bit, [M][d])
+//               QKV = Xn Wq^T | Xn Wk^T | Xn Wv^T   (fp32, [M][qd + 2 kvd])
+//               rotary embedding of q (in place, fp32) and k; k, v appended
+//               to the KV cache
+//               A = causal attention of q over the cache rows 0 .. p0+m
+//               X += A Wo^T
+//               Xn = RMSNorm(X) * g_ffn
+//               H = silu(Xn Wg^T) * (Xn Wu^T)       (16-bit, [M][F])
+//               X += H Wd^T
+// The last prompt position then runs through the persistent decode kernel as
+// one forced step, which appends its KV row and yields the LM-head logits and
+// the first greedy token (kie_prefill in kie_runtime.hip).
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_f16, checked on the device): lane l
+// holds A[m = l%32][k = 8*(l/32) + 0..7] and B[k = 8*(l/32) + 0..7][n = l%32];
+// accumulator element 4i+j is C[m = 8i + 4*(l/32) + j][n = l%32].
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kie.h"
+#include "kie_params.hpp"
+#include "kie_prefill.hpp"
+
+namespace kie {
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+__device__ __forceinline__ h8_t ld8(const uint16_t* p) {
+  return __builtin_bit_cast(h8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+// ---- embedding and RMSNorm -------------------------------------------------
+
+__global__ __launch_bounds__(256) void pf_embed(const uint16_t* E, const int* tok, int M, int d, float* X) {
+  const int m = blockIdx.x;
+  if (m >= M) return;
+  const uint16_t* row = E + (size_t)tok[m] * d;
+  for (int i = threadIdx.x; i < d; i += 256) X[(size_t)m * d + i] = h2f(row[i]);
+}
+
+__global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t* g, float eps, int M, int d,
+                                                  uint16_t* Xn) {
+  __shared__ float part[4];
+  const int m = blockIdx.x;
+  if (m >= M) return;
+  const float* x = X + (size_t)m * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += 256) ss += x[i] * x[i];
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += 256) Xn[(size_t)m * d + i] = f2h(x[i] * r * h2f(g[i]));
+}
+
+// ---- GEMM: C[M][N] = A[M][K] W[N][K]^T on the matrix cores --------------------
+//
+// Work-group (4 waves) tile 64 x 128; wave w: rows 32*(w/2) .., columns
+// 64*(w%2) .. as two 32x32 accumulators.  Operands go straight from memory to
+// registers (16 contiguous bytes per lane per operand and k-step), kPfDepth
+// k-steps ahead of the matrix-core instructions.  Rows of A beyond M re-read
+// row M-1 and are not stored.  Requires N % 128 == 0 and K % (16 kPfDepth) == 0.
+enum : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+constexpr int kPfDepth = 4;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void pf_gemm(const uint16_t* A, int M, int K, const uint16_t* W,
+                                               const uint16_t* W2, float* C, int ldc, uint16_t* H, int ldh) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int m0 = blockIdx.y * 64 + (wave >> 1) * 32, n0 = blockIdx.x * 128 + (wave & 1) * 64;
+  const int ar = min(m0 + (l & 31), M - 1);
+  const int kq = (l >> 5) * 8;
+  const uint16_t* ap = A + (size_t)ar * K + kq;
+  const uint16_t* bp = W + (size_t)(n0 + (l & 31)) * K + kq;
+  const uint16_t* cp = EPI == EPI_SWIGLU ? W2 + (size_t)(n0 + (l & 31)) * K + kq : nullptr;
+  const size_t b32 = (size_t)32 * K;
+  constexpr int NB = EPI == EPI_SWIGLU ? 4 : 2;  // B operands per k-step: 2 column tiles (x 2 matrices)
+  f16x_t acc[NB] = {};
+  h8_t ra[kPfDepth], rb[kPfDepth][NB];
+  auto load = [&](int s, int k) {
+    ra[s] = ld8(ap + k);
+    rb[s][0] = ld8(bp + k);
+    rb[s][1] = ld8(bp + b32 + k);
+    if constexpr (EPI == EPI_SWIGLU) {
+      rb[s][2] = ld8(cp + k);
+      rb[s][3] = ld8(cp + b32 + k);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < kPfDepth; ++s) load(s, s * 16);
+  for (int k0 = 0; k0 < K; k0 += 16 * kPfDepth) {
+#pragma unroll
+    for (int s = 0; s < kPfDepth; ++s) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[s], rb[s][b], acc[b], 0, 0, 0);
+      const int kn = k0 + (s + kPfDepth) * 16;
+      if (kn < K) load(s, kn);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + i * 8 + (l >> 5) * 4 + j;
+      if (m >= M) continue;
+      const int n = n0 + (l & 31);
+      if constexpr (EPI == EPI_STORE) {
+        C[(size_t)m * ldc + n] = acc[0][i * 4 + j];
+        C[(size_t)m * ldc + n + 32] = acc[1][i * 4 + j];
+      } else if constexpr (EPI == EPI_ADD) {
+        C[(size_t)m * ldc + n] += acc[0][i * 4 + j];
+        C[(size_t)m * ldc + n + 32] += acc[1][i * 4 + j];
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float gt = acc[b][i * 4 + j], up = acc[b + 2][i * 4 + j];
+          H[(size_t)m * ldh + n + 32 * b] = f2h(gt / (1.0f + expf(-gt)) * up);
+        }
+      }
+    }
+  }
+}
+
+// ---- rotary embedding, KV append ------------------------------------------
+//
+// Thread (m, i) for rotary pair i < hd/2 of every head: q rotated in place
+// (fp32, as the decode path keeps it); k rotated and v copied into the cache
+// rows at position p0 + m.
+__global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int hkv, int hd, const float* rope,
+                                                  int p0, int max_seq, uint16_t* kc, uint16_t* vc) {
+  const int half = hd >> 1, qd = hq * hd, kvd = hkv * hd, ld = qd + 2 * kvd;
+  const int per_row = (hq + hkv) * half + hkv * half;  // q pairs, k pairs, v pairs
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * per_row) return;
+  const int m = idx / per_row, r = idx % per_row, pos = p0 + m;
+  const float* row = QKV + (size_t)m * ld;
+  if (r < (hq + hkv) * half) {
+    const int h = r / half, i = r % half;
+    const float c = rope[((size_t)pos * half + i) * 2], s = rope[((size_t)pos * half + i) * 2 + 1];
+    float* src = QKV + (size_t)m * ld + (size_t)h * hd;  // q heads, then k heads (contiguous)
+    const float a = src[i], b = src[i + half];
+    const float ra = a * c - b * s, rb = a * s + b * c;
+    if (h < hq) {
+      src[i] = ra;
+      src[i + half] = rb;
+    } else {
+      uint16_t* dst = kc + ((size_t)(h - hq) * max_seq + pos) * hd;
+      dst[i] = f2h(ra);
+      dst[i + half] = f2h(rb);
+    }
+  } else {
+    const int rr = r - (hq + hkv) * half, g = rr / half, i = rr % half;
+    const float* src = row + qd + kvd + (size_t)g * hd;
+    uint16_t* dst = vc + ((size_t)g * max_seq + pos) * hd;
+    dst[i] = f2h(src[i]);
+    dst[i + half] = f2h(src[i + half]);
+  }
+}
+
+// ---- causal attention ------------------------------------------------------
+//
+// Lane group (hd/8 lanes, 8 dimensions each) per (query m, head h): online
+// softmax in base 2 over the cache rows 0 .. p0+m of KV head h / (hq/hkv).
+__device__ __forceinline__ float grp_sum(float v, int lpp) {
+  for (int o = 1; o < lpp; o <<= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, int hkv, int hd, int p0,
+                                               int max_seq, const uint16_t* kc, const uint16_t* vc, uint16_t* A16) {
+  const int lpp = hd >> 3, gpb = 256 / lpp;
+  const int grp = blockIdx.x * gpb + threadIdx.x / lpp, e8 = (threadIdx.x % lpp) * 8;
+  const int qd = hq * hd, ldq = qd + 2 * hkv * hd;
+  if (grp >= M * hq) return;  // whole groups leave together
+  const int m = grp / hq, h = grp % hq, g = h / (hq / hkv), n = p0 + m + 1;
+  const float scale = 1.4426950408889634f / sqrtf((float)hd);
+  float q[8], o[8];
+  const float* qp = QKV + (size_t)m * ldq + (size_t)h * hd + e8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    q[e] = qp[e] * scale;
+    o[e] = 0.f;
+  }
+  const uint16_t* kb = kc + (size_t)g * max_seq * hd + e8;
+  const uint16_t* vb = vc + (size_t)g * max_seq * hd + e8;
+  float mx = -INFINITY, ls = 0.f;
+  // rows j .. j+3 in flight (rows beyond n re-read row n-1 and are not used)
+  constexpr int R = 4;
+  uint4 kr[R], vr[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int jj = min(s, n - 1);
+    kr[s] = *reinterpret_cast<const uint4*>(kb + (size_t)jj * hd);
+    vr[s] = *reinterpret_cast<const uint4*>(vb + (size_t)jj * hd);
+  }
+  for (int j0 = 0; j0 < n; j0 += R)
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    const int j = j0 + s;
+    if (j >= n) break;
+    const uint4 kv = kr[s], vv = vr[s];
+    const int jn = min(j + R, n - 1);
+    kr[s] = *reinterpret_cast<const uint4*>(kb + (size_t)jn * hd);
+    vr[s] = *reinterpret_cast<const uint4*>(vb + (size_t)jn * hd);
+    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    float sd = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sd += q[2 * e] * h2f(kw[e] & 0xFFFF) + q[2 * e + 1] * h2f(kw[e] >> 16);
+    sd = grp_sum(sd, lpp);
+    const float mn = fmaxf(mx, sd);
+    const float fo = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn), fp = __builtin_amdgcn_exp2f(sd - mn);
+    ls = ls * fo + fp;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = o[2 * e] * fo + fp * h2f(vw[e] & 0xFFFF);
+      o[2 * e + 1] = o[2 * e + 1] * fo + fp * h2f(vw[e] >> 16);
+    }
+    mx = mn;
+  }
+  const float inv = 1.0f / ls;
+  uint4 out;
+  uint32_t ow[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ow[e] = (uint32_t)f2h(o[2 * e] * inv) | ((uint32_t)f2h(o[2 * e + 1] * inv) << 16);
+  out.x = ow[0]; out.y = ow[1]; out.z = ow[2]; out.w = ow[3];
+  *reinterpret_cast<uint4*>(A16 + (size_t)m * qd + (size_t)h * hd + e8) = out;
+}
+
+}  // namespace
+
+bool prefill_supported(const kie_config& c) {
+  const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  const int kstep = 16 * kPfDepth;
+  return c.dtype == KIE_F16 && c.d_model % 128 == 0 && qd % 128 == 0 && kvd % 128 == 0 && c.d_ffn % 128 == 0 &&
+         c.d_model % kstep == 0 && qd % kstep == 0 && c.d_ffn % kstep == 0;
+}
+
+hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
+  const kie_config& c = x.cfg;
+  const int d = c.d_model, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, F = c.d_ffn;
+  const int ldq = qd + 2 * kvd;
+  const dim3 blk(256);
+  const int mt = (M + 63) / 64;
+  hipStream_t st = x.stream;
+  pf_embed<<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const uint16_t* const* w = x.wtab + (size_t)l * W_PER_LAYER;
+    const size_t plane = (size_t)l * c.n_kv_heads * c.max_seq * c.head_dim;
+    pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_ATTN_NORM], c.rms_eps, M, d, x.Xn);
+    pf_gemm<EPI_STORE><<<dim3(qd / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_Q], nullptr, x.QKV, ldq, nullptr, 0);
+    pf_gemm<EPI_STORE><<<dim3(kvd / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_K], nullptr, x.QKV + qd, ldq, nullptr, 0);
+    pf_gemm<EPI_STORE><<<dim3(kvd / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_V], nullptr, x.QKV + qd + kvd, ldq,
+                                                            nullptr, 0);
+    const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
+    pf_rope_kv<<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope, p0,
+                                                        c.max_seq, x.kc + plane, x.vc + plane);
+    const int gpb = 256 / (c.head_dim / 8);
+    pf_attn<<<(M * c.n_heads + gpb - 1) / gpb, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, p0,
+                                                             c.max_seq, x.kc + plane, x.vc + plane, x.A16);
+    pf_gemm<EPI_ADD><<<dim3(d / 128, mt), blk, 0, st>>>(x.A16, M, qd, w[W_O], nullptr, x.X, d, nullptr, 0);
+    pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, x.Xn);
+    pf_gemm<EPI_SWIGLU><<<dim3(F / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_GATE], w[W_UP], nullptr, 0, x.H16, F);
+    pf_gemm<EPI_ADD><<<dim3(d / 128, mt), blk, 0, st>>>(x.H16, M, F, w[W_DOWN], nullptr, x.X, d, nullptr, 0);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kie

@@ -1,0 +1,36 @@
+// Host interface of the matrix-core prompt path (kie_prefill.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kie.h"
+
+namespace kie {
+
+constexpr int kPfChunk = 1024;  // prompt positions per chunk (bounds the activation buffers)
+
+// Device buffers and weights of one engine for the prompt path.
+struct PrefillCtx {
+  kie_config cfg;
+  hipStream_t stream;
+  const uint16_t* tok_emb;
+  const uint16_t* const* wtab;  // host table [L][W_PER_LAYER] of device pointers
+  const float* rope;            // [max_seq][hd/2][cos, sin]
+  uint16_t* kc;                 // KV cache [L][Hkv][max_seq][hd]
+  uint16_t* vc;
+  float* X;                     // [chunk][d] residual
+  uint16_t* Xn;                 // [chunk][d] normalised input
+  float* QKV;                   // [chunk][qd + 2 kvd] (q rotated in place)
+  uint16_t* A16;                // [chunk][qd] attention output
+  uint16_t* H16;                // [chunk][F] SwiGLU output
+};
+
+// Shapes the prompt path handles (fp16 weights; projection widths multiples
+// of 128, reduction widths multiples of 64).
+bool prefill_supported(const kie_config& c);
+
+// Positions p0 .. p0+M-1 (tokens tok_dev[0 .. M-1], device) through every
+// layer: KV cache rows written, residual left in ctx.X.  M <= kPfChunk.
+hipError_t prefill_chunk(const PrefillCtx& ctx, const int* tok_dev, int p0, int M);
+
+}  // namespace kie

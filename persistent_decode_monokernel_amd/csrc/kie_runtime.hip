@@ -11,6 +11,7 @@
 
 #include "kie.h"
 #include "kie_params.hpp"
+#include "kie_prefill.hpp"
 #include "kie_tiling.hpp"
 
 namespace kie {
@@ -75,6 +76,8 @@ XchLayout xch_layout(const kie_config& c) {
 
 struct Layout {
   size_t params, rope, lw, kc, vc, xch, ctl, tok, forced, total;
+  size_t pf_x, pf_xn, pf_qkv, pf_a, pf_h;  // matrix-core prompt path (0 bytes when unsupported)
+  int pf_chunk;
   size_t kv_plane_bytes;
   XchLayout xl;
 };
@@ -98,6 +101,15 @@ Layout make_layout(const kie_config& c) {
   y.ctl = take(CTL_WORDS * 4);
   y.tok = take((size_t)c.max_seq * 4);
   y.forced = take((size_t)c.max_seq * 4);
+  y.pf_chunk = prefill_supported(c) ? (c.max_seq < kPfChunk ? c.max_seq : kPfChunk) : 0;
+  {
+    const size_t pc = (size_t)y.pf_chunk, qd = (size_t)c.n_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
+    y.pf_x = take(pc * c.d_model * 4);
+    y.pf_xn = take(pc * c.d_model * 2);
+    y.pf_qkv = take(pc * (qd + 2 * kvd) * 4);
+    y.pf_a = take(pc * qd * 2);
+    y.pf_h = take(pc * c.d_ffn * 2);
+  }
   y.total = o;
   return y;
 }
@@ -183,6 +195,8 @@ struct kie_engine {
   Params params_host{};
   uint64_t* trace = nullptr;
   int trace_step = 0;
+  std::vector<const uint16_t*> wtab;  // host copy of the per-layer weight table
+  int prefill_mode = KIE_PREFILL_AUTO;
 };
 
 extern "C" const char* kie_status_string(kie_status s) {
@@ -345,6 +359,8 @@ extern "C" kie_status kie_load_weights(kie_engine* e, const kie_weights* w) {
     if ((reinterpret_cast<uintptr_t>(p) & 15) != 0) return KIE_ERR_ARG;
   KIE_HIP(hipMemcpyAsync(e->ws + e->lay.lw, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice, e->stream));
   KIE_HIP(hipStreamSynchronize(e->stream));
+  e->wtab.assign(tab.size(), nullptr);
+  for (size_t i = 0; i < tab.size(); ++i) e->wtab[i] = reinterpret_cast<const uint16_t*>(tab[i]);
   e->tok_emb = reinterpret_cast<const uint16_t*>(w->tok_emb);
   e->final_norm = reinterpret_cast<const uint16_t*>(w->final_norm);
   e->lm_head = reinterpret_cast<const uint16_t*>(w->lm_head);
@@ -417,23 +433,54 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
   for (int i = 0; i < n_prompt; ++i)
     if (prompt_host[i] < 0 || prompt_host[i] >= e->cfg.vocab) return KIE_ERR_ARG;
   e->have_seq = false;
-  Params P = base_params(e);
   KIE_HIP(hipMemcpyAsync(e->ws + e->lay.forced, prompt_host, (size_t)n_prompt * 4, hipMemcpyHostToDevice, e->stream));
-  P.forced = reinterpret_cast<const int*>(e->ws + e->lay.forced);
-  P.pos0 = 0;
-  P.n_steps = n_prompt;
+  const int* forced = reinterpret_cast<const int*>(e->ws + e->lay.forced);
+  // positions 0 .. n_prompt-2 on the matrix cores (when the shape allows), the
+  // last one -- or all of them -- as forced steps of the persistent kernel
+  int first = 0;
+  if (e->prefill_mode == KIE_PREFILL_AUTO && e->lay.pf_chunk > 0 && n_prompt >= 2) {
+    const kie_config& c = e->cfg;
+    PrefillCtx x{};
+    x.cfg = c;
+    x.stream = e->stream;
+    x.tok_emb = e->tok_emb;
+    x.wtab = e->wtab.data();
+    x.rope = reinterpret_cast<const float*>(e->ws + e->lay.rope);
+    x.kc = reinterpret_cast<uint16_t*>(e->ws + e->lay.kc);
+    x.vc = reinterpret_cast<uint16_t*>(e->ws + e->lay.vc);
+    x.X = reinterpret_cast<float*>(e->ws + e->lay.pf_x);
+    x.Xn = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_xn);
+    x.QKV = reinterpret_cast<float*>(e->ws + e->lay.pf_qkv);
+    x.A16 = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_a);
+    x.H16 = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_h);
+    first = n_prompt - 1;
+    for (int p0 = 0; p0 < first; p0 += e->lay.pf_chunk) {
+      const int M = first - p0 < e->lay.pf_chunk ? first - p0 : e->lay.pf_chunk;
+      KIE_HIP(prefill_chunk(x, forced + p0, p0, M));
+    }
+  }
+  Params P = base_params(e);
+  P.forced = forced + first;
+  P.pos0 = first;
+  P.n_steps = n_prompt - first;
   P.eos_id = -1;
-  P.in_tok = prompt_host[0];
+  P.in_tok = prompt_host[first];
   P.lm_last_only = 1;
   P.logits = logits_dev;
   int done = 0, last = 0;
   const kie_status st = run_persistent(e, P, &done, &last);
   if (st != KIE_OK) return st;
-  if (done != n_prompt) return KIE_ERR_TIMEOUT;
+  if (done != n_prompt - first) return KIE_ERR_TIMEOUT;
   e->pos = n_prompt;
   e->pending = last;
   e->have_seq = true;
   *next_token_host = last;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode) {
+  if (!e || (mode != KIE_PREFILL_AUTO && mode != KIE_PREFILL_DECODE_LOOP)) return KIE_ERR_ARG;
+  e->prefill_mode = mode;
   return KIE_OK;
 }
 

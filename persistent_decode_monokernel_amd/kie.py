@@ -26,6 +26,8 @@ KIE_ERR_TIMEOUT = -6
 KIE_ERR_ABORTED = -7
 KIE_F16 = 1
 KIE_BF16 = 2
+KIE_PREFILL_AUTO = 0
+KIE_PREFILL_DECODE_LOOP = 1
 
 
 class KieError(RuntimeError):
@@ -66,6 +68,7 @@ class kie_info(ctypes.Structure):
 SIGNATURES = {
     "kie_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kie_config_validate": (ctypes.c_int, [ctypes.POINTER(kie_config)]),
+    "kie_set_prefill_mode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kie_config)]),
     "kie_create": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                   ctypes.POINTER(ctypes.c_void_p)]),
@@ -258,6 +261,10 @@ class Engine:
         _check(lib().kie_set_trace(self._h, ctypes.c_void_p(_dptr(buf)) if buf is not None else None, int(step)),
                "kie_set_trace")
         self._trace_buf = buf
+
+    def set_prefill_mode(self, mode: int):
+        """KIE_PREFILL_AUTO (matrix-core prompt path where supported) or KIE_PREFILL_DECODE_LOOP."""
+        _check(lib().kie_set_prefill_mode(self._h, int(mode)), "kie_set_prefill_mode")
 
     def set_withhold(self, wg: int):
         _check(lib().kie_set_withhold(self._h, int(wg)), "kie_set_withhold")

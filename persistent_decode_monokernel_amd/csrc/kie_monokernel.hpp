@@ -50,6 +50,13 @@ __device__ __forceinline__ T* opaque_s(T* p) {
   return p;
 }
 
+// The launch parameters are read through the constant address space: they
+// do not change during a launch, so every field read is a scalar load (scalar
+// data cache, lgkmcnt) instead of a vector-memory load whose wait would also
+// wait for the weight vectors already in flight.
+typedef const __attribute__((address_space(4))) Params CParams;
+__device__ __forceinline__ CParams& cparams(const Params* Pp) { return *(CParams*)opaque_s(Pp); }
+
 // Timeline stamp k of a slot, by thread `who` of the work-group (only on the
 // traced step).  k: 0 entry, 1 input arrived, 2 compute done, 3 exit.
 __device__ __forceinline__ void stamp(uint64_t* tr, int slot, int k, int t, int who = 0) {
@@ -86,7 +93,7 @@ struct Lds {
   int* imisc;      // 64 ints
 };
 
-__device__ __forceinline__ Lds lds_view(char* smem, const Params& P) {
+__device__ __forceinline__ Lds lds_view(char* smem, CParams& P) {
   Lds s;
   s.xres = reinterpret_cast<float*>(smem + P.lds_xres);
   s.xn = reinterpret_cast<uint16_t*>(smem + P.lds_xn);
@@ -101,14 +108,14 @@ __device__ __forceinline__ Lds lds_view(char* smem, const Params& P) {
 
 // Per-stage context: everything re-derived at stage entry (see note above).
 struct Sc {
-  const Params& P;
+  CParams& P;
   Lds s;
   Watch w;
   int t, wg, nb;
 };
 
 __device__ __forceinline__ Sc stage_ctx(const Params* Pp, char* smem) {
-  const Params& P = *opaque_s(Pp);
+  CParams& P = cparams(Pp);
   return Sc{P, lds_view(smem, P), Watch{P.timeout, P.ctl + CTL_STATUS}, opaque_v((int)threadIdx.x),
             (int)blockIdx.x, (int)gridDim.x};
 }
@@ -428,8 +435,10 @@ __device__ __forceinline__ bool gemv_any(const StagePlan& g, Prep prep, const ui
 }
 
 
-__device__ __forceinline__ const uint16_t* lw_ptr(const Params& P, int l, int k) {
-  return P.lw[l * W_PER_LAYER + k];
+__device__ __forceinline__ const uint16_t* lw_ptr(CParams& P, int l, int k) {
+  typedef const uint16_t* wptr;  // the weight table does not change during a launch either
+  const __attribute__((address_space(4))) wptr* tab = (const __attribute__((address_space(4))) wptr*)P.lw;
+  return tab[l * W_PER_LAYER + k];
 }
 
 // ---------------------------------------------------------------------------
@@ -438,7 +447,7 @@ __device__ __forceinline__ const uint16_t* lw_ptr(const Params& P, int l, int k)
 
 // The plan of GEMV stage `st` of layer l for this thread (tiling in
 // kie_tiling.hpp; matrix bases from the weight-pointer table).
-__device__ __forceinline__ StagePlan plan_stage(const Params& P, int l, int st, int t, int wg, int nb) {
+__device__ __forceinline__ StagePlan plan_stage(CParams& P, int l, int st, int t, int wg, int nb) {
   const TileDims D{P.d, P.hq, P.hkv, P.hd, P.F, P.V};
   const uint16_t* mats[M_COUNT] = {lw_ptr(P, l, W_Q),    lw_ptr(P, l, W_K),    lw_ptr(P, l, W_V),
                                    lw_ptr(P, l, W_O),    lw_ptr(P, l, W_GATE), lw_ptr(P, l, W_UP),
@@ -454,7 +463,7 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 0;
   stamp(tr, slot, 0, c.t);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int hd = P.hd, d = P.d;
   const int nq = P.hq * hd, nk = P.hkv * hd;
   const int N = nq + 2 * nk;
@@ -473,7 +482,7 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
   return true;
 }
 
-__device__ __forceinline__ void attn_chunking(const Params& P, int n, int& CL, int& nch) {
+__device__ __forceinline__ void attn_chunking(CParams& P, int n, int& CL, int& nch) {
   CL = (n + P.cmax - 1) / P.cmax;
   if (CL < kClMin) CL = kClMin;
   nch = (n + CL - 1) / CL;
@@ -500,7 +509,7 @@ __device__ __forceinline__ float safe_exp_diff(float a, float m) { return a == -
 template <int DT, int G>
 __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int slot = l * kStagesPerLayer + 1;
   stamp(tr, slot, 0, c.t);
   const int t = c.t;
@@ -684,7 +693,7 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 2;
   stamp(tr, slot, 0, c.t);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int hd = P.hd, hq = P.hq;
   int CL, nch;
   attn_chunking(P, pos + 1, CL, nch);
@@ -743,7 +752,7 @@ __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* 
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 3;
   stamp(tr, slot, 0, c.t);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int d = P.d, K = P.hq * P.hd;
   const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, l, GS_WO, c.t, c.wg, c.nb);
@@ -768,7 +777,7 @@ __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 4;
   stamp(tr, slot, 0, c.t);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int d = P.d, F = P.F;
   const int f0 = split_lo(F, c.nb, c.wg), f1 = split_lo(F, c.nb, c.wg + 1);
   const int nf = f1 - f0;
@@ -797,7 +806,7 @@ __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t
   const Sc c = stage_ctx(Pp, smem);
   const int slot = l * kStagesPerLayer + 5;
   stamp(tr, slot, 0, c.t);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int d = P.d, F = P.F;
   const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
@@ -857,7 +866,7 @@ template <int DT, int VD>
 __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, float* logits, float& best_v,
                                      int& best_i, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
-  const Params& P = c.P;
+  CParams& P = c.P;
   const int slot = P.L * kStagesPerLayer;
   stamp(tr, slot, 0, c.t);
   const int d = P.d, V = P.V;
@@ -897,7 +906,7 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
 __device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr, int nch_prev, int t_lo,
                                      uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
-  const Params& P = c.P;
+  CParams& P = c.P;
   if (c.t < t_lo) return;
   const uint32_t tt = c.t - t_lo, nt = kThreads - t_lo;
   const uint64_t sent2 = ~0ull;
@@ -925,7 +934,7 @@ __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* 
   const Sc c = stage_ctx(Pp, smem);
   const int slot = c.P.L * kStagesPerLayer + 1;
   stamp(tr, slot, 0, c.t);
-  const Params& P = c.P;
+  CParams& P = c.P;
   float gv = -INFINITY;
   int gi = 0x7FFFFFFF;
   bool ok = true;
@@ -964,7 +973,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
   bool ok = true;
   uint4 ring[kDepth];  // weight-stream ring shared by consecutive GEMV stages
   for (int s = 0; s < n_steps && ok; ++s) {
-    const Params& P = *opaque_s(Pp);
+    CParams& P = cparams(Pp);
     const int pos = P.pos0 + s;
     if (P.forced) tok = P.forced[s];
     uint32_t* X = P.xch + (size_t)(s % kRingSets) * P.xl.words;
@@ -984,7 +993,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     float bv = 0.f;
     int bi = 0;
     {
-      const Params& Q = *opaque_s(Pp);
+      CParams& Q = cparams(Pp);
       if (!Q.lm_last_only || s == Q.n_steps - 1) {
         float* lg = Q.logits ? Q.logits + (size_t)(Q.lm_last_only ? 0 : s) * Q.V : nullptr;
         if (!st_lmhead<DT, VD>(Pp, smem, X, lg, bv, bi, tr, ring)) {
@@ -1001,7 +1010,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     // set while the lower half gathers the partials (grid <= kThreads / 2)
     if (s >= 1) {
       int CL, nch;
-      attn_chunking(*Pp, pos, CL, nch);
+      attn_chunking(cparams(Pp), pos, CL, nch);
       reset_set(Pp, smem, Pp->xch + (size_t)((s + 2) % kRingSets) * Pp->xl.words, nch, kThreads / 2, tr);
     }
     if (!gather_token(Pp, smem, X, tok, tr)) {

@@ -665,15 +665,31 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
       uint32_t* att = X + P.xl.att;
       for (int idx = t; idx < HB * hd; idx += kThreads) {
         const int h = idx / hd, e = idx % hd;
-        float M = -INFINITY;
-#pragma unroll 8
-        for (int g2 = 0; g2 < ngrp; ++g2) M = fmaxf(M, gml[(g2 * HB + h) * 2]);
-        float Ls = 0.f, Os = 0.f;
-#pragma unroll 8
-        for (int g2 = 0; g2 < ngrp; ++g2) {
-          const float f = safe_exp_diff(gml[(g2 * HB + h) * 2], M);
-          Ls += gml[(g2 * HB + h) * 2 + 1] * f;
-          Os += go[(g2 * HB + h) * hd + e] * f;
+        // eight groups' values are read before any is used (clamped indices,
+        // the surplus masked), so the LDS round trips overlap
+        float M = -INFINITY, Ls = 0.f, Os = 0.f;
+        for (int g0 = 0; g0 < ngrp; g0 += 8) {
+          float mv[8], lv[8], ov[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int g2 = min(g0 + q, ngrp - 1);
+            mv[q] = gml[(g2 * HB + h) * 2];
+            lv[q] = gml[(g2 * HB + h) * 2 + 1];
+            ov[q] = go[(g2 * HB + h) * hd + e];
+          }
+          float Mb = M;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) Mb = fmaxf(Mb, mv[q]);
+          const float r = safe_exp_diff(M, Mb);  // rescale what was folded so far
+          Ls *= r;
+          Os *= r;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float f = g0 + q < ngrp ? safe_exp_diff(mv[q], Mb) : 0.f;
+            Ls += lv[q] * f;
+            Os += ov[q] * f;
+          }
+          M = Mb;
         }
         uint32_t* rowp = att + (((size_t)l * hq + (size_t)g * G + hb + h) * P.cmax + ch) * P.astride;
         xst32(rowp + 4 + e, __float_as_uint(Os));

@@ -13,7 +13,8 @@ does (everything else in the oracle stays float64).  bf16 keeps 8 significant
 bits, and against an exact float64 cache that one storage rounding alone moves
 the logits by ~0.15 over 512 steps: a property of the storage format, not an
 error of the kernel.  The engine feeds bf16 activations to the dot2 unit as
-two bf16 terms (value and rounding residual), so the GEMVs see ~16 bits.
+three bf16 terms (value and two rounding residuals), so the GEMVs see ~24
+bits of each activation.
 """
 import time
 

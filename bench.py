@@ -176,9 +176,10 @@ def gemv_probe_bench(n_copies: int = 16):
             torch.cuda.empty_cache()
 
 
-def ttft_bench(name: str, modes=("auto", "decode_loop")):
+def ttft_bench(name: str, modes=("auto", "decode_loop"), chunks=(0,)):
     """Time to first token: wall time of kie_prefill (prompt already on the
-    host, weights resident) for the workload's prompt, per prefill mode."""
+    host, weights resident) for the workload's prompt, per prefill mode (and
+    per matrix-core chunk size in the auto mode; 0 = the engine's default)."""
     import torch
 
     from persistent_decode_monokernel_amd import kie, synth
@@ -187,10 +188,12 @@ def ttft_bench(name: str, modes=("auto", "decode_loop")):
     s = wl.shape
     w = synth.make_weights(s, wl.weight_seed, device="cuda")
     prompt = synth.make_prompt(s, wl.n_prompt, wl.prompt_seed).tolist()
-    for mode in modes:
+    fits = tuple(c for c in chunks if c <= wl.n_prompt + 8) or (0,)  # the workspace holds max_seq positions
+    for mode, chunk in [(m, c) for m in modes for c in (fits if m == "auto" else (0,))]:
         eng = kie.Engine(s, max_seq=wl.n_prompt + 8)
         eng.load_weights(w)
         eng.set_prefill_mode(kie.KIE_PREFILL_AUTO if mode == "auto" else kie.KIE_PREFILL_DECODE_LOOP)
+        eng.set_prefill_chunk(chunk)
         eng.prefill(prompt[:64])  # warm-up
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -199,6 +202,7 @@ def ttft_bench(name: str, modes=("auto", "decode_loop")):
         dt = time.perf_counter() - t0
         flops = 2.0 * synth.param_count(s) * wl.n_prompt
         print(json.dumps({"ttft_ms": dt * 1e3, "workload": name, "prompt": wl.n_prompt, "mode": mode,
+                          "chunk": chunk if mode == "auto" else None,
                           "prompt_tokens_per_s": wl.n_prompt / dt, "dense_TFLOP_per_s": flops / dt / 1e12,
                           "first_token": tok}), flush=True)
         eng.close()
@@ -316,6 +320,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0, help="bytes read (= written) by the copy probe")
     ap.add_argument("--gemv", action="store_true", help="only run the isolated GEMV probe workload")
     ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")
+    ap.add_argument("--pf-chunk", type=int, nargs="+", default=[0],
+                    help="with --ttft: matrix-core chunk sizes to time (0 = default)")
+    ap.add_argument("--ttft-modes", nargs="+", default=["auto", "decode_loop"], choices=["auto", "decode_loop"],
+                    help="with --ttft: prefill modes to time")
     ap.add_argument("--timeline", type=int, default=None, metavar="STEP",
                     help="only print the per-stage timeline of decode step STEP of a 32-step launch")
     args = ap.parse_args()
@@ -337,7 +345,7 @@ def main():
         gemv_probe_bench()
         return
     if args.ttft:
-        ttft_bench(args.workload)
+        ttft_bench(args.workload, tuple(args.ttft_modes), tuple(args.pf_chunk))
         return
     if args.timeline is not None:
         from persistent_decode_monokernel_amd import synth

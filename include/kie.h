@@ -165,6 +165,14 @@ kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prom
 typedef enum { KIE_PREFILL_AUTO = 0, KIE_PREFILL_DECODE_LOOP = 1 } kie_prefill_mode;
 kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode);
 
+/* Prompt positions per matrix-core chunk in KIE_PREFILL_AUTO (each chunk runs
+ * every layer before the next starts).  The workspace holds the activations of
+ * min(max_seq, 4096) positions; 0 (default) uses all of them, a smaller value
+ * trades throughput for shorter launch sequences.  KIE_ERR_CAPACITY above the
+ * workspace's chunk (0 for shapes without the matrix-core path), KIE_ERR_ARG
+ * below 0.  Same results for every chunk size up to rounding order. */
+kie_status kie_set_prefill_chunk(kie_engine* e, int32_t positions);
+
 /* Greedy decode of up to n_steps tokens in ONE persistent kernel launch.
  * Step i feeds the pending token at position pos+i and emits token i.  If
  * eos_id >= 0 and a step emits eos_id, that token is written and counted and

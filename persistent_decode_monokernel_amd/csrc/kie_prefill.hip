@@ -171,73 +171,149 @@ __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int
   }
 }
 
-// ---- causal attention ------------------------------------------------------
+// ---- causal attention on the matrix cores ------------------------------------
 //
-// Lane group (hd/8 lanes, 8 dimensions each) per (query m, head h): online
-// softmax in base 2 over the cache rows 0 .. p0+m of KV head h / (hq/hkv).
-__device__ __forceinline__ float grp_sum(float v, int lpp) {
-  for (int o = 1; o < lpp; o <<= 1) v += __shfl_xor(v, o);
-  return v;
-}
+// Flash attention over the cache rows 0 .. p0+m of query m.  A work-group (4
+// waves) takes one block of query rows and one KV head g with up to four of
+// its query heads: HW = min(G, 4) heads and 4/HW sub-blocks of 32 rows, wave w
+// on head hb + w%HW and sub-block w/HW.  Per tile of 32 cache rows the
+// work-group stages K row-major and V transposed ([dimension][row]) in LDS,
+// double-buffered with one barrier per tile, the next tile's loads in flight
+// during the current tile's products.  Each wave then
+//   - forms S^T = K Q^T (32 rows x 32 queries) on the matrix cores, so that
+//     lane l owns query l%32 and 16 of the 32 rows (8i + 4(l/32) + j);
+//   - takes the online softmax in base 2 (scores pre-scaled by log2(e)/sqrt(hd)),
+//     the running maximum shared with lane l^32, the running sum per lane;
+//   - accumulates O^T += V^T P^T: P's fp16 values are already in the B-operand
+//     layout, with operand row 8(l/32) + s holding cache row
+//     16c + 8(s/4) + 4(l/32) + s%4 for product c = 0, 1 of the tile, and V^T is
+//     read from LDS in that same row order.
+// Rows past the work-group's last key re-read that key (finite values, masked).
+template <int HD>
+__global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, int hkv, int p0, int max_seq,
+                                               const uint16_t* kc, const uint16_t* vc, uint16_t* A16) {
+  constexpr int KS = HD + 8;  // K tile row stride (halves): 16-byte aligned rows, 4-bank skew
+  constexpr int VS = 36;      // V^T tile row stride (halves): 8-byte reads of 32 rows hit distinct banks
+  constexpr int KT = 32 * KS, VT = HD * VS, NO = HD / 32, NK = HD / 16;
+  constexpr int CPR = HD / 8;  // 16-byte pieces per cache row
+  __shared__ __align__(16) uint16_t lds[2 * (KT + VT)];
+  const int G = hq / hkv, HW = G < 4 ? G : 4, QB = 4 / HW, sets = G / HW;
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, hf = l >> 5;
+  const int rows = 32 * QB, nqb = (M + rows - 1) / rows;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // longest key ranges first
+  const int g = (int)blockIdx.y / sets, h = g * G + ((int)blockIdx.y % sets) * HW + wave % HW;
+  const int mq0 = qb * rows + (wave / HW) * 32;
+  const int nkeys = p0 + min((qb + 1) * rows, M), nt = (nkeys + 31) / 32;
+  const int qd = hq * HD, ldq = qd + 2 * hkv * HD;
 
-__global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, int hkv, int hd, int p0,
-                                               int max_seq, const uint16_t* kc, const uint16_t* vc, uint16_t* A16) {
-  const int lpp = hd >> 3, gpb = 256 / lpp;
-  const int grp = blockIdx.x * gpb + threadIdx.x / lpp, e8 = (threadIdx.x % lpp) * 8;
-  const int qd = hq * hd, ldq = qd + 2 * hkv * hd;
-  if (grp >= M * hq) return;  // whole groups leave together
-  const int m = grp / hq, h = grp % hq, g = h / (hq / hkv), n = p0 + m + 1;
-  const float scale = 1.4426950408889634f / sqrtf((float)hd);
-  float q[8], o[8];
-  const float* qp = QKV + (size_t)m * ldq + (size_t)h * hd + e8;
+  // this lane's query, scaled for base-2 exponentials, as B operands
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
+  h8_t qf[NK];
+  {
+    const float* qp = QKV + (size_t)min(mq0 + r, M - 1) * ldq + (size_t)h * HD + 8 * hf;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    q[e] = qp[e] * scale;
-    o[e] = 0.f;
-  }
-  const uint16_t* kb = kc + (size_t)g * max_seq * hd + e8;
-  const uint16_t* vb = vc + (size_t)g * max_seq * hd + e8;
-  float mx = -INFINITY, ls = 0.f;
-  // rows j .. j+3 in flight (rows beyond n re-read row n-1 and are not used)
-  constexpr int R = 4;
-  uint4 kr[R], vr[R];
-#pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int jj = min(s, n - 1);
-    kr[s] = *reinterpret_cast<const uint4*>(kb + (size_t)jj * hd);
-    vr[s] = *reinterpret_cast<const uint4*>(vb + (size_t)jj * hd);
-  }
-  for (int j0 = 0; j0 < n; j0 += R)
-#pragma unroll
-  for (int s = 0; s < R; ++s) {
-    const int j = j0 + s;
-    if (j >= n) break;
-    const uint4 kv = kr[s], vv = vr[s];
-    const int jn = min(j + R, n - 1);
-    kr[s] = *reinterpret_cast<const uint4*>(kb + (size_t)jn * hd);
-    vr[s] = *reinterpret_cast<const uint4*>(vb + (size_t)jn * hd);
-    const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w}, vw[4] = {vv.x, vv.y, vv.z, vv.w};
-    float sd = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sd += q[2 * e] * h2f(kw[e] & 0xFFFF) + q[2 * e + 1] * h2f(kw[e] >> 16);
-    sd = grp_sum(sd, lpp);
-    const float mn = fmaxf(mx, sd);
-    const float fo = mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mx - mn), fp = __builtin_amdgcn_exp2f(sd - mn);
-    ls = ls * fo + fp;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = o[2 * e] * fo + fp * h2f(vw[e] & 0xFFFF);
-      o[2 * e + 1] = o[2 * e + 1] * fo + fp * h2f(vw[e] >> 16);
+    for (int kk = 0; kk < NK; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 16 * kk);
+      const float4 b = *reinterpret_cast<const float4*>(qp + 16 * kk + 4);
+      qf[kk] = h8_t{(_Float16)(a.x * scale), (_Float16)(a.y * scale), (_Float16)(a.z * scale),
+                    (_Float16)(a.w * scale), (_Float16)(b.x * scale), (_Float16)(b.y * scale),
+                    (_Float16)(b.z * scale), (_Float16)(b.w * scale)};
     }
-    mx = mn;
   }
-  const float inv = 1.0f / ls;
-  uint4 out;
-  uint32_t ow[4];
+
+  // tile staging: thread t moves 16-byte piece t%CPR of cache rows 2(t/CPR), +1
+  const int tid = threadIdx.x, pe = tid % CPR, pr = tid / CPR;
+  const bool loader = tid < 16 * CPR;
+  const uint16_t* kb = kc + (size_t)g * max_seq * HD + 8 * pe;
+  const uint16_t* vb = vc + (size_t)g * max_seq * HD + 8 * pe;
+  uint4 k0r, k1r, v0r, v1r;
+  auto fetch = [&](int t) {
+    const int j0 = min(32 * t + 2 * pr, nkeys - 1), j1 = min(32 * t + 2 * pr + 1, nkeys - 1);
+    k0r = *reinterpret_cast<const uint4*>(kb + (size_t)j0 * HD);
+    k1r = *reinterpret_cast<const uint4*>(kb + (size_t)j1 * HD);
+    v0r = *reinterpret_cast<const uint4*>(vb + (size_t)j0 * HD);
+    v1r = *reinterpret_cast<const uint4*>(vb + (size_t)j1 * HD);
+  };
+  auto stage = [&](int buf) {
+    uint16_t* kt = lds + buf * (KT + VT);
+    uint16_t* vt = kt + KT;
+    *reinterpret_cast<uint4*>(kt + (2 * pr) * KS + 8 * pe) = k0r;
+    *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * KS + 8 * pe) = k1r;
+    const uint32_t a[4] = {v0r.x, v0r.y, v0r.z, v0r.w}, b[4] = {v1r.x, v1r.y, v1r.z, v1r.w};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ow[e] = (uint32_t)f2h(o[2 * e] * inv) | ((uint32_t)f2h(o[2 * e + 1] * inv) << 16);
-  out.x = ow[0]; out.y = ow[1]; out.z = ow[2]; out.w = ow[3];
-  *reinterpret_cast<uint4*>(A16 + (size_t)m * qd + (size_t)h * hd + e8) = out;
+    for (int u = 0; u < 4; ++u) {  // dimensions 8pe+2u and 8pe+2u+1, rows 2pr (low half) and 2pr+1
+      *reinterpret_cast<uint32_t*>(vt + (8 * pe + 2 * u) * VS + 2 * pr) = (a[u] & 0xFFFFu) | (b[u] << 16);
+      *reinterpret_cast<uint32_t*>(vt + (8 * pe + 2 * u + 1) * VS + 2 * pr) = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+    }
+  };
+
+  f16x_t o[NO] = {};
+  float mrun = -INFINITY, lrun = 0.f;
+  const int qpos = p0 + mq0 + r;
+  if (loader) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < nt; ++t) {
+    if (loader && t + 1 < nt) fetch(t + 1);
+    const uint16_t* kt = lds + (t & 1) * (KT + VT);
+    const uint16_t* vt = kt + KT;
+    f16x_t s = {};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const h8_t*>(kt + r * KS + 16 * kk + 8 * hf),
+                                                 qf[kk], s, 0, 0, 0);
+    const int k0 = 32 * t;
+    if (k0 + 31 > p0 + mq0) {  // the tile reaches past this wave's first query: causal mask
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (k0 + 8 * (e >> 2) + 4 * hf + (e & 3) > qpos) s[e] = -INFINITY;
+    }
+    float tm = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, s[e]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float mn = fmaxf(mrun, tm);  // finite: cache row 0 is in every query's range
+    const float al = __builtin_amdgcn_exp2f(mrun - mn);
+    float ps = 0.f;
+    h8_t pb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(s[e] - mn);
+      ps += p;
+      pb[e >> 3][e & 7] = (_Float16)p;
+    }
+    lrun = lrun * al + ps;
+    mrun = mn;
+#pragma unroll
+    for (int ot = 0; ot < NO; ++ot) o[ot] *= al;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ot = 0; ot < NO; ++ot) {
+        const uint16_t* vp = vt + (32 * ot + r) * VS + 16 * c + 4 * hf;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp), hi = *reinterpret_cast<const uint2*>(vp + 8);
+        const h8_t a = __builtin_bit_cast(h8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[ot] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[c], o[ot], 0, 0, 0);
+      }
+    if (loader && t + 1 < nt) stage((t + 1) & 1);
+    __syncthreads();
+  }
+  const float inv = 1.0f / (lrun + __shfl_xor(lrun, 32));
+  const int m = mq0 + r;
+  if (m < M) {
+    uint16_t* op = A16 + (size_t)m * qd + (size_t)h * HD + 4 * hf;
+#pragma unroll
+    for (int ot = 0; ot < NO; ++ot)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x_t& v = o[ot];
+        const uint2 w = make_uint2((uint32_t)f2h(v[4 * i] * inv) | ((uint32_t)f2h(v[4 * i + 1] * inv) << 16),
+                                   (uint32_t)f2h(v[4 * i + 2] * inv) | ((uint32_t)f2h(v[4 * i + 3] * inv) << 16));
+        *reinterpret_cast<uint2*>(op + 32 * ot + 8 * i) = w;  // dimensions 32ot + 8i + 4(l/32) + 0..3
+      }
+  }
 }
 
 }  // namespace
@@ -245,7 +321,7 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
 bool prefill_supported(const kie_config& c) {
   const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   const int kstep = 16 * kPfDepth;
-  return c.dtype == KIE_F16 && c.d_model % 128 == 0 && qd % 128 == 0 && kvd % 128 == 0 && c.d_ffn % 128 == 0 &&
+  return c.dtype == KIE_F16 && (c.head_dim == 64 || c.head_dim == 128) && c.d_model % 128 == 0 && qd % 128 == 0 && kvd % 128 == 0 && c.d_ffn % 128 == 0 &&
          c.d_model % kstep == 0 && qd % kstep == 0 && c.d_ffn % kstep == 0;
 }
 
@@ -268,9 +344,14 @@ hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M)
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
     pf_rope_kv<<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope, p0,
                                                         c.max_seq, x.kc + plane, x.vc + plane);
-    const int gpb = 256 / (c.head_dim / 8);
-    pf_attn<<<(M * c.n_heads + gpb - 1) / gpb, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, p0,
-                                                             c.max_seq, x.kc + plane, x.vc + plane, x.A16);
+    const int G = c.n_heads / c.n_kv_heads, hw = G < 4 ? G : 4, rows = 32 * (4 / hw);
+    const dim3 ag((M + rows - 1) / rows, c.n_kv_heads * (G / hw));
+    if (c.head_dim == 128)
+      pf_attn<128><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane, x.vc + plane,
+                                       x.A16);
+    else
+      pf_attn<64><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane, x.vc + plane,
+                                      x.A16);
     pf_gemm<EPI_ADD><<<dim3(d / 128, mt), blk, 0, st>>>(x.A16, M, qd, w[W_O], nullptr, x.X, d, nullptr, 0);
     pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, x.Xn);
     pf_gemm<EPI_SWIGLU><<<dim3(F / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_GATE], w[W_UP], nullptr, 0, x.H16, F);

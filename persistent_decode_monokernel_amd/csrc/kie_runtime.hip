@@ -197,6 +197,7 @@ struct kie_engine {
   int trace_step = 0;
   std::vector<const uint16_t*> wtab;  // host copy of the per-layer weight table
   int prefill_mode = KIE_PREFILL_AUTO;
+  int prefill_chunk = 0;  // positions per matrix-core chunk; 0 = the workspace's (lay.pf_chunk)
 };
 
 extern "C" const char* kie_status_string(kie_status s) {
@@ -454,8 +455,9 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
     x.A16 = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_a);
     x.H16 = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_h);
     first = n_prompt - 1;
-    for (int p0 = 0; p0 < first; p0 += e->lay.pf_chunk) {
-      const int M = first - p0 < e->lay.pf_chunk ? first - p0 : e->lay.pf_chunk;
+    const int chunk = e->prefill_chunk > 0 ? e->prefill_chunk : e->lay.pf_chunk;
+    for (int p0 = 0; p0 < first; p0 += chunk) {
+      const int M = first - p0 < chunk ? first - p0 : chunk;
       KIE_HIP(prefill_chunk(x, forced + p0, p0, M));
     }
   }
@@ -481,6 +483,13 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
 extern "C" kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode) {
   if (!e || (mode != KIE_PREFILL_AUTO && mode != KIE_PREFILL_DECODE_LOOP)) return KIE_ERR_ARG;
   e->prefill_mode = mode;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_prefill_chunk(kie_engine* e, int32_t positions) {
+  if (!e || positions < 0) return KIE_ERR_ARG;
+  if (positions > e->lay.pf_chunk) return KIE_ERR_CAPACITY;
+  e->prefill_chunk = positions;
   return KIE_OK;
 }
 

@@ -69,6 +69,7 @@ SIGNATURES = {
     "kie_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kie_config_validate": (ctypes.c_int, [ctypes.POINTER(kie_config)]),
     "kie_set_prefill_mode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_prefill_chunk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kie_config)]),
     "kie_create": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                   ctypes.POINTER(ctypes.c_void_p)]),
@@ -265,6 +266,10 @@ class Engine:
     def set_prefill_mode(self, mode: int):
         """KIE_PREFILL_AUTO (matrix-core prompt path where supported) or KIE_PREFILL_DECODE_LOOP."""
         _check(lib().kie_set_prefill_mode(self._h, int(mode)), "kie_set_prefill_mode")
+
+    def set_prefill_chunk(self, positions: int):
+        """Prompt positions per matrix-core chunk (0 = as many as the workspace holds)."""
+        _check(lib().kie_set_prefill_chunk(self._h, int(positions)), "kie_set_prefill_chunk")
 
     def set_withhold(self, wg: int):
         _check(lib().kie_set_withhold(self._h, int(wg)), "kie_set_withhold")

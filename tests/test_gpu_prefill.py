@@ -5,8 +5,10 @@ position as one forced step of the persistent kernel.  Checked against the
 oracle: the logits of the last prompt position and the first token, the KV
 cache rows the prompt path wrote (the oracle's keys/values rounded to fp16,
 the cache format), and the decode that continues from them.  Prompts cover a
-ragged tail (not a multiple of the 64-row tiles), two chunks (1100 > 1024
-positions per chunk) and the one-token prompt (no matrix-core part).
+ragged tail (not a multiple of the 64-row tiles), several chunks (1100
+positions in chunks of 512), the one-token prompt (no matrix-core part), and
+every query-head grouping (1, 2, 4, 8 query heads per KV head) at head_dim 64
+and 128 over several 32-row attention tiles.
 """
 import pytest
 import torch
@@ -21,11 +23,20 @@ MID = synth.ModelShape("mid", 2, 512, 8, 2, 64, 1024, 1000, synth.F16)
 KV_TOL = 2e-2  # max |cache row - oracle row| (values ~N(0, 1); fp16 storage 2^-11 relative)
 
 
-def run_case(s, P, n_dec, seed=31):
+GROUPINGS = {
+    "g1_hd128": synth.ModelShape("g1_hd128", 2, 512, 4, 4, 128, 1024, 1000, synth.F16),
+    "g2_hd64": synth.ModelShape("g2_hd64", 2, 512, 8, 4, 64, 1024, 1000, synth.F16),
+    "g4_hd128": synth.ModelShape("g4_hd128", 1, 1024, 8, 2, 128, 2048, 1000, synth.F16),
+    "g8_hd64": synth.ModelShape("g8_hd64", 2, 512, 8, 1, 64, 1024, 1000, synth.F16),
+}
+
+
+def run_case(s, P, n_dec, seed=31, chunk=0):
     w = synth.make_weights(s, seed, device="cuda", gain_jitter=0.1)
     prompt = synth.make_prompt(s, P, seed + 1).tolist()
     eng = kie.Engine(s, max_seq=P + n_dec + 1)
     eng.load_weights(w)
+    eng.set_prefill_chunk(chunk)
     tok0, lg0 = eng.prefill(prompt, want_logits=True)
     k, v, pend = eng.export_kv()
     toks, lgs, st = eng.decode(n_dec, want_logits=True)
@@ -48,8 +59,13 @@ def test_tiny_prompt_path(P):
     run_case(synth.TINY, P, 24)
 
 
-def test_two_chunks_ragged():
-    run_case(MID, 1100, 16)
+def test_three_chunks_ragged():
+    run_case(MID, 1100, 16, chunk=512)
+
+
+@pytest.mark.parametrize("name", list(GROUPINGS))
+def test_query_head_groupings(name):
+    run_case(GROUPINGS[name], 300, 8)
 
 
 def test_one_token_prompt():
@@ -82,4 +98,10 @@ def test_mode_argument_checked():
     with pytest.raises(kie.KieError) as ei:
         eng.set_prefill_mode(7)
     assert ei.value.status == kie.KIE_ERR_ARG
+    for bad, code in ((-1, kie.KIE_ERR_ARG), (33, kie.KIE_ERR_CAPACITY)):  # workspace chunk = max_seq = 32
+        with pytest.raises(kie.KieError) as ei:
+            eng.set_prefill_chunk(bad)
+        assert ei.value.status == code
+    eng.set_prefill_chunk(32)
+    eng.set_prefill_chunk(0)
     eng.close()

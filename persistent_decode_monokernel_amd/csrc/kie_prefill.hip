@@ -69,70 +69,140 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t
 
 // ---- GEMM: C[M][N] = A[M][K] W[N][K]^T on the matrix cores --------------------
 //
-// Work-group (4 waves) tile 64 x 128; wave w: rows 32*(w/2) .., columns
-// 64*(w%2) .. as two 32x32 accumulators.  Operands go straight from memory to
-// registers (16 contiguous bytes per lane per operand and k-step), kPfDepth
-// k-steps ahead of the matrix-core instructions.  Rows of A beyond M re-read
-// row M-1 and are not stored.  Requires N % 128 == 0 and K % (16 kPfDepth) == 0.
+// Work-group (4 waves) tile 128 x 128, k-tiles of 64 staged in LDS (row-major,
+// rows padded to 144 bytes so that the 16-byte operand reads of 16 lanes hit
+// distinct banks), double-buffered with one barrier per k-tile; the next
+// k-tile's global loads are in flight during the current one's products.
+// Wave (wm, wn) computes rows 64wm .. and columns 64wn .. as 2 x 2
+// accumulators of 32 x 32.  Both operands are k-contiguous in memory and in
+// LDS, so every lane reads its 8 consecutive k values with one 16-byte load.
+//   EPI_STORE / EPI_ADD: W is up to three matrices stacked along N (the
+//   column tile picks one; segment widths are multiples of 128).
+//   EPI_SWIGLU: a work-group tile covers 64 output columns; its B rows are 64
+//   rows of the gate matrix then the same 64 rows of the up matrix, and wave
+//   (wm, wn) takes gate columns 32wn .. and the matching up columns, so gate
+//   and up of one output land in the same lane: H = silu(gate) * up.
+// Rows of A beyond M re-read row M-1 and are not stored.  K % 64 == 0.
 enum : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
-constexpr int kPfDepth = 4;
+constexpr int kTM = 128, kTN = 128, kBK = 64, kLS = kBK + 8;  // LDS row stride in halves
+constexpr int kTile = kTM * kLS;                                // halves per operand tile
+
+struct GemmB {
+  const uint16_t* w[3];  // stacked matrices ([rows][K] each); EPI_SWIGLU: gate, up
+  int end[3];            // cumulative row counts
+};
 
 template <int EPI>
-__global__ __launch_bounds__(256) void pf_gemm(const uint16_t* A, int M, int K, const uint16_t* W,
-                                               const uint16_t* W2, float* C, int ldc, uint16_t* H, int ldh) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int m0 = blockIdx.y * 64 + (wave >> 1) * 32, n0 = blockIdx.x * 128 + (wave & 1) * 64;
-  const int ar = min(m0 + (l & 31), M - 1);
-  const int kq = (l >> 5) * 8;
-  const uint16_t* ap = A + (size_t)ar * K + kq;
-  const uint16_t* bp = W + (size_t)(n0 + (l & 31)) * K + kq;
-  const uint16_t* cp = EPI == EPI_SWIGLU ? W2 + (size_t)(n0 + (l & 31)) * K + kq : nullptr;
-  const size_t b32 = (size_t)32 * K;
-  constexpr int NB = EPI == EPI_SWIGLU ? 4 : 2;  // B operands per k-step: 2 column tiles (x 2 matrices)
-  f16x_t acc[NB] = {};
-  h8_t ra[kPfDepth], rb[kPfDepth][NB];
-  auto load = [&](int s, int k) {
-    ra[s] = ld8(ap + k);
-    rb[s][0] = ld8(bp + k);
-    rb[s][1] = ld8(bp + b32 + k);
-    if constexpr (EPI == EPI_SWIGLU) {
-      rb[s][2] = ld8(cp + k);
-      rb[s][3] = ld8(cp + b32 + k);
-    }
-  };
-#pragma unroll
-  for (int s = 0; s < kPfDepth; ++s) load(s, s * 16);
-  for (int k0 = 0; k0 < K; k0 += 16 * kPfDepth) {
-#pragma unroll
-    for (int s = 0; s < kPfDepth; ++s) {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ra[s], rb[s][b], acc[b], 0, 0, 0);
-      const int kn = k0 + (s + kPfDepth) * 16;
-      if (kn < K) load(s, kn);
-    }
+__global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int K, GemmB wb, float* C, int ldc,
+                                                  uint16_t* H, int ldh) {
+  __shared__ __align__(16) uint16_t lds[2][2 * kTile];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 31, hf = l >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * kTM;
+  // B rows of this tile: 128 consecutive rows of one stacked matrix, or 64 gate + 64 up rows
+  const uint16_t* b_lo;
+  const uint16_t* b_hi;
+  int n0;
+  if constexpr (EPI == EPI_SWIGLU) {
+    n0 = blockIdx.x * 64;
+    b_lo = wb.w[0] + (size_t)n0 * K;
+    b_hi = wb.w[1] + (size_t)n0 * K;
+  } else {
+    n0 = blockIdx.x * kTN;
+    const bool s0 = n0 < wb.end[0], s1 = n0 < wb.end[1];  // selects, not an indexed argument (no scratch copy)
+    const uint16_t* wsel = s0 ? wb.w[0] : s1 ? wb.w[1] : wb.w[2];
+    b_lo = wsel + (size_t)(n0 - (s0 ? 0 : s1 ? wb.end[0] : wb.end[1])) * K;
+    b_hi = b_lo + (size_t)64 * K;
   }
+  // staging: thread t moves 16-byte piece t%8 of rows t/8 + 32i (i = 0..3) of both tiles
+  const int pc = tid & 7, pr = tid >> 3;
+  const uint16_t* ag[4];
+  const uint16_t* bg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int row = pr + 32 * i;
+    ag[i] = A + (size_t)min(m0 + row, M - 1) * K + 8 * pc;
+    bg[i] = (row < 64 ? b_lo + (size_t)row * K : b_hi + (size_t)(row - 64) * K) + 8 * pc;
+  }
+  // operand rows read by this lane: A rows 64wm + 32i + r; B rows per column block j
+  const int arow0 = 64 * wm + r;
+  const int brow0 = EPI == EPI_SWIGLU ? 32 * wn + r : 64 * wn + r;
+  const int bstep = EPI == EPI_SWIGLU ? 64 : 32;  // B row offset of column block 1 (up rows for SwiGLU)
+  const int soff = pr * kLS + 8 * pc;              // this thread's staging offset (row pr, piece pc)
+  f16x_t acc[2][2] = {};
+  const int nk = K / kBK;
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+#define KIE_PF_FETCH(k0)                                              \
+  do {                                                                \
+    ra0 = *reinterpret_cast<const uint4*>(ag[0] + (k0));              \
+    ra1 = *reinterpret_cast<const uint4*>(ag[1] + (k0));              \
+    ra2 = *reinterpret_cast<const uint4*>(ag[2] + (k0));              \
+    ra3 = *reinterpret_cast<const uint4*>(ag[3] + (k0));              \
+    rb0 = *reinterpret_cast<const uint4*>(bg[0] + (k0));              \
+    rb1 = *reinterpret_cast<const uint4*>(bg[1] + (k0));              \
+    rb2 = *reinterpret_cast<const uint4*>(bg[2] + (k0));              \
+    rb3 = *reinterpret_cast<const uint4*>(bg[3] + (k0));              \
+  } while (0)
+#define KIE_PF_STAGE(buf)                                                       \
+  do {                                                                          \
+    uint16_t* sa = &lds[buf][soff];                                             \
+    *reinterpret_cast<uint4*>(sa) = ra0;                                        \
+    *reinterpret_cast<uint4*>(sa + 32 * kLS) = ra1;                             \
+    *reinterpret_cast<uint4*>(sa + 64 * kLS) = ra2;                             \
+    *reinterpret_cast<uint4*>(sa + 96 * kLS) = ra3;                             \
+    *reinterpret_cast<uint4*>(sa + kTile) = rb0;                                \
+    *reinterpret_cast<uint4*>(sa + kTile + 32 * kLS) = rb1;                     \
+    *reinterpret_cast<uint4*>(sa + kTile + 64 * kLS) = rb2;                     \
+    *reinterpret_cast<uint4*>(sa + kTile + 96 * kLS) = rb3;                     \
+  } while (0)
+  KIE_PF_FETCH(0);
+  KIE_PF_STAGE(0);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) KIE_PF_FETCH((t + 1) * kBK);
+    const uint16_t* la = lds[t & 1];
+    const uint16_t* lb = la + kTile;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + i * 8 + (l >> 5) * 4 + j;
-      if (m >= M) continue;
-      const int n = n0 + (l & 31);
-      if constexpr (EPI == EPI_STORE) {
-        C[(size_t)m * ldc + n] = acc[0][i * 4 + j];
-        C[(size_t)m * ldc + n + 32] = acc[1][i * 4 + j];
-      } else if constexpr (EPI == EPI_ADD) {
-        C[(size_t)m * ldc + n] += acc[0][i * 4 + j];
-        C[(size_t)m * ldc + n + 32] += acc[1][i * 4 + j];
-      } else {
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int ko = 16 * kk + 8 * hf;
+      const h8_t a0 = *reinterpret_cast<const h8_t*>(la + arow0 * kLS + ko);
+      const h8_t a1 = *reinterpret_cast<const h8_t*>(la + (arow0 + 32) * kLS + ko);
+      const h8_t b0 = *reinterpret_cast<const h8_t*>(lb + brow0 * kLS + ko);
+      const h8_t b1 = *reinterpret_cast<const h8_t*>(lb + (brow0 + bstep) * kLS + ko);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    if (t + 1 < nk) KIE_PF_STAGE((t + 1) & 1);
+    __syncthreads();
+  }
+#undef KIE_PF_FETCH
+#undef KIE_PF_STAGE
+  // accumulator element 4ii + jj of acc[i][j]: row 64wm + 32i + 8ii + 4hf + jj, column block j, column r
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const float gt = acc[b][i * 4 + j], up = acc[b + 2][i * 4 + j];
-          H[(size_t)m * ldh + n + 32 * b] = f2h(gt / (1.0f + expf(-gt)) * up);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = m0 + 64 * wm + 32 * i + 8 * ii + 4 * hf + jj;
+        if (m >= M) continue;
+        const int e = 4 * ii + jj;
+        if constexpr (EPI == EPI_SWIGLU) {
+          const float gt = acc[i][0][e], up = acc[i][1][e];
+          H[(size_t)m * ldh + n0 + 32 * wn + r] = f2h(gt / (1.0f + expf(-gt)) * up);
+        } else {
+          float* cp = C + (size_t)m * ldc + n0 + 64 * wn + r;
+          if constexpr (EPI == EPI_ADD) {
+            cp[0] += acc[i][0][e];
+            cp[32] += acc[i][1][e];
+          } else {
+            cp[0] = acc[i][0][e];
+            cp[32] = acc[i][1][e];
+          }
         }
       }
-    }
-  }
 }
 
 // ---- rotary embedding, KV append ------------------------------------------
@@ -320,9 +390,8 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
 
 bool prefill_supported(const kie_config& c) {
   const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
-  const int kstep = 16 * kPfDepth;
-  return c.dtype == KIE_F16 && (c.head_dim == 64 || c.head_dim == 128) && c.d_model % 128 == 0 && qd % 128 == 0 && kvd % 128 == 0 && c.d_ffn % 128 == 0 &&
-         c.d_model % kstep == 0 && qd % kstep == 0 && c.d_ffn % kstep == 0;
+  return c.dtype == KIE_F16 && (c.head_dim == 64 || c.head_dim == 128) && c.d_model % kTN == 0 && qd % kTN == 0 &&
+         kvd % kTN == 0 && c.d_ffn % kTN == 0 && c.d_model % kBK == 0 && qd % kBK == 0 && c.d_ffn % kBK == 0;
 }
 
 hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
@@ -330,17 +399,15 @@ hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M)
   const int d = c.d_model, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, F = c.d_ffn;
   const int ldq = qd + 2 * kvd;
   const dim3 blk(256);
-  const int mt = (M + 63) / 64;
+  const int mt = (M + kTM - 1) / kTM;
   hipStream_t st = x.stream;
   pf_embed<<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
   for (int l = 0; l < c.n_layers; ++l) {
     const uint16_t* const* w = x.wtab + (size_t)l * W_PER_LAYER;
     const size_t plane = (size_t)l * c.n_kv_heads * c.max_seq * c.head_dim;
     pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_ATTN_NORM], c.rms_eps, M, d, x.Xn);
-    pf_gemm<EPI_STORE><<<dim3(qd / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_Q], nullptr, x.QKV, ldq, nullptr, 0);
-    pf_gemm<EPI_STORE><<<dim3(kvd / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_K], nullptr, x.QKV + qd, ldq, nullptr, 0);
-    pf_gemm<EPI_STORE><<<dim3(kvd / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_V], nullptr, x.QKV + qd + kvd, ldq,
-                                                            nullptr, 0);
+    const GemmB bqkv{{w[W_Q], w[W_K], w[W_V]}, {qd, qd + kvd, ldq}};
+    pf_gemm<EPI_STORE><<<dim3(ldq / kTN, mt), blk, 0, st>>>(x.Xn, M, d, bqkv, x.QKV, ldq, nullptr, 0);
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
     pf_rope_kv<<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope, p0,
                                                         c.max_seq, x.kc + plane, x.vc + plane);
@@ -352,10 +419,12 @@ hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M)
     else
       pf_attn<64><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane, x.vc + plane,
                                       x.A16);
-    pf_gemm<EPI_ADD><<<dim3(d / 128, mt), blk, 0, st>>>(x.A16, M, qd, w[W_O], nullptr, x.X, d, nullptr, 0);
+    pf_gemm<EPI_ADD><<<dim3(d / kTN, mt), blk, 0, st>>>(x.A16, M, qd, GemmB{{w[W_O]}, {d, d, d}}, x.X, d, nullptr, 0);
     pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, x.Xn);
-    pf_gemm<EPI_SWIGLU><<<dim3(F / 128, mt), blk, 0, st>>>(x.Xn, M, d, w[W_GATE], w[W_UP], nullptr, 0, x.H16, F);
-    pf_gemm<EPI_ADD><<<dim3(d / 128, mt), blk, 0, st>>>(x.H16, M, F, w[W_DOWN], nullptr, x.X, d, nullptr, 0);
+    pf_gemm<EPI_SWIGLU><<<dim3(F / 64, mt), blk, 0, st>>>(x.Xn, M, d, GemmB{{w[W_GATE], w[W_UP]}, {F, F, F}}, nullptr,
+                                                          0, x.H16, F);
+    pf_gemm<EPI_ADD><<<dim3(d / kTN, mt), blk, 0, st>>>(x.H16, M, F, GemmB{{w[W_DOWN]}, {d, d, d}}, x.X, d, nullptr,
+                                                        0);
   }
   return hipGetLastError();
 }

@@ -211,7 +211,7 @@ def ttft_bench(name: str, modes=("auto", "decode_loop"), chunks=(0,)):
 STAGES = ("qkv", "attention", "merge", "wo", "gate/up", "down")
 
 
-def timeline(wl, step: int = 10, n_decode: int = 32):
+def timeline(wl, step: int = 10, n_decode: int = 32, samp=None):
     """Per-token timeline of one decode step (the step-th of a kie_decode(n_decode)
     launch after the workload's prompt): for every stage, the median over
     work-groups of the time from stage entry until its input had arrived (the
@@ -230,6 +230,8 @@ def timeline(wl, step: int = 10, n_decode: int = 32):
     P = wl.n_prompt
     eng = kie.Engine(s, max_seq=P + n_decode, device=dev)
     eng.load_weights(w)
+    if samp is not None:
+        eng.set_sampling(samp[0], int(samp[1]), samp[2], wl.prompt_seed)
     eng.prefill(synth.make_prompt(s, P, wl.prompt_seed).tolist())
     buf = torch.zeros(eng.trace_words(), dtype=torch.int64, device=dev)
     eng.set_trace(buf, step)
@@ -268,6 +270,12 @@ def timeline(wl, step: int = 10, n_decode: int = 32):
     x = tr[6 * L + 1]  # gather: entry, partials gathered, (recycling done), token known
     print(f"{'step tail':10s} {G:8d} {np.median(x[:, 1] - x[:, 0]):7.2f} {np.median(x[:, 3] - x[:, 1]):8.2f} "
           f"{0.0:7.2f} {x[:, 3].max() - tr[6 * L, :, 3].max():14.2f}   (wait = all argmax partials gathered)")
+    if samp is not None:
+        x = tr[6 * L + 2]  # work-group 0: entry, lists gathered and merged per wave, token drawn, exit
+        print(f"{'sampling':10s} {1:8d} {x[0, 1] - x[0, 0]:7.2f} {x[0, 2] - x[0, 1]:8.2f} {x[0, 3] - x[0, 2]:7.2f} "
+              f"{x[:, 3].max() - tr[6 * L + 1, :, 3].max():14.2f}   (work-group 0: wait = lists loaded and merged "
+              f"per wave, compute = cross-wave merge and draw; others wait {np.median(x[1:, 3] - x[1:, 0]):.2f} us "
+              f"for the token)")
     print(f"per layer: critical span {tot_span:.2f} us, of which hand-off waits (sum of stage medians) {tot_wait:.2f} us "
           f"= {tot_wait / tot_span:.0%}")
 
@@ -324,6 +332,8 @@ def main():
                     help="with --ttft: matrix-core chunk sizes to time (0 = default)")
     ap.add_argument("--ttft-modes", nargs="+", default=["auto", "decode_loop"], choices=["auto", "decode_loop"],
                     help="with --ttft: prefill modes to time")
+    ap.add_argument("--sampling", type=float, nargs=3, default=None, metavar=("T", "TOP_K", "TOP_P"),
+                    help="decode with on-device temperature / top-k / nucleus sampling instead of greedy")
     ap.add_argument("--timeline", type=int, default=None, metavar="STEP",
                     help="only print the per-stage timeline of decode step STEP of a 32-step launch")
     args = ap.parse_args()
@@ -350,7 +360,7 @@ def main():
     if args.timeline is not None:
         from persistent_decode_monokernel_amd import synth
 
-        timeline(synth.WORKLOADS[args.workload], step=args.timeline)
+        timeline(synth.WORKLOADS[args.workload], step=args.timeline, samp=args.sampling)
         return
 
     import torch
@@ -369,6 +379,11 @@ def main():
     prompt = synth.make_prompt(s, P, wl.prompt_seed).tolist()
     eng = kie.Engine(s, max_seq=P + max(K, Wm, 1), device=dev)
     eng.load_weights(w)
+    samp = None
+    if args.sampling is not None:
+        samp = {"temperature": args.sampling[0], "top_k": int(args.sampling[1]), "top_p": args.sampling[2],
+                "seed": wl.prompt_seed}
+        eng.set_sampling(samp["temperature"], samp["top_k"], samp["top_p"], samp["seed"])
     info = eng.info()
     log(f"engine grid {info.grid} x {info.block}, lds {info.lds_bytes} B")
 
@@ -411,7 +426,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: {s.n_layers}L d{s.d_model} GQA {s.n_heads}/{s.n_kv_heads}x{s.head_dim} "
-                        f"F{s.d_ffn} V{s.vocab}, prompt {P}, decode {K}, batch 1, greedy",
+                        f"F{s.d_ffn} V{s.vocab}, prompt {P}, decode {K}, batch 1, "
+                        + ("greedy" if samp is None else
+                           f"sampled (T {samp['temperature']}, top-k {samp['top_k']}, top-p {samp['top_p']})"),
             "prompt": P,
             "decode_tokens": K,
             "batch": 1,
@@ -422,7 +439,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": measured_traffic(wl.name, n_done),
+            "traffic": measured_traffic(wl.name, n_done) if samp is None else None,
         },
         "kernel": {
             "name": "kie::monokernel (persistent decode)",
@@ -432,6 +449,7 @@ def main():
             "grid": inf.grid,
             "block": inf.block,
         },
+        "sampling": samp,
         "prefill_s": prefill_s,
         "status": st,
     }

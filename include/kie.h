@@ -173,7 +173,28 @@ kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode);
  * below 0.  Same results for every chunk size up to rounding order. */
 kie_status kie_set_prefill_chunk(kie_engine* e, int32_t positions);
 
-/* Greedy decode of up to n_steps tokens in ONE persistent kernel launch.
+/* How the emitted tokens are chosen from the LM-head logits (by kie_decode
+ * and for kie_prefill's next token).  The pages end every token with LM-head
+ * sampling and the end-of-sequence check on the device (revietech.ru page,
+ * section "Chto takoye monokernel") without naming a rule; this is the rule
+ * taken.
+ *   temperature <= 0: greedy, the first index of the largest logit (default;
+ *   top_k, top_p and seed are then ignored).
+ *   temperature > 0: candidates are the top_k largest logits (ties to the
+ *   lower index), 1 <= top_k <= min(64, vocab); weights exp((z - zmax) /
+ *   temperature); the nucleus is the shortest prefix of the candidates, in
+ *   that order, whose weight reaches the fraction top_p (0 < top_p <= 1) of
+ *   their total; the token is the first nucleus candidate whose cumulative
+ *   weight exceeds u times the nucleus weight.  u = (x >> 8) * 2^-24, x the
+ *   first output word of Philox4x32-10 (Salmon et al., SC'11) with counter
+ *   (p, 0, 0, 0) and key (seed low 32 bits, seed high 32 bits), p the position
+ *   of the token fed to the step: the sequence does not depend on how decoding
+ *   is split into calls.  Weights and sums are fp32 on the device.
+ * KIE_ERR_ARG for arguments out of range (the previous setting stays). */
+kie_status kie_set_sampling(kie_engine* e, float temperature, int32_t top_k, float top_p, uint64_t seed);
+
+/* Decode of up to n_steps tokens (greedy unless kie_set_sampling chose
+ * otherwise) in ONE persistent kernel launch.
  * Step i feeds the pending token at position pos+i and emits token i.  If
  * eos_id >= 0 and a step emits eos_id, that token is written and counted and
  * the loop stops.

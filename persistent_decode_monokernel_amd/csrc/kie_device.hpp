@@ -98,6 +98,25 @@ __device__ __forceinline__ bool poll64(const uint32_t* p, uint64_t& v, const Wat
   }
 }
 
+// Philox4x32-10 block function (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E.
+// Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds; each
+// multiplies counter words 0 and 2 by the two round constants and recombines
+// the 64-bit products' halves with words 1, 3 and the key, which advances by
+// the two Weyl constants before every round after the first.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
 // ---------------------------------------------------------------------------
 // Wave64 reductions on DPP (no LDS traffic).  dpp<CTRL, ROWMASK>(v) reads v
 // from the lane that CTRL selects; rows outside ROWMASK receive 0.

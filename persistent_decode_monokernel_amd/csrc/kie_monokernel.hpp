@@ -876,6 +876,327 @@ __device__ __forceinline__ void block_argmax(float& v, int& i, const Lds& s, int
   i = bi;
 }
 
+// ---- sampling (temperature, top-k, nucleus) --------------------------------
+//
+// Candidate order: larger logit first, lower index on ties.  In registers a
+// candidate is one 64-bit key whose unsigned order is that order: the logit's
+// bits made order-preserving (sign flipped for positives, all bits for
+// negatives; NaN taken as -inf) above the complemented index.  Every candidate
+// has its own index (vocabulary rows, or padding indices from kPadIdx up), so
+// keys are distinct and every step of the selection is a plain comparison.
+__device__ __forceinline__ uint64_t cand_key(float v, int i) {
+  const uint32_t u = __float_as_uint(v == v ? v : -INFINITY);
+  const uint32_t h = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)h << 32) | (uint32_t)~(uint32_t)i;
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t h = (uint32_t)(k >> 32);
+  return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+// Published lists alternate in direction so that merge trees always pair
+// opposite directions.  Work-group lists (merged in groups of 8 consecutive
+// ones): best-first for odd work-groups.  Group lists (wave w of work-group 0
+// merges groups w, w + 8, ...): best-first when bit 3 of the group is set.
+__device__ __forceinline__ bool wg_list_desc(int wg) { return wg & 1; }
+__device__ __forceinline__ bool group_list_desc(int g) { return (g >> 3) & 1; }
+
+// Padding candidates (logit -inf) get distinct indices from kPadIdx up: row
+// slots of work-group wg at (wg << 10) + slot, the gatherer's padding lists
+// and idle waves from kPadRest.
+constexpr int kPadRest = kPadIdx + (kMaxWG << 10);
+
+// x from lane (lane ^ S), S a power of two below 64: DPP within rows of 16
+// lanes, the gfx950 row / half-wave swaps above (their two results XOR the own
+// value out, whichever order they come in).
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (S == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, (int)x, 0x104, 0xF, 0xF, false);  // row_shl:4, lane + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4, lane - 4
+    return (uint32_t)((lane & 4) ? dn : up);
+  } else if constexpr (S == 8) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  } else if constexpr (S == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return p[0] ^ p[1] ^ x;
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return p[0] ^ p[1] ^ x;
+  }
+}
+
+// Compare-exchange with lane (lane ^ S): the lower lane of each pair keeps the
+// larger key in a best-first (desc) block, the smaller one otherwise.
+template <int S>
+__device__ __forceinline__ void cas_step(uint64_t& k, int lane, bool desc) {
+  const uint64_t p = ((uint64_t)lane_xor<S>((uint32_t)(k >> 32), lane) << 32) | lane_xor<S>((uint32_t)k, lane);
+  const bool keep_max = ((lane & S) == 0) == desc;
+  k = ((p > k) == keep_max) ? p : k;
+}
+
+// Lists of 64 keys (lane j = entry j) sorted in opposite directions: their
+// concatenation is bitonic, so the lane-wise larger key is the 64 best of the
+// union, itself bitonic; six compare-exchange steps at distances 32 .. 1 sort
+// it best-first (desc) or worst-first.
+__device__ __forceinline__ void merge_lists(uint64_t& a, uint64_t b, int lane, bool desc) {
+  a = b > a ? b : a;
+  cas_step<32>(a, lane, desc);
+  cas_step<16>(a, lane, desc);
+  cas_step<8>(a, lane, desc);
+  cas_step<4>(a, lane, desc);
+  cas_step<2>(a, lane, desc);
+  cas_step<1>(a, lane, desc);
+}
+
+// Sort 64 keys (lane j holds one) best-first (desc) or worst-first: a bitonic
+// network over blocks of 2, 4, ..., 64 lanes; below 64 the blocks alternate
+// direction so that neighbouring blocks form a bitonic block of the next size.
+template <int B>
+__device__ __forceinline__ void sort_stage(uint64_t& k, int lane, bool desc) {
+  const bool d = B == 64 ? desc : (desc != ((lane & B) != 0));
+  if constexpr (B >= 64) cas_step<32>(k, lane, d);
+  if constexpr (B >= 32) cas_step<16>(k, lane, d);
+  if constexpr (B >= 16) cas_step<8>(k, lane, d);
+  if constexpr (B >= 8) cas_step<4>(k, lane, d);
+  if constexpr (B >= 4) cas_step<2>(k, lane, d);
+  cas_step<1>(k, lane, d);
+}
+__device__ __forceinline__ void sort64(uint64_t& k, int lane, bool desc) {
+  sort_stage<2>(k, lane, desc);
+  sort_stage<4>(k, lane, desc);
+  sort_stage<8>(k, lane, desc);
+  sort_stage<16>(k, lane, desc);
+  sort_stage<32>(k, lane, desc);
+  sort_stage<64>(k, lane, desc);
+}
+
+// Pairwise merge tree over N lists in registers (N a power of two; list k is
+// worst-first for even k, best-first for odd k).  Pair m of every round is
+// written worst-first for even m, best-first for odd m; the last merge gives
+// direction `last_desc`.  The merges of a round are independent and overlap.
+template <int N>
+__device__ __forceinline__ void merge_tree(uint64_t (&k)[N], int lane, bool last_desc) {
+#pragma unroll
+  for (int span = 1; span < N; span *= 2) {
+#pragma unroll
+    for (int a = 0; a < N; a += 2 * span)
+      merge_lists(k[a], k[a + span], lane, 2 * span == N ? last_desc : ((a / (2 * span)) & 1) != 0);
+  }
+}
+
+// Padding list in direction `desc`: indices base + rank, rank = lane (best
+// first) or 63 - lane.
+__device__ __forceinline__ uint64_t pad_list(int base, int lane, bool desc) {
+  return cand_key(-INFINITY, base + (desc ? lane : kCand - 1 - lane));
+}
+
+// This work-group's 64 best rows (n <= 1024 logits in yv): wave w sorts rows
+// 64w + lane (and 512 + 64w + lane); the waves' lists meet in a merge tree in
+// wave 0 (over the smallest power of two of waves that holds every row),
+// which publishes the list, direction wg_list_desc(wg), as (logit, index) pairs.
+// Ranks past the row count are padding.
+__device__ __forceinline__ void publish_candidates(const float* yv, int n, int v0, uint32_t* dst, int wg, int t,
+                                                   float* lds) {
+  const int lane = t & 63, wv = t >> 6;
+  auto key = [&](int r) { return r < n ? cand_key(yv[r], v0 + r) : cand_key(-INFINITY, kPadIdx + (wg << 10) + r); };
+  const int used = n > 512 ? kWaves : n > 256 ? 8 : n > 128 ? 4 : n > 64 ? 2 : 1;  // lists in the tree
+  uint64_t* lk = reinterpret_cast<uint64_t*>(lds);
+  if (wv < used) {
+    uint64_t k = key(64 * wv + lane);
+    sort64(k, lane, (wv & 1) != 0);
+    if (n > 512) {
+      uint64_t k2 = key(512 + 64 * wv + lane);
+      sort64(k2, lane, (wv & 1) == 0);
+      merge_lists(k, k2, lane, (wv & 1) != 0);
+    }
+    lk[wv * kCand + lane] = k;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    uint64_t k;
+    if (used == 1) {  // wave 0 sorted worst-first: a best-first list takes its entries in reverse
+      k = lk[wg_list_desc(wg) ? kCand - 1 - lane : lane];
+    } else if (used == 2) {
+      uint64_t kk[2] = {lk[lane], lk[kCand + lane]};
+      merge_tree<2>(kk, lane, wg_list_desc(wg));
+      k = kk[0];
+    } else if (used == 4) {
+      uint64_t kk[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) kk[w] = lk[w * kCand + lane];
+      merge_tree<4>(kk, lane, wg_list_desc(wg));
+      k = kk[0];
+    } else {
+      uint64_t kk[kWaves];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) kk[w] = lk[w * kCand + lane];
+      merge_tree<kWaves>(kk, lane, wg_list_desc(wg));
+      k = kk[0];
+    }
+    xst64(dst + 2 * lane, pack2f(key_value(k), __int_as_float(key_index(k))));
+  }
+  __syncthreads();
+}
+
+// Poll-load entry `lane` of list `l` of an exchange array of lists and make it
+// a key; false (for the whole wave) when a poll gave up.
+__device__ __forceinline__ bool load_list(const uint32_t* src, int l, int lane, uint64_t& k, const Watch& w) {
+  const uint32_t* p = src + ((size_t)l * kCand + lane) * 2;
+  uint64_t e = xld64(p);
+  const bool got = Ready32x2{}(e) || poll64(p, e, w, Ready32x2{});
+  k = cand_key(lo_f(e), __float_as_int(hi_f(e)));
+  return __all(got);
+}
+
+// Work-group g < ceil(grid / 8): merge the lists of work-groups 8g .. 8g+7
+// (wave w loads one; missing ones are padding) in a tree in wave 0 and
+// publish the group's 64 best, direction group_list_desc(g).
+__device__ KIE_INLINE bool group_merge(const Params* Pp, char* smem, uint32_t* X) {
+  const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  const int lane = c.t & 63, wv = c.t >> 6, g = c.wg, l = 8 * g + wv;
+  uint64_t k = pad_list(kPadRest + l * kCand, lane, wg_list_desc(l));
+  bool ok = l >= c.nb || load_list(X + P.xl.cand, l, lane, k, c.w);
+  if (any_failed(!ok)) return false;
+  uint64_t* lk = reinterpret_cast<uint64_t*>(c.s.red);  // red/yv are idle after the LM head
+  lk[wv * kCand + lane] = k;
+  __syncthreads();
+  if (wv == 0) {
+    uint64_t k8[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) k8[w] = lk[w * kCand + lane];
+    merge_tree<kWaves>(k8, lane, group_list_desc(g));
+    xst64(X + P.xl.cand2 + ((size_t)g * kCand + lane) * 2, pack2f(key_value(k8[0]), __int_as_float(key_index(k8[0]))));
+  }
+  __syncthreads();
+  return true;
+}
+
+// Work-group 0: gather the group lists and reduce them to the global 64 best,
+// then wave 0 draws.  Wave w loads groups w, w + 8, ... (all in flight) and
+// merges them in a register tree; the eight waves' lists meet in a second tree
+// in wave 0.  Draw: weights exp2((z - z0) * log2(e) / T) over the first
+// samp_k, inclusive prefix sums S across lanes, nucleus n = 1 + #{S_j < top_p *
+// S_{k-1}}, u from Philox4x32-10 (counter (pos, 0, 0, 0)), token = entry
+// #{j < n : S_j <= u S_{n-1}}.
+constexpr int kGroupsPerWave = kMaxWG / 8 / kWaves;  // 16 group lists per wave at most
+__device__ KIE_INLINE bool gather_sample(const Params* Pp, char* smem, uint32_t* X, int pos, int& tok,
+                                          uint64_t* tr) {
+  const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  const int slot = P.L * kStagesPerLayer + 2;
+  stamp(tr, slot, 0, c.t);
+  const int lane = c.t & 63, wv = c.t >> 6, ng = (c.nb + 7) / 8;
+  const uint32_t* src = X + P.xl.cand2;
+  uint64_t kk[kGroupsPerWave];
+  uint64_t e[kGroupsPerWave];
+#pragma unroll
+  for (int k = 0; k < kGroupsPerWave; ++k) {  // issue every load first
+    const int g = wv + 8 * k;
+    e[k] = g < ng ? xld64(src + ((size_t)g * kCand + lane) * 2) : 0ull;
+  }
+  bool ok = true;
+#pragma unroll
+  for (int k = 0; k < kGroupsPerWave; ++k) {
+    const int g = wv + 8 * k;
+    if (g < ng) {
+      if (ok) {
+        const bool got = Ready32x2{}(e[k]) || poll64(src + ((size_t)g * kCand + lane) * 2, e[k], c.w, Ready32x2{});
+        ok = __all(got);
+      }
+      kk[k] = cand_key(lo_f(e[k]), __float_as_int(hi_f(e[k])));
+    } else {  // padding list in the direction group g would have had
+      kk[k] = pad_list(kPadRest + (kMaxWG + g) * kCand, lane, group_list_desc(g));
+    }
+  }
+  if (any_failed(!ok)) return false;
+  uint64_t run;
+  if (ng <= 8) {
+    run = kk[0];
+  } else if (ng <= 16) {
+    uint64_t k2[2] = {kk[0], kk[1]};
+    merge_tree<2>(k2, lane, (wv & 1) != 0);
+    run = k2[0];
+  } else if (ng <= 32) {
+    uint64_t k4[4] = {kk[0], kk[1], kk[2], kk[3]};
+    merge_tree<4>(k4, lane, (wv & 1) != 0);
+    run = k4[0];
+  } else {
+    merge_tree<kGroupsPerWave>(kk, lane, (wv & 1) != 0);
+    run = kk[0];
+  }
+  if (ng <= 8 && (wv & 1) != group_list_desc(wv))  // one group per wave: already in the list's direction
+    run = __shfl(run, kCand - 1 - lane);
+  stamp(tr, slot, 1, c.t);
+  uint64_t* lk = reinterpret_cast<uint64_t*>(c.s.red);  // the waves' lists (red/yv are idle after the LM head)
+  lk[wv * kCand + lane] = run;
+  __syncthreads();
+  if (wv == 0) {
+    uint64_t k8[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) k8[w] = lk[w * kCand + lane];
+    merge_tree<kWaves>(k8, lane, true);
+    const float v = key_value(k8[0]);
+    const int i = key_index(k8[0]);
+    const int K = P.samp_k;
+    const float z0 = __shfl(v, 0);
+    float S = lane < K ? __builtin_amdgcn_exp2f((v - z0) * P.samp_scale) : 0.f;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const float o = __shfl_up(S, s);
+      if (lane >= s) S += o;
+    }
+    const float total = __shfl(S, K - 1);
+    const int n = 1 + (int)__popcll(__ballot(lane < K && S < P.samp_top_p * total));
+    const float Sn = __shfl(S, n - 1);
+    const uint4 x = philox4x32_10(make_uint4((uint32_t)pos, 0u, 0u, 0u), P.samp_key0, P.samp_key1);
+    const float r = (float)(x.x >> 8) * 0x1p-24f * Sn;
+    int j = (int)__popcll(__ballot(lane < n && S <= r));
+    j = j < n ? j : n - 1;
+    const int tk = __shfl(i, j);
+    if (lane == 0) c.s.imisc[0] = tk;
+  }
+  __syncthreads();
+  stamp(tr, slot, 2, c.t);
+  const int tk = c.s.imisc[0];
+  __syncthreads();
+  tok = (tk >= 0 && tk < P.V) ? tk : 0;
+  stamp(tr, slot, 3, c.t);
+  return true;
+}
+
+// The sampled token: work-groups 0 .. ceil(grid/8)-1 merge groups of lists,
+// work-group 0 draws the token and publishes it, the others poll it.
+__device__ KIE_INLINE bool sampled_token(const Params* Pp, char* smem, uint32_t* X, int pos, int& tok, uint64_t* tr) {
+  if ((int)blockIdx.x < ((int)gridDim.x + 7) / 8 && !group_merge(Pp, smem, X)) return false;
+  if (blockIdx.x == 0) {
+    if (!gather_sample(Pp, smem, X, pos, tok, tr)) return false;
+    if (threadIdx.x == 0) xst64(X + cparams(Pp).xl.stok, pack2f(__int_as_float(tok), 0.f));
+    return true;
+  }
+  const Sc c = stage_ctx(Pp, smem);
+  const int slot = c.P.L * kStagesPerLayer + 2;
+  stamp(tr, slot, 0, c.t);
+  bool ok = true;
+  if (c.t == 0) {
+    uint64_t v = 0;
+    ok = poll64(X + c.P.xl.stok, v, c.w, Ready32x2{});
+    c.s.imisc[0] = __float_as_int(lo_f(v));
+  }
+  if (any_failed(!ok)) return false;
+  const int tk = c.s.imisc[0];
+  __syncthreads();
+  tok = (tk >= 0 && tk < c.P.V) ? tk : 0;
+  stamp(tr, slot, 3, c.t);
+  return true;
+}
+
 // LM head on this work-group's vocabulary rows; logits optionally written.
 // The host guarantees ceil(V / grid) rows fit the LDS partial-sum buffers.
 template <int DT, int VD>
@@ -905,6 +1226,8 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
       bi = v0 + r;
     }
   }
+  if (P.samp_k > 0)
+    publish_candidates(c.s.yv, v1 - v0, v0, X + P.xl.cand + (size_t)c.wg * kCand * 2, c.wg, c.t, c.s.red);
   block_argmax(bv, bi, c.s, c.t);
   best_v = bv;
   best_i = bi;
@@ -1008,9 +1331,11 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     if (!ok) break;
     float bv = 0.f;
     int bi = 0;
+    bool lm = false;
     {
       CParams& Q = cparams(Pp);
-      if (!Q.lm_last_only || s == Q.n_steps - 1) {
+      lm = !Q.lm_last_only || s == Q.n_steps - 1;
+      if (lm) {
         float* lg = Q.logits ? Q.logits + (size_t)(Q.lm_last_only ? 0 : s) * Q.V : nullptr;
         if (!st_lmhead<DT, VD>(Pp, smem, X, lg, bv, bi, tr, ring)) {
           ok = false;
@@ -1030,6 +1355,10 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       reset_set(Pp, smem, Pp->xch + (size_t)((s + 2) % kRingSets) * Pp->xl.words, nch, kThreads / 2, tr);
     }
     if (!gather_token(Pp, smem, X, tok, tr)) {
+      ok = false;
+      break;
+    }
+    if (lm && cparams(Pp).samp_k > 0 && !sampled_token(Pp, smem, X, pos, tok, tr)) {
       ok = false;
       break;
     }

@@ -15,6 +15,8 @@ constexpr int kRedCap = 8192;            // LDS floats for per-wave GEMV partial
 constexpr int kYCap = 1024;              // LDS floats for finished GEMV rows
 constexpr int kDepth = 8;               // weight vectors in flight per thread
 constexpr uint32_t kSent = 0xFFFFFFFFu;  // NaN pattern that marks "not written yet"
+constexpr int kCand = 64;                // sampling: candidates per work-group list and in the global list
+constexpr int kPadIdx = 0x40000000;      // sampling: indices of padding candidates (logit -inf) start here
 constexpr int kStagesPerLayer = 6;       // qkv, attn, merge, wo, gate/up, down
 constexpr int kTraceStamps = 4;          // per (slot, work-group): entry, input, compute done, exit
 
@@ -34,6 +36,9 @@ struct XchLayout {
   uint64_t a;      // [L][Hq*hd]    merged attention output
   uint64_t h;      // [L][F]        silu(gate) * up
   uint64_t arg;    // [kMaxWG][2]   per-work-group (max logit, index)
+  uint64_t cand;   // [kMaxWG][kCand][2] per-work-group sampling candidates (logit, index), sorted
+  uint64_t cand2;  // [kMaxWG / 8][kCand][2] the same, merged over groups of 8 work-groups
+  uint64_t stok;   // [2]           sampled token (work-group 0 draws it)
   uint64_t att;    // [L][Hq][cmax][astride]  split-KV partials (m, l, pad, pad, o[hd])
   uint64_t dense;  // words before att (reset wholesale)
   uint64_t words;  // total words of one set
@@ -61,6 +66,11 @@ struct Params {
   const int* forced;          // prompt tokens (prefill) or null
   // launch
   int pos0, n_steps, eos_id, in_tok, abort_after, lm_last_only, withhold_wg;
+  // sampling: samp_k = 0 greedy; else top-k (<= kCand), log2(e) / temperature,
+  // nucleus mass, Philox4x32-10 key
+  int samp_k;
+  float samp_scale, samp_top_p;
+  uint32_t samp_key0, samp_key1;
   // per-token timeline: step `trace_step` of the launch is stamped into
   // trace[((slot) * grid + wg) * kTraceStamps + k], slot = layer *
   // kStagesPerLayer + stage (then kStagesPerLayer*L + {0: LM head, 1: step

@@ -68,6 +68,9 @@ XchLayout xch_layout(const kie_config& c) {
   x.a = take(L * qd);
   x.h = take(L * F);
   x.arg = take(2 * (uint64_t)kMaxWG);
+  x.cand = take(2ull * kMaxWG * kCand);
+  x.cand2 = take(2ull * (kMaxWG / 8) * kCand);
+  x.stok = take(2);
   x.dense = o;
   x.att = take(L * c.n_heads * (uint64_t)attn_cmax(c) * (c.head_dim + 4));
   x.words = align_up(o, 64);
@@ -198,6 +201,9 @@ struct kie_engine {
   std::vector<const uint16_t*> wtab;  // host copy of the per-layer weight table
   int prefill_mode = KIE_PREFILL_AUTO;
   int prefill_chunk = 0;  // positions per matrix-core chunk; 0 = the workspace's (lay.pf_chunk)
+  int samp_k = 0;         // sampling (kie_set_sampling); 0 = greedy
+  float samp_scale = 0.f, samp_top_p = 1.f;
+  uint64_t samp_seed = 0;
 };
 
 extern "C" const char* kie_status_string(kie_status s) {
@@ -394,6 +400,11 @@ static Params base_params(const kie_engine* e) {
   P.trace_step = e->trace_step;
   P.lds_xres = e->lds.xres; P.lds_xn = e->lds.xn; P.lds_scr = e->lds.scr; P.lds_misc = e->lds.misc;
   P.lds_bytes = e->lds.bytes;
+  P.samp_k = e->samp_k;
+  P.samp_scale = e->samp_scale;
+  P.samp_top_p = e->samp_top_p;
+  P.samp_key0 = (uint32_t)e->samp_seed;
+  P.samp_key1 = (uint32_t)(e->samp_seed >> 32);
   return P;
 }
 
@@ -490,6 +501,23 @@ extern "C" kie_status kie_set_prefill_chunk(kie_engine* e, int32_t positions) {
   if (!e || positions < 0) return KIE_ERR_ARG;
   if (positions > e->lay.pf_chunk) return KIE_ERR_CAPACITY;
   e->prefill_chunk = positions;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_sampling(kie_engine* e, float temperature, int32_t top_k, float top_p,
+                                       uint64_t seed) {
+  if (!e || std::isnan(temperature)) return KIE_ERR_ARG;
+  if (temperature <= 0.f) {
+    e->samp_k = 0;
+    return KIE_OK;
+  }
+  if (top_k < 1 || top_k > kCand || top_k > e->cfg.vocab || !(top_p > 0.f && top_p <= 1.f) ||
+      !std::isfinite(1.0f / temperature))
+    return KIE_ERR_ARG;
+  e->samp_k = top_k;
+  e->samp_scale = 1.4426950408889634f / temperature;
+  e->samp_top_p = top_p;
+  e->samp_seed = seed;
   return KIE_OK;
 }
 
@@ -648,7 +676,7 @@ extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t co
 
 extern "C" size_t kie_trace_words(const kie_engine* e) {
   if (!e) return 0;
-  return (size_t)(e->cfg.n_layers * kStagesPerLayer + 2) * e->grid * kTraceStamps;
+  return (size_t)(e->cfg.n_layers * kStagesPerLayer + 3) * e->grid * kTraceStamps;
 }
 
 extern "C" kie_status kie_set_trace(kie_engine* e, uint64_t* trace_dev, int32_t step) {

@@ -70,6 +70,8 @@ SIGNATURES = {
     "kie_config_validate": (ctypes.c_int, [ctypes.POINTER(kie_config)]),
     "kie_set_prefill_mode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_prefill_chunk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_sampling": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_float,
+                                        ctypes.c_uint64]),
     "kie_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kie_config)]),
     "kie_create": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                   ctypes.POINTER(ctypes.c_void_p)]),
@@ -266,6 +268,12 @@ class Engine:
     def set_prefill_mode(self, mode: int):
         """KIE_PREFILL_AUTO (matrix-core prompt path where supported) or KIE_PREFILL_DECODE_LOOP."""
         _check(lib().kie_set_prefill_mode(self._h, int(mode)), "kie_set_prefill_mode")
+
+    def set_sampling(self, temperature: float, top_k: int = 64, top_p: float = 1.0, seed: int = 0):
+        """Token choice: greedy for temperature <= 0, else temperature / top-k (<= 64) /
+        nucleus sampling with Philox4x32-10 uniforms keyed by seed and position."""
+        _check(lib().kie_set_sampling(self._h, float(temperature), int(top_k), float(top_p),
+                                      int(seed) & (2**64 - 1)), "kie_set_sampling")
 
     def set_prefill_chunk(self, positions: int):
         """Prompt positions per matrix-core chunk (0 = as many as the workspace holds)."""

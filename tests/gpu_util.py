@@ -41,3 +41,35 @@ def check_tokens_and_logits(gpu_tokens, gpu_logits, ora_logits, what=""):
     bad = (ora_tok != gt) & decisive
     assert not bad.any(), f"{what}: token mismatch at rows {torch.nonzero(bad).flatten().tolist()[:10]}"
     return err, int(decisive.sum())
+
+
+def check_logits(gpu_logits, ora_logits, what=""):
+    """max |logit_gpu - logit_oracle| <= LOGIT_TOL over all rows and vocabulary entries."""
+    g = gpu_logits.detach().to("cpu", torch.float64)
+    o = ora_logits.detach().to("cpu", torch.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    err = (g - o).abs().max().item()
+    assert math.isfinite(err) and err <= LOGIT_TOL, f"{what}: max |dlogit| = {err:.3e} > {LOGIT_TOL}"
+    return err
+
+
+DRAW_MARGIN = 1e-4   # sampled decisions closer than this (relative mass) to a boundary may differ
+
+
+def check_sampled(gpu_tokens, gpu_logits, positions, temperature, top_k, top_p, seed, what=""):
+    """Each sampled token equals the oracle sampler's choice on the GPU's own fp32 logits
+    and the same Philox uniform, except where the decision lies within DRAW_MARGIN of a
+    boundary of the cumulative weights (fp32 on the device, float64 in the oracle).
+    Returns (agreeing, borderline)."""
+    g = gpu_logits.detach().to("cpu", torch.float32)
+    agree = border = 0
+    for row, (tok, pos) in enumerate(zip(gpu_tokens, positions)):
+        u = oracle.sampling.uniform_for_position(seed, pos)
+        ref, m = oracle.sampling.sample_detail(g[row], temperature, top_k, top_p, u)
+        if ref == tok:
+            agree += 1
+            continue
+        assert m is not None and min(m["draw"], m["nucleus"]) < DRAW_MARGIN, \
+            f"{what}: row {row} (pos {pos}) token {tok} != oracle {ref}, margins {m}"
+        border += 1
+    return agree, border

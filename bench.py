@@ -74,11 +74,14 @@ KERNEL_SRC_DIR = os.path.join(ROOT, "persistent_decode_monokernel_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources the decode kernel and its launch code are built from
+    (the prompt-path kernels excluded): stored counter readings count only
+    while it matches."""
     import hashlib
 
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SRC_DIR)):
-        if name.endswith((".hip", ".hpp", ".h")):
+        if name.endswith((".hip", ".hpp", ".h")) and not name.startswith("kie_prefill"):
             h.update(name.encode())
             with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
                 h.update(f.read())

@@ -211,6 +211,43 @@ def ttft_bench(name: str, modes=("auto", "decode_loop"), chunks=(0,)):
         eng.close()
 
 
+def grid_sweep(name: str, grids, steps=None):
+    """Decode tokens/s and roofline fraction of the workload's timed launch on a
+    subset of the compute units (kie_set_grid), one line per grid size."""
+    import torch
+
+    from persistent_decode_monokernel_amd import kie, synth
+
+    wl = synth.WORKLOADS[name]
+    s = wl.shape
+    K = steps or wl.n_decode
+    P = wl.n_prompt
+    w = synth.make_weights(s, wl.weight_seed, device="cuda")
+    prompt = synth.make_prompt(s, P, wl.prompt_seed).tolist()
+    for g in grids:
+        eng = kie.Engine(s, max_seq=P + K)
+        eng.load_weights(w)
+        try:
+            eng.set_grid(g)
+        except kie.KieError as e:
+            print(json.dumps({"workload": name, "grid": g, "error": str(e)}), flush=True)
+            eng.close()
+            continue
+        eng.prefill(prompt)
+        eng.decode(16)
+        eng.prefill(prompt)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        toks, _, st = eng.decode(K)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = eng.info().last_kernel_ms
+        gbs = bytes_per_launch(s, P, len(toks)) / (ms / 1e3) / 1e9
+        print(json.dumps({"workload": name, "grid": eng.info().grid, "tokens_per_s": len(toks) / wall,
+                          "kernel_ms": ms, "GBps": gbs, "frac": gbs / HBM_PEAK_GBS, "status": st}), flush=True)
+        eng.close()
+
+
 STAGES = ("qkv", "attention", "merge", "wo", "gate/up", "down")
 
 
@@ -335,6 +372,8 @@ def main():
                     help="with --ttft: matrix-core chunk sizes to time (0 = default)")
     ap.add_argument("--ttft-modes", nargs="+", default=["auto", "decode_loop"], choices=["auto", "decode_loop"],
                     help="with --ttft: prefill modes to time")
+    ap.add_argument("--grid-sweep", type=int, nargs="+", default=None, metavar="G",
+                    help="only time the workload's decode launch on G work-groups (0 = one per CU), per G")
     ap.add_argument("--sampling", type=float, nargs=3, default=None, metavar=("T", "TOP_K", "TOP_P"),
                     help="decode with on-device temperature / top-k / nucleus sampling instead of greedy")
     ap.add_argument("--timeline", type=int, default=None, metavar="STEP",
@@ -356,6 +395,9 @@ def main():
         return
     if args.gemv:
         gemv_probe_bench()
+        return
+    if args.grid_sweep:
+        grid_sweep(args.workload, args.grid_sweep, args.steps)
         return
     if args.ttft:
         ttft_bench(args.workload, tuple(args.ttft_modes), tuple(args.pf_chunk))

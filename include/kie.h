@@ -165,6 +165,15 @@ kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prom
 typedef enum { KIE_PREFILL_AUTO = 0, KIE_PREFILL_DECODE_LOOP = 1 } kie_prefill_mode;
 kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode);
 
+/* Work-groups of the persistent kernel: 0 (default) = one per compute unit;
+ * 1 <= grid <= compute units runs on a subset (the pages' kernel deliberately
+ * uses 256 of MI300X's 304 CUs: revietech.ru page, section "Arkhitektura i
+ * osobennosti").  KIE_ERR_ARG above the compute-unit count,
+ * KIE_ERR_UNSUPPORTED when a stage's rows per work-group would not fit LDS.
+ * Results do not depend on the grid beyond rounding order.  Takes effect at
+ * the next kie_prefill / kie_decode. */
+kie_status kie_set_grid(kie_engine* e, int32_t grid);
+
 /* Prompt positions per matrix-core chunk in KIE_PREFILL_AUTO (each chunk runs
  * every layer before the next starts).  The workspace holds the activations of
  * min(max_seq, 4096) positions; 0 (default) uses all of them, a smaller value

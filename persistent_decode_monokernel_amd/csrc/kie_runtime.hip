@@ -262,6 +262,23 @@ static kie_status hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);      \
   } while (0)
 
+// Can `grid` work-groups run the shape: every GEMV stage's rows per
+// work-group fit the LDS partial sums, the step tail's gather covers the grid,
+// and the index arithmetic stays within 32 bits.
+static bool grid_fits(const kie_config& c, const Layout& lay, int grid) {
+  if (grid < 1 || grid > kMaxWG || grid > kThreads / 2) return false;
+  auto fits = [&](long long rows, int K) {
+    const int vpr = K / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
+    return rows <= kYCap && rows * nwr <= kRedCap;
+  };
+  auto per = [&](long long n) { return (n + grid - 1) / grid; };
+  const long long qkv = (long long)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  return fits(per(qkv), c.d_model) && fits(per(c.d_model), c.n_heads * c.head_dim) &&
+         fits(2 * per(c.d_ffn), c.d_model) && fits(per(c.d_model), c.d_ffn) && fits(per(c.vocab), c.d_model) &&
+         (uint64_t)c.vocab * grid < (1ull << 32) && (lay.xl.dense / 2) * grid < (1ull << 32) &&
+         (uint64_t)c.d_ffn * grid < (1ull << 32);
+}
+
 extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes, void* hip_stream,
                                  kie_engine** out) {
   if (!out) return KIE_ERR_ARG;
@@ -300,22 +317,9 @@ extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, siz
   }
   // One resident work-group per compute unit.
   e->grid = e->cu_count < kMaxWG ? e->cu_count : kMaxWG;
-  // every GEMV stage's rows per work-group must fit the LDS partial sums
-  {
-    const kie_config& c = *cfg;
-    auto fits = [&](long long rows, int K) {
-      const int vpr = K / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
-      return rows <= kYCap && rows * nwr <= kRedCap;
-    };
-    auto per = [&](long long n) { return (n + e->grid - 1) / e->grid; };
-    const long long qkv = (long long)(c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
-    if (!fits(per(qkv), c.d_model) || !fits(per(c.d_model), c.n_heads * c.head_dim) ||
-        !fits(2 * per(c.d_ffn), c.d_model) || !fits(per(c.d_model), c.d_ffn) || !fits(per(c.vocab), c.d_model) ||
-        e->grid > kThreads / 2 || (uint64_t)c.vocab * e->grid >= (1ull << 32) ||
-        (lay.xl.dense / 2) * e->grid >= (1ull << 32) || (uint64_t)c.d_ffn * e->grid >= (1ull << 32)) {
-      delete e;
-      return KIE_ERR_UNSUPPORTED;
-    }
+  if (!grid_fits(*cfg, lay, e->grid)) {
+    delete e;
+    return KIE_ERR_UNSUPPORTED;
   }
 
   // Rotary table, built in double precision: angle(p, i) = p * base^(-2i/hd).
@@ -494,6 +498,16 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
 extern "C" kie_status kie_set_prefill_mode(kie_engine* e, int32_t mode) {
   if (!e || (mode != KIE_PREFILL_AUTO && mode != KIE_PREFILL_DECODE_LOOP)) return KIE_ERR_ARG;
   e->prefill_mode = mode;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_grid(kie_engine* e, int32_t grid) {
+  if (!e || grid < 0) return KIE_ERR_ARG;
+  const int full = e->cu_count < kMaxWG ? e->cu_count : kMaxWG;
+  if (grid == 0) grid = full;
+  if (grid > full) return KIE_ERR_ARG;
+  if (!grid_fits(e->cfg, e->lay, grid) || kie_check_tiling(&e->cfg, grid, 0) != KIE_OK) return KIE_ERR_UNSUPPORTED;
+  e->grid = grid;
   return KIE_OK;
 }
 

@@ -70,6 +70,7 @@ SIGNATURES = {
     "kie_config_validate": (ctypes.c_int, [ctypes.POINTER(kie_config)]),
     "kie_set_prefill_mode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_prefill_chunk": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_grid": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_sampling": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_float,
                                         ctypes.c_uint64]),
     "kie_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kie_config)]),
@@ -274,6 +275,10 @@ class Engine:
         nucleus sampling with Philox4x32-10 uniforms keyed by seed and position."""
         _check(lib().kie_set_sampling(self._h, float(temperature), int(top_k), float(top_p),
                                       int(seed) & (2**64 - 1)), "kie_set_sampling")
+
+    def set_grid(self, grid: int):
+        """Work-groups of the persistent kernel (0 = one per compute unit)."""
+        _check(lib().kie_set_grid(self._h, int(grid)), "kie_set_grid")
 
     def set_prefill_chunk(self, positions: int):
         """Prompt positions per matrix-core chunk (0 = as many as the workspace holds)."""

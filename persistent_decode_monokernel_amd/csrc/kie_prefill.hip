@@ -6,25 +6,34 @@
 // The prompt is processed in chunks of up to kPfChunk positions, layer by
 // layer, with one launch per operation on the engine's stream:
 //   X = E[tokens]                                   (fp32 residual, [M][d])
-//   per layer:  Xn = RMSNorm(X) * g_attn            (16-bit, [M][d])
+//   per layer:  Xn = RMSNorm(X) * g_attn            (activation, [M][d])
 //               QKV = Xn Wq^T | Xn Wk^T | Xn Wv^T   (fp32, [M][qd + 2 kvd])
 //               rotary embedding of q (in place, fp32) and k; k, v appended
 //               to the KV cache
 //               A = causal attention of q over the cache rows 0 .. p0+m
 //               X += A Wo^T
 //               Xn = RMSNorm(X) * g_ffn
-//               H = silu(Xn Wg^T) * (Xn Wu^T)       (16-bit, [M][F])
+//               H = silu(Xn Wg^T) * (Xn Wu^T)       (activation, [M][F])
 //               X += H Wd^T
 // The last prompt position then runs through the persistent decode kernel as
 // one forced step, which appends its KV row and yields the LM-head logits and
-// the first greedy token (kie_prefill in kie_runtime.hip).
+// the first token (kie_prefill in kie_runtime.hip).
 //
-// Matrix-core layout (v_mfma_f32_32x32x16_f16, checked on the device): lane l
-// holds A[m = l%32][k = 8*(l/32) + 0..7] and B[k = 8*(l/32) + 0..7][n = l%32];
-// accumulator element 4i+j is C[m = 8i + 4*(l/32) + j][n = l%32].
+// Activations: fp16 models store them as fp16, the matrix cores' input.  bf16
+// models store them as fp32 and the GEMMs split each value into three bf16
+// terms (b0 = bf16(x), b1 = bf16(x - b0), b2 = bf16(x - b0 - b1)), one product
+// per term against the exact bf16 weights: fp32-accurate activations, as the
+// decode path's bf16 GEMVs take them.  Attention splits the scaled queries
+// and the softmax probabilities into two bf16 terms likewise.
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_{f16,bf16}, checked on the device):
+// lane l holds A[m = l%32][k = 8*(l/32) + 0..7] and B[k = 8*(l/32) + 0..7][n =
+// l%32]; accumulator element 4i+j is C[m = 8i + 4*(l/32) + j][n = l%32].
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "kie.h"
 #include "kie_params.hpp"
@@ -34,26 +43,76 @@ namespace kie {
 namespace {
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f16x_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }  // nearest even
 
-__device__ __forceinline__ h8_t ld8(const uint16_t* p) {
-  return __builtin_bit_cast(h8_t, *reinterpret_cast<const uint4*>(p));
+// 16-bit storage format of the engine dtype
+template <int DT>
+__device__ __forceinline__ float to_f(uint16_t u) {
+  return DT == KIE_BF16 ? bf2f(u) : h2f(u);
+}
+template <int DT>
+__device__ __forceinline__ uint16_t from_f(float f) {
+  return DT == KIE_BF16 ? f2bf(f) : f2h(f);
+}
+
+// Activation element between the prompt-path kernels: fp16 (fp16 models) or
+// fp32 (bf16 models, split into bf16 terms where a GEMM stages it).
+template <int DT>
+using act_t = typename std::conditional<DT == KIE_BF16, float, uint16_t>::type;
+template <int DT>
+constexpr int kTerms = DT == KIE_BF16 ? 3 : 1;  // A-operand terms per GEMM product
+template <int DT>
+__device__ __forceinline__ act_t<DT> to_act(float v) {
+  if constexpr (DT == KIE_BF16)
+    return v;
+  else
+    return f2h(v);
+}
+
+// One 32x32x16 matrix-core product in the engine dtype; operands are 8 16-bit
+// values per lane.
+template <int DT>
+__device__ __forceinline__ f16x_t mma(uint4 a, uint4 b, f16x_t c) {
+  if constexpr (DT == KIE_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8_t, a), __builtin_bit_cast(b8_t, b), c, 0,
+                                                    0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), c, 0,
+                                                   0, 0);
+}
+
+// x -> bf16 terms: term t of the split b0 = bf16(x), b1 = bf16(x - b0), ...
+// packed two per word (element 2e in the low half).
+template <int T>
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t (&w)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const uint16_t b0 = f2bf(x0), b1 = f2bf(x1);
+    w[t] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+    x0 -= bf2f(b0);
+    x1 -= bf2f(b1);
+  }
 }
 
 // ---- embedding and RMSNorm -------------------------------------------------
 
+template <int DT>
 __global__ __launch_bounds__(256) void pf_embed(const uint16_t* E, const int* tok, int M, int d, float* X) {
   const int m = blockIdx.x;
   if (m >= M) return;
   const uint16_t* row = E + (size_t)tok[m] * d;
-  for (int i = threadIdx.x; i < d; i += 256) X[(size_t)m * d + i] = h2f(row[i]);
+  for (int i = threadIdx.x; i < d; i += 256) X[(size_t)m * d + i] = to_f<DT>(row[i]);
 }
 
+template <int DT>
 __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t* g, float eps, int M, int d,
-                                                  uint16_t* Xn) {
+                                                  act_t<DT>* Xn) {
   __shared__ float part[4];
   const int m = blockIdx.x;
   if (m >= M) return;
@@ -64,7 +123,7 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += 256) Xn[(size_t)m * d + i] = f2h(x[i] * r * h2f(g[i]));
+  for (int i = threadIdx.x; i < d; i += 256) Xn[(size_t)m * d + i] = to_act<DT>(x[i] * r * to_f<DT>(g[i]));
 }
 
 // ---- GEMM: C[M][N] = A[M][K] W[N][K]^T on the matrix cores --------------------
@@ -76,6 +135,8 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t
 // Wave (wm, wn) computes rows 64wm .. and columns 64wn .. as 2 x 2
 // accumulators of 32 x 32.  Both operands are k-contiguous in memory and in
 // LDS, so every lane reads its 8 consecutive k values with one 16-byte load.
+// bf16: A arrives in fp32 and is split into kTerms bf16 planes while staged;
+// each product runs once per plane, the smallest first.
 //   EPI_STORE / EPI_ADD: W is up to three matrices stacked along N (the
 //   column tile picks one; segment widths are multiples of 128).
 //   EPI_SWIGLU: a work-group tile covers 64 output columns; its B rows are 64
@@ -92,10 +153,30 @@ struct GemmB {
   int end[3];            // cumulative row counts
 };
 
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int K, GemmB wb, float* C, int ldc,
-                                                  uint16_t* H, int ldh) {
-  __shared__ __align__(16) uint16_t lds[2][2 * kTile];
+// Write one staged A piece (8 elements: v0, and v1 for fp32) to LDS: fp16 as
+// is; fp32 as kTerms bf16 planes of kTile halves each.
+template <int DT>
+__device__ __forceinline__ void stage_a(uint4 v0, uint4 v1, uint16_t* dst) {
+  if constexpr (DT == KIE_BF16) {
+    const float x[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z), __uint_as_float(v0.w),
+                        __uint_as_float(v1.x), __uint_as_float(v1.y), __uint_as_float(v1.z), __uint_as_float(v1.w)};
+    uint32_t w[4][kTerms<DT>];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_pair<kTerms<DT>>(x[2 * e], x[2 * e + 1], w[e]);
+#pragma unroll
+    for (int t = 0; t < kTerms<DT>; ++t)
+      *reinterpret_cast<uint4*>(dst + t * kTile) = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
+  } else {
+    *reinterpret_cast<uint4*>(dst) = v0;
+  }
+}
+
+template <int EPI, int DT>
+__global__ __launch_bounds__(256, DT == KIE_BF16 ? 1 : 2) void pf_gemm(const act_t<DT>* A, int M, int K, GemmB wb,
+                                                                        float* C, int ldc, act_t<DT>* H, int ldh) {
+  constexpr int NT = kTerms<DT>;
+  constexpr int kBuf = (NT + 1) * kTile;  // halves per buffer: NT A planes, then B
+  __shared__ __align__(16) uint16_t lds[2][kBuf];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 31, hf = l >> 5;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * kTM;
@@ -114,9 +195,9 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int 
     b_lo = wsel + (size_t)(n0 - (s0 ? 0 : s1 ? wb.end[0] : wb.end[1])) * K;
     b_hi = b_lo + (size_t)64 * K;
   }
-  // staging: thread t moves 16-byte piece t%8 of rows t/8 + 32i (i = 0..3) of both tiles
+  // staging: thread t moves 8-element piece t%8 of rows t/8 + 32i (i = 0..3) of both tiles
   const int pc = tid & 7, pr = tid >> 3;
-  const uint16_t* ag[4];
+  const act_t<DT>* ag[4];
   const uint16_t* bg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -131,29 +212,39 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int 
   const int soff = pr * kLS + 8 * pc;              // this thread's staging offset (row pr, piece pc)
   f16x_t acc[2][2] = {};
   const int nk = K / kBK;
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-#define KIE_PF_FETCH(k0)                                              \
-  do {                                                                \
-    ra0 = *reinterpret_cast<const uint4*>(ag[0] + (k0));              \
-    ra1 = *reinterpret_cast<const uint4*>(ag[1] + (k0));              \
-    ra2 = *reinterpret_cast<const uint4*>(ag[2] + (k0));              \
-    ra3 = *reinterpret_cast<const uint4*>(ag[3] + (k0));              \
-    rb0 = *reinterpret_cast<const uint4*>(bg[0] + (k0));              \
-    rb1 = *reinterpret_cast<const uint4*>(bg[1] + (k0));              \
-    rb2 = *reinterpret_cast<const uint4*>(bg[2] + (k0));              \
-    rb3 = *reinterpret_cast<const uint4*>(bg[3] + (k0));              \
+  constexpr bool F32A = DT == KIE_BF16;  // fp32 A pieces: two 16-byte vectors each
+  uint4 a00, a01, a10, a11, a20, a21, a30, a31, rb0, rb1, rb2, rb3;
+  a01 = a11 = a21 = a31 = make_uint4(0, 0, 0, 0);
+#define KIE_PF_LDA(i, k0, v) reinterpret_cast<const uint4*>(ag[i] + (k0))[v]
+#define KIE_PF_FETCH(k0)                                    \
+  do {                                                      \
+    a00 = KIE_PF_LDA(0, k0, 0);                             \
+    a10 = KIE_PF_LDA(1, k0, 0);                             \
+    a20 = KIE_PF_LDA(2, k0, 0);                             \
+    a30 = KIE_PF_LDA(3, k0, 0);                             \
+    if constexpr (F32A) {                                   \
+      a01 = KIE_PF_LDA(0, k0, 1);                           \
+      a11 = KIE_PF_LDA(1, k0, 1);                           \
+      a21 = KIE_PF_LDA(2, k0, 1);                           \
+      a31 = KIE_PF_LDA(3, k0, 1);                           \
+    }                                                       \
+    rb0 = *reinterpret_cast<const uint4*>(bg[0] + (k0));    \
+    rb1 = *reinterpret_cast<const uint4*>(bg[1] + (k0));    \
+    rb2 = *reinterpret_cast<const uint4*>(bg[2] + (k0));    \
+    rb3 = *reinterpret_cast<const uint4*>(bg[3] + (k0));    \
   } while (0)
-#define KIE_PF_STAGE(buf)                                                       \
-  do {                                                                          \
-    uint16_t* sa = &lds[buf][soff];                                             \
-    *reinterpret_cast<uint4*>(sa) = ra0;                                        \
-    *reinterpret_cast<uint4*>(sa + 32 * kLS) = ra1;                             \
-    *reinterpret_cast<uint4*>(sa + 64 * kLS) = ra2;                             \
-    *reinterpret_cast<uint4*>(sa + 96 * kLS) = ra3;                             \
-    *reinterpret_cast<uint4*>(sa + kTile) = rb0;                                \
-    *reinterpret_cast<uint4*>(sa + kTile + 32 * kLS) = rb1;                     \
-    *reinterpret_cast<uint4*>(sa + kTile + 64 * kLS) = rb2;                     \
-    *reinterpret_cast<uint4*>(sa + kTile + 96 * kLS) = rb3;                     \
+#define KIE_PF_STAGE(buf)                                   \
+  do {                                                      \
+    uint16_t* sa = &lds[buf][soff];                         \
+    stage_a<DT>(a00, a01, sa);                              \
+    stage_a<DT>(a10, a11, sa + 32 * kLS);                   \
+    stage_a<DT>(a20, a21, sa + 64 * kLS);                   \
+    stage_a<DT>(a30, a31, sa + 96 * kLS);                   \
+    uint16_t* sb = sa + NT * kTile;                         \
+    *reinterpret_cast<uint4*>(sb) = rb0;                    \
+    *reinterpret_cast<uint4*>(sb + 32 * kLS) = rb1;         \
+    *reinterpret_cast<uint4*>(sb + 64 * kLS) = rb2;         \
+    *reinterpret_cast<uint4*>(sb + 96 * kLS) = rb3;         \
   } while (0)
   KIE_PF_FETCH(0);
   KIE_PF_STAGE(0);
@@ -161,22 +252,27 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int 
   for (int t = 0; t < nk; ++t) {
     if (t + 1 < nk) KIE_PF_FETCH((t + 1) * kBK);
     const uint16_t* la = lds[t & 1];
-    const uint16_t* lb = la + kTile;
+    const uint16_t* lb = la + NT * kTile;
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int ko = 16 * kk + 8 * hf;
-      const h8_t a0 = *reinterpret_cast<const h8_t*>(la + arow0 * kLS + ko);
-      const h8_t a1 = *reinterpret_cast<const h8_t*>(la + (arow0 + 32) * kLS + ko);
-      const h8_t b0 = *reinterpret_cast<const h8_t*>(lb + brow0 * kLS + ko);
-      const h8_t b1 = *reinterpret_cast<const h8_t*>(lb + (brow0 + bstep) * kLS + ko);
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b1, acc[1][1], 0, 0, 0);
+      const uint4 b0 = *reinterpret_cast<const uint4*>(lb + brow0 * kLS + ko);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(lb + (brow0 + bstep) * kLS + ko);
+#pragma unroll
+      for (int tt = NT - 1; tt >= 0; --tt) {
+        const uint16_t* lt = la + tt * kTile;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(lt + arow0 * kLS + ko);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(lt + (arow0 + 32) * kLS + ko);
+        acc[0][0] = mma<DT>(a0, b0, acc[0][0]);
+        acc[0][1] = mma<DT>(a0, b1, acc[0][1]);
+        acc[1][0] = mma<DT>(a1, b0, acc[1][0]);
+        acc[1][1] = mma<DT>(a1, b1, acc[1][1]);
+      }
     }
     if (t + 1 < nk) KIE_PF_STAGE((t + 1) & 1);
     __syncthreads();
   }
+#undef KIE_PF_LDA
 #undef KIE_PF_FETCH
 #undef KIE_PF_STAGE
   // accumulator element 4ii + jj of acc[i][j]: row 64wm + 32i + 8ii + 4hf + jj, column block j, column r
@@ -191,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int 
         const int e = 4 * ii + jj;
         if constexpr (EPI == EPI_SWIGLU) {
           const float gt = acc[i][0][e], up = acc[i][1][e];
-          H[(size_t)m * ldh + n0 + 32 * wn + r] = f2h(gt / (1.0f + expf(-gt)) * up);
+          H[(size_t)m * ldh + n0 + 32 * wn + r] = to_act<DT>(gt / (1.0f + expf(-gt)) * up);
         } else {
           float* cp = C + (size_t)m * ldc + n0 + 64 * wn + r;
           if constexpr (EPI == EPI_ADD) {
@@ -210,6 +306,7 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const uint16_t* A, int M, int 
 // Thread (m, i) for rotary pair i < hd/2 of every head: q rotated in place
 // (fp32, as the decode path keeps it); k rotated and v copied into the cache
 // rows at position p0 + m.
+template <int DT>
 __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int hkv, int hd, const float* rope,
                                                   int p0, int max_seq, uint16_t* kc, uint16_t* vc) {
   const int half = hd >> 1, qd = hq * hd, kvd = hkv * hd, ld = qd + 2 * kvd;
@@ -229,15 +326,15 @@ __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int
       src[i + half] = rb;
     } else {
       uint16_t* dst = kc + ((size_t)(h - hq) * max_seq + pos) * hd;
-      dst[i] = f2h(ra);
-      dst[i + half] = f2h(rb);
+      dst[i] = from_f<DT>(ra);
+      dst[i + half] = from_f<DT>(rb);
     }
   } else {
     const int rr = r - (hq + hkv) * half, g = rr / half, i = rr % half;
     const float* src = row + qd + kvd + (size_t)g * hd;
     uint16_t* dst = vc + ((size_t)g * max_seq + pos) * hd;
-    dst[i] = f2h(src[i]);
-    dst[i + half] = f2h(src[i + half]);
+    dst[i] = from_f<DT>(src[i]);
+    dst[i + half] = from_f<DT>(src[i + half]);
   }
 }
 
@@ -259,9 +356,9 @@ __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int
 //     16c + 8(s/4) + 4(l/32) + s%4 for product c = 0, 1 of the tile, and V^T is
 //     read from LDS in that same row order.
 // Rows past the work-group's last key re-read that key (finite values, masked).
-template <int HD>
+template <int HD, int DT>
 __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, int hkv, int p0, int max_seq,
-                                               const uint16_t* kc, const uint16_t* vc, uint16_t* A16) {
+                                               const uint16_t* kc, const uint16_t* vc, act_t<DT>* Aout) {
   constexpr int KS = HD + 8;  // K tile row stride (halves): 16-byte aligned rows, 4-bank skew
   constexpr int VS = 36;      // V^T tile row stride (halves): 8-byte reads of 32 rows hit distinct banks
   constexpr int KT = 32 * KS, VT = HD * VS, NO = HD / 32, NK = HD / 16;
@@ -276,18 +373,29 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
   const int nkeys = p0 + min((qb + 1) * rows, M), nt = (nkeys + 31) / 32;
   const int qd = hq * HD, ldq = qd + 2 * hkv * HD;
 
-  // this lane's query, scaled for base-2 exponentials, as B operands
+  // this lane's query, scaled for base-2 exponentials, as B operands (bf16:
+  // QT terms of the split, each a product of its own)
+  constexpr int QT = DT == KIE_BF16 ? 2 : 1;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
-  h8_t qf[NK];
+  uint4 qf[QT][NK];
   {
     const float* qp = QKV + (size_t)min(mq0 + r, M - 1) * ldq + (size_t)h * HD + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 16 * kk);
       const float4 b = *reinterpret_cast<const float4*>(qp + 16 * kk + 4);
-      qf[kk] = h8_t{(_Float16)(a.x * scale), (_Float16)(a.y * scale), (_Float16)(a.z * scale),
-                    (_Float16)(a.w * scale), (_Float16)(b.x * scale), (_Float16)(b.y * scale),
-                    (_Float16)(b.z * scale), (_Float16)(b.w * scale)};
+      const float x[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
+                          b.x * scale, b.y * scale, b.z * scale, b.w * scale};
+      if constexpr (DT == KIE_BF16) {
+        uint32_t w[4][QT];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_pair<QT>(x[2 * e], x[2 * e + 1], w[e]);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) qf[t][kk] = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
+      } else {
+        qf[0][kk] = __builtin_bit_cast(uint4, h8_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                                                   (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]});
+      }
     }
   }
 
@@ -331,9 +439,11 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
     const uint16_t* vt = kt + KT;
     f16x_t s = {};
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const h8_t*>(kt + r * KS + 16 * kk + 8 * hf),
-                                                 qf[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < NK; ++kk) {
+      const uint4 ka = *reinterpret_cast<const uint4*>(kt + r * KS + 16 * kk + 8 * hf);
+#pragma unroll
+      for (int t = QT - 1; t >= 0; --t) s = mma<DT>(ka, qf[t][kk], s);
+    }
     const int k0 = 32 * t;
     if (k0 + 31 > p0 + mq0) {  // the tile reaches past this wave's first query: causal mask
 #pragma unroll
@@ -347,12 +457,26 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
     const float mn = fmaxf(mrun, tm);  // finite: cache row 0 is in every query's range
     const float al = __builtin_amdgcn_exp2f(mrun - mn);
     float ps = 0.f;
-    h8_t pb[2];
+    float pv[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(s[e] - mn);
-      ps += p;
-      pb[e >> 3][e & 7] = (_Float16)p;
+      pv[e] = __builtin_amdgcn_exp2f(s[e] - mn);
+      ps += pv[e];
+    }
+    uint4 pb[QT][2];  // probabilities as B operands (bf16: QT terms)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if constexpr (DT == KIE_BF16) {
+        uint32_t w[4][QT];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_pair<QT>(pv[8 * c + 2 * e], pv[8 * c + 2 * e + 1], w[e]);
+#pragma unroll
+        for (int t = 0; t < QT; ++t) pb[t][c] = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
+      } else {
+        const float* q = pv + 8 * c;
+        pb[0][c] = __builtin_bit_cast(uint4, h8_t{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3],
+                                                  (_Float16)q[4], (_Float16)q[5], (_Float16)q[6], (_Float16)q[7]});
+      }
     }
     lrun = lrun * al + ps;
     mrun = mn;
@@ -364,8 +488,9 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
       for (int ot = 0; ot < NO; ++ot) {
         const uint16_t* vp = vt + (32 * ot + r) * VS + 16 * c + 4 * hf;
         const uint2 lo = *reinterpret_cast<const uint2*>(vp), hi = *reinterpret_cast<const uint2*>(vp + 8);
-        const h8_t a = __builtin_bit_cast(h8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[ot] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[c], o[ot], 0, 0, 0);
+        const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int t = QT - 1; t >= 0; --t) o[ot] = mma<DT>(a, pb[t][c], o[ot]);
       }
     if (loader && t + 1 < nt) stage((t + 1) & 1);
     __syncthreads();
@@ -373,15 +498,20 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
   const float inv = 1.0f / (lrun + __shfl_xor(lrun, 32));
   const int m = mq0 + r;
   if (m < M) {
-    uint16_t* op = A16 + (size_t)m * qd + (size_t)h * HD + 4 * hf;
+    act_t<DT>* op = Aout + (size_t)m * qd + (size_t)h * HD + 4 * hf;
 #pragma unroll
     for (int ot = 0; ot < NO; ++ot)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {  // dimensions 32ot + 8i + 4(l/32) + 0..3
         const f16x_t& v = o[ot];
-        const uint2 w = make_uint2((uint32_t)f2h(v[4 * i] * inv) | ((uint32_t)f2h(v[4 * i + 1] * inv) << 16),
-                                   (uint32_t)f2h(v[4 * i + 2] * inv) | ((uint32_t)f2h(v[4 * i + 3] * inv) << 16));
-        *reinterpret_cast<uint2*>(op + 32 * ot + 8 * i) = w;  // dimensions 32ot + 8i + 4(l/32) + 0..3
+        if constexpr (DT == KIE_BF16) {
+          *reinterpret_cast<float4*>(op + 32 * ot + 8 * i) =
+              make_float4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+        } else {
+          *reinterpret_cast<uint2*>(op + 32 * ot + 8 * i) =
+              make_uint2((uint32_t)f2h(v[4 * i] * inv) | ((uint32_t)f2h(v[4 * i + 1] * inv) << 16),
+                         (uint32_t)f2h(v[4 * i + 2] * inv) | ((uint32_t)f2h(v[4 * i + 3] * inv) << 16));
+        }
       }
   }
 }
@@ -390,43 +520,59 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
 
 bool prefill_supported(const kie_config& c) {
   const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
-  return c.dtype == KIE_F16 && (c.head_dim == 64 || c.head_dim == 128) && c.d_model % kTN == 0 && qd % kTN == 0 &&
-         kvd % kTN == 0 && c.d_ffn % kTN == 0 && c.d_model % kBK == 0 && qd % kBK == 0 && c.d_ffn % kBK == 0;
+  return (c.dtype == KIE_F16 || c.dtype == KIE_BF16) && (c.head_dim == 64 || c.head_dim == 128) &&
+         c.d_model % kTN == 0 && qd % kTN == 0 && kvd % kTN == 0 && c.d_ffn % kTN == 0 && c.d_model % kBK == 0 &&
+         qd % kBK == 0 && c.d_ffn % kBK == 0;
 }
 
-hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
+size_t prefill_act_bytes(const kie_config& c) { return c.dtype == KIE_BF16 ? 4 : 2; }
+
+namespace {
+
+template <int DT>
+hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
   const kie_config& c = x.cfg;
   const int d = c.d_model, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, F = c.d_ffn;
   const int ldq = qd + 2 * kvd;
   const dim3 blk(256);
   const int mt = (M + kTM - 1) / kTM;
   hipStream_t st = x.stream;
-  pf_embed<<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
+  act_t<DT>* Xn = static_cast<act_t<DT>*>(x.Xn);
+  act_t<DT>* Aa = static_cast<act_t<DT>*>(x.A);
+  act_t<DT>* Hh = static_cast<act_t<DT>*>(x.H);
+  pf_embed<DT><<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
   for (int l = 0; l < c.n_layers; ++l) {
     const uint16_t* const* w = x.wtab + (size_t)l * W_PER_LAYER;
     const size_t plane = (size_t)l * c.n_kv_heads * c.max_seq * c.head_dim;
-    pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_ATTN_NORM], c.rms_eps, M, d, x.Xn);
+    pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_ATTN_NORM], c.rms_eps, M, d, Xn);
     const GemmB bqkv{{w[W_Q], w[W_K], w[W_V]}, {qd, qd + kvd, ldq}};
-    pf_gemm<EPI_STORE><<<dim3(ldq / kTN, mt), blk, 0, st>>>(x.Xn, M, d, bqkv, x.QKV, ldq, nullptr, 0);
+    pf_gemm<EPI_STORE, DT><<<dim3(ldq / kTN, mt), blk, 0, st>>>(Xn, M, d, bqkv, x.QKV, ldq, nullptr, 0);
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
-    pf_rope_kv<<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope, p0,
-                                                        c.max_seq, x.kc + plane, x.vc + plane);
+    pf_rope_kv<DT><<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope,
+                                                            p0, c.max_seq, x.kc + plane, x.vc + plane);
     const int G = c.n_heads / c.n_kv_heads, hw = G < 4 ? G : 4, rows = 32 * (4 / hw);
     const dim3 ag((M + rows - 1) / rows, c.n_kv_heads * (G / hw));
     if (c.head_dim == 128)
-      pf_attn<128><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane, x.vc + plane,
-                                       x.A16);
+      pf_attn<128, DT><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane,
+                                           x.vc + plane, Aa);
     else
-      pf_attn<64><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane, x.vc + plane,
-                                      x.A16);
-    pf_gemm<EPI_ADD><<<dim3(d / kTN, mt), blk, 0, st>>>(x.A16, M, qd, GemmB{{w[W_O]}, {d, d, d}}, x.X, d, nullptr, 0);
-    pf_rmsnorm<<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, x.Xn);
-    pf_gemm<EPI_SWIGLU><<<dim3(F / 64, mt), blk, 0, st>>>(x.Xn, M, d, GemmB{{w[W_GATE], w[W_UP]}, {F, F, F}}, nullptr,
-                                                          0, x.H16, F);
-    pf_gemm<EPI_ADD><<<dim3(d / kTN, mt), blk, 0, st>>>(x.H16, M, F, GemmB{{w[W_DOWN]}, {d, d, d}}, x.X, d, nullptr,
-                                                        0);
+      pf_attn<64, DT><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane,
+                                          x.vc + plane, Aa);
+    pf_gemm<EPI_ADD, DT><<<dim3(d / kTN, mt), blk, 0, st>>>(Aa, M, qd, GemmB{{w[W_O]}, {d, d, d}}, x.X, d, nullptr,
+                                                            0);
+    pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, Xn);
+    pf_gemm<EPI_SWIGLU, DT><<<dim3(F / 64, mt), blk, 0, st>>>(Xn, M, d, GemmB{{w[W_GATE], w[W_UP]}, {F, F, F}},
+                                                              nullptr, 0, Hh, F);
+    pf_gemm<EPI_ADD, DT><<<dim3(d / kTN, mt), blk, 0, st>>>(Hh, M, F, GemmB{{w[W_DOWN]}, {d, d, d}}, x.X, d,
+                                                            nullptr, 0);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
+  return x.cfg.dtype == KIE_BF16 ? run_chunk<KIE_BF16>(x, tok_dev, p0, M) : run_chunk<KIE_F16>(x, tok_dev, p0, M);
 }
 
 }  // namespace kie

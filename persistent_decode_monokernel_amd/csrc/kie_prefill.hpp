@@ -19,15 +19,18 @@ struct PrefillCtx {
   uint16_t* kc;                 // KV cache [L][Hkv][max_seq][hd]
   uint16_t* vc;
   float* X;                     // [chunk][d] residual
-  uint16_t* Xn;                 // [chunk][d] normalised input
-  float* QKV;                   // [chunk][qd + 2 kvd] (q rotated in place)
-  uint16_t* A16;                // [chunk][qd] attention output
-  uint16_t* H16;                // [chunk][F] SwiGLU output
+  void* Xn;                     // [chunk][d] normalised input      (activations: fp16 for
+  float* QKV;                   // [chunk][qd + 2 kvd] (q rotated in place)     fp16 models,
+  void* A;                      // [chunk][qd] attention output                 fp32 for
+  void* H;                      // [chunk][F] SwiGLU output                     bf16 models)
 };
 
-// Shapes the prompt path handles (fp16 weights; projection widths multiples
-// of 128, reduction widths multiples of 64).
+// Shapes the prompt path handles (fp16 or bf16 weights, head_dim 64 or 128;
+// projection widths multiples of 128, reduction widths multiples of 64).
 bool prefill_supported(const kie_config& c);
+
+// Bytes of one activation element between the prompt-path kernels.
+size_t prefill_act_bytes(const kie_config& c);
 
 // Positions p0 .. p0+M-1 (tokens tok_dev[0 .. M-1], device) through every
 // layer: KV cache rows written, residual left in ctx.X.  M <= kPfChunk.

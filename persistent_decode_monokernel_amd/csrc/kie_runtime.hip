@@ -107,11 +107,12 @@ Layout make_layout(const kie_config& c) {
   y.pf_chunk = prefill_supported(c) ? (c.max_seq < kPfChunk ? c.max_seq : kPfChunk) : 0;
   {
     const size_t pc = (size_t)y.pf_chunk, qd = (size_t)c.n_heads * c.head_dim, kvd = (size_t)c.n_kv_heads * c.head_dim;
+    const size_t ab = y.pf_chunk > 0 ? prefill_act_bytes(c) : 0;  // activation element: fp16, or fp32 (bf16)
     y.pf_x = take(pc * c.d_model * 4);
-    y.pf_xn = take(pc * c.d_model * 2);
+    y.pf_xn = take(pc * c.d_model * ab);
     y.pf_qkv = take(pc * (qd + 2 * kvd) * 4);
-    y.pf_a = take(pc * qd * 2);
-    y.pf_h = take(pc * c.d_ffn * 2);
+    y.pf_a = take(pc * qd * ab);
+    y.pf_h = take(pc * c.d_ffn * ab);
   }
   y.total = o;
   return y;
@@ -465,10 +466,10 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
     x.kc = reinterpret_cast<uint16_t*>(e->ws + e->lay.kc);
     x.vc = reinterpret_cast<uint16_t*>(e->ws + e->lay.vc);
     x.X = reinterpret_cast<float*>(e->ws + e->lay.pf_x);
-    x.Xn = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_xn);
+    x.Xn = e->ws + e->lay.pf_xn;
     x.QKV = reinterpret_cast<float*>(e->ws + e->lay.pf_qkv);
-    x.A16 = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_a);
-    x.H16 = reinterpret_cast<uint16_t*>(e->ws + e->lay.pf_h);
+    x.A = e->ws + e->lay.pf_a;
+    x.H = e->ws + e->lay.pf_h;
     first = n_prompt - 1;
     const int chunk = e->prefill_chunk > 0 ? e->prefill_chunk : e->lay.pf_chunk;
     for (int p0 = 0; p0 < first; p0 += chunk) {

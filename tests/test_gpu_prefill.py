@@ -8,7 +8,9 @@ the cache format), and the decode that continues from them.  Prompts cover a
 ragged tail (not a multiple of the 64-row tiles), several chunks (1100
 positions in chunks of 512), the one-token prompt (no matrix-core part), and
 every query-head grouping (1, 2, 4, 8 query heads per KV head) at head_dim 64
-and 128 over several 32-row attention tiles.
+and 128 over several 32-row attention tiles, and bf16 models (fp32
+activations split into bf16 terms on the matrix cores; the oracle's cache then
+stores each row in bf16, the engine's format).
 """
 import pytest
 import torch
@@ -20,6 +22,7 @@ from tests.gpu_util import LOGIT_TOL, check_tokens_and_logits, cpu_copy
 pytestmark = pytest.mark.gpu
 
 MID = synth.ModelShape("mid", 2, 512, 8, 2, 64, 1024, 1000, synth.F16)
+MID_BF16 = synth.ModelShape("mid_bf16", 2, 512, 8, 2, 64, 1024, 1000, synth.BF16)
 KV_TOL = 2e-2  # max |cache row - oracle row| (values ~N(0, 1); fp16 storage 2^-11 relative)
 
 
@@ -28,6 +31,8 @@ GROUPINGS = {
     "g2_hd64": synth.ModelShape("g2_hd64", 2, 512, 8, 4, 64, 1024, 1000, synth.F16),
     "g4_hd128": synth.ModelShape("g4_hd128", 1, 1024, 8, 2, 128, 2048, 1000, synth.F16),
     "g8_hd64": synth.ModelShape("g8_hd64", 2, 512, 8, 1, 64, 1024, 1000, synth.F16),
+    "g2_hd128_bf16": synth.ModelShape("g2_hd128_bf16", 3, 1024, 8, 4, 128, 2048, 2048, synth.BF16),
+    "g8_hd64_bf16": synth.ModelShape("g8_hd64_bf16", 2, 512, 8, 1, 64, 1024, 1000, synth.BF16),
 }
 
 
@@ -43,7 +48,8 @@ def run_case(s, P, n_dec, seed=31, chunk=0):
     assert st == kie.KIE_OK and pend == tok0
     eng.close()
     wc = cpu_copy(w)
-    cache = oracle.KVCache(s.n_layers, s.n_kv_heads, s.head_dim)
+    cache = oracle.KVCache(s.n_layers, s.n_kv_heads, s.head_dim,
+                           store_dtype=torch.bfloat16 if s.dtype == synth.BF16 else None)
     seq = [tok0] + toks
     ora = oracle.forward(wc, s, prompt + seq[:-1], cache, logits_rows=list(range(P - 1, P + n_dec)))
     gpu = torch.cat([lg0[None].cpu(), lgs.cpu()])
@@ -59,8 +65,9 @@ def test_tiny_prompt_path(P):
     run_case(synth.TINY, P, 24)
 
 
-def test_three_chunks_ragged():
-    run_case(MID, 1100, 16, chunk=512)
+@pytest.mark.parametrize("shape", [MID, MID_BF16])
+def test_three_chunks_ragged(shape):
+    run_case(shape, 1100, 16, chunk=512)
 
 
 @pytest.mark.parametrize("name", list(GROUPINGS))
@@ -72,8 +79,8 @@ def test_one_token_prompt():
     run_case(MID, 1, 8)
 
 
-def test_modes_agree():
-    s = MID
+@pytest.mark.parametrize("s", [MID, MID_BF16])
+def test_modes_agree(s):
     w = synth.make_weights(s, 41, device="cuda")
     prompt = synth.make_prompt(s, 200, 42).tolist()
     out = {}

@@ -399,18 +399,23 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
     }
   }
 
-  // tile staging: thread t moves 16-byte piece t%CPR of cache rows 2(t/CPR), +1
-  const int tid = threadIdx.x, pe = tid % CPR, pr = tid / CPR;
+  // tile staging.  K: thread t moves 16-byte piece t%CPR of cache rows
+  // 2(t/CPR), +1 (a wave's row-major writes cover consecutive banks).  V:
+  // thread t moves piece t/16 of rows 2(t%16), +1, so that the 16 lanes of a
+  // piece write the transposed words of 16 consecutive row pairs, 64 lanes
+  // spanning all banks.
+  const int tid = threadIdx.x, pe = tid % CPR, pr = tid / CPR, vpe = tid >> 4, vpr = tid & 15;
   const bool loader = tid < 16 * CPR;
   const uint16_t* kb = kc + (size_t)g * max_seq * HD + 8 * pe;
-  const uint16_t* vb = vc + (size_t)g * max_seq * HD + 8 * pe;
+  const uint16_t* vb = vc + (size_t)g * max_seq * HD + 8 * vpe;
   uint4 k0r, k1r, v0r, v1r;
   auto fetch = [&](int t) {
     const int j0 = min(32 * t + 2 * pr, nkeys - 1), j1 = min(32 * t + 2 * pr + 1, nkeys - 1);
     k0r = *reinterpret_cast<const uint4*>(kb + (size_t)j0 * HD);
     k1r = *reinterpret_cast<const uint4*>(kb + (size_t)j1 * HD);
-    v0r = *reinterpret_cast<const uint4*>(vb + (size_t)j0 * HD);
-    v1r = *reinterpret_cast<const uint4*>(vb + (size_t)j1 * HD);
+    const int i0 = min(32 * t + 2 * vpr, nkeys - 1), i1 = min(32 * t + 2 * vpr + 1, nkeys - 1);
+    v0r = *reinterpret_cast<const uint4*>(vb + (size_t)i0 * HD);
+    v1r = *reinterpret_cast<const uint4*>(vb + (size_t)i1 * HD);
   };
   auto stage = [&](int buf) {
     uint16_t* kt = lds + buf * (KT + VT);
@@ -419,9 +424,10 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
     *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * KS + 8 * pe) = k1r;
     const uint32_t a[4] = {v0r.x, v0r.y, v0r.z, v0r.w}, b[4] = {v1r.x, v1r.y, v1r.z, v1r.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // dimensions 8pe+2u and 8pe+2u+1, rows 2pr (low half) and 2pr+1
-      *reinterpret_cast<uint32_t*>(vt + (8 * pe + 2 * u) * VS + 2 * pr) = (a[u] & 0xFFFFu) | (b[u] << 16);
-      *reinterpret_cast<uint32_t*>(vt + (8 * pe + 2 * u + 1) * VS + 2 * pr) = (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+    for (int u = 0; u < 4; ++u) {  // dimensions 8vpe+2u and 8vpe+2u+1, rows 2vpr (low half) and 2vpr+1
+      *reinterpret_cast<uint32_t*>(vt + (8 * vpe + 2 * u) * VS + 2 * vpr) = (a[u] & 0xFFFFu) | (b[u] << 16);
+      *reinterpret_cast<uint32_t*>(vt + (8 * vpe + 2 * u + 1) * VS + 2 * vpr) =
+          (a[u] >> 16) | (b[u] & 0xFFFF0000u);
     }
   };
 
@@ -454,8 +460,20 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
 #pragma unroll
     for (int e = 1; e < 16; ++e) tm = fmaxf(tm, s[e]);
     tm = fmaxf(tm, __shfl_xor(tm, 32));
-    const float mn = fmaxf(mrun, tm);  // finite: cache row 0 is in every query's range
-    const float al = __builtin_amdgcn_exp2f(mrun - mn);
+    // Lazy rescaling: the reference maximum mrun moves only when a score
+    // exceeds it by more than 8 (base 2), so probabilities stay below 2^8 and
+    // most tiles skip rescaling the accumulators (the first tile always moves
+    // it: cache row 0 is in every query's range, so tm is finite).
+    const bool grow = tm > mrun + 8.f;
+    if (__any(grow)) {
+      const float mn = grow ? tm : mrun;
+      const float al = __builtin_amdgcn_exp2f(mrun - mn);
+      lrun *= al;
+#pragma unroll
+      for (int ot = 0; ot < NO; ++ot) o[ot] *= al;
+      mrun = mn;
+    }
+    const float mn = mrun;
     float ps = 0.f;
     float pv[16];
 #pragma unroll
@@ -478,10 +496,7 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
                                                   (_Float16)q[4], (_Float16)q[5], (_Float16)q[6], (_Float16)q[7]});
       }
     }
-    lrun = lrun * al + ps;
-    mrun = mn;
-#pragma unroll
-    for (int ot = 0; ot < NO; ++ot) o[ot] *= al;
+    lrun += ps;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll

@@ -128,9 +128,10 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t
 
 // ---- GEMM: C[M][N] = A[M][K] W[N][K]^T on the matrix cores --------------------
 //
-// Work-group (4 waves) tile 128 x 128, k-tiles of 64 staged in LDS (row-major,
-// rows padded to 144 bytes so that the 16-byte operand reads of 16 lanes hit
-// distinct banks), double-buffered with one barrier per k-tile; the next
+// Work-group (4 waves) tile 128 x 128, k-tiles of 64 (fp16) or 32 (bf16)
+// staged in LDS (row-major, rows padded to 144 or 80 bytes so that the
+// 16-byte operand reads of 16 lanes hit distinct banks), double-buffered with
+// one barrier per k-tile; the next
 // k-tile's global loads are in flight during the current one's products.
 // Wave (wm, wn) computes rows 64wm .. and columns 64wn .. as 2 x 2
 // accumulators of 32 x 32.  Both operands are k-contiguous in memory and in
@@ -144,9 +145,23 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t
 //   (wm, wn) takes gate columns 32wn .. and the matching up columns, so gate
 //   and up of one output land in the same lane: H = silu(gate) * up.
 // Rows of A beyond M re-read row M-1 and are not stored.  K % 64 == 0.
+// 72 KB of LDS per work-group (fp16: two per CU), 80 KB (bf16, three A term
+// planes: two per CU).
 enum : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
-constexpr int kTM = 128, kTN = 128, kBK = 64, kLS = kBK + 8;  // LDS row stride in halves
-constexpr int kTile = kTM * kLS;                                // halves per operand tile
+constexpr int kTM = 128, kTN = 128;
+template <int DT>
+constexpr int kBK = DT == KIE_BF16 ? 32 : 64;  // k-tile width (measured best per dtype)
+template <int DT>
+constexpr int kLS = kBK<DT> + 8;  // LDS row stride in halves (144 or 80 bytes)
+template <int DT>
+constexpr int kTile = kTM * kLS<DT>;  // halves per operand tile
+template <int DT>
+constexpr int kPPR = kBK<DT> / 8;  // 8-element pieces per tile row
+template <int DT>
+constexpr int kRPP = 256 / kPPR<DT>;  // tile rows staged per pass
+template <int DT>
+constexpr int kPasses = kTM / kRPP<DT>;  // passes per operand tile (4 or 2)
+constexpr int kBKMax = 64;                // every supported reduction width is a multiple of this
 
 struct GemmB {
   const uint16_t* w[3];  // stacked matrices ([rows][K] each); EPI_SWIGLU: gate, up
@@ -165,17 +180,18 @@ __device__ __forceinline__ void stage_a(uint4 v0, uint4 v1, uint16_t* dst) {
     for (int e = 0; e < 4; ++e) split_pair<kTerms<DT>>(x[2 * e], x[2 * e + 1], w[e]);
 #pragma unroll
     for (int t = 0; t < kTerms<DT>; ++t)
-      *reinterpret_cast<uint4*>(dst + t * kTile) = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
+      *reinterpret_cast<uint4*>(dst + t * kTile<DT>) = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
   } else {
     *reinterpret_cast<uint4*>(dst) = v0;
   }
 }
 
 template <int EPI, int DT>
-__global__ __launch_bounds__(256, DT == KIE_BF16 ? 1 : 2) void pf_gemm(const act_t<DT>* A, int M, int K, GemmB wb,
+__global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int K, GemmB wb,
                                                                         float* C, int ldc, act_t<DT>* H, int ldh) {
   constexpr int NT = kTerms<DT>;
-  constexpr int kBuf = (NT + 1) * kTile;  // halves per buffer: NT A planes, then B
+  constexpr int BK = kBK<DT>, LS = kLS<DT>, TILE = kTile<DT>, PPR = kPPR<DT>, RPP = kRPP<DT>, PASSES = kPasses<DT>;
+  constexpr int kBuf = (NT + 1) * TILE;  // halves per buffer: NT A planes, then B
   __shared__ __align__(16) uint16_t lds[2][kBuf];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 31, hf = l >> 5;
   const int wm = wave >> 1, wn = wave & 1;
@@ -196,12 +212,12 @@ __global__ __launch_bounds__(256, DT == KIE_BF16 ? 1 : 2) void pf_gemm(const act
     b_hi = b_lo + (size_t)64 * K;
   }
   // staging: thread t moves 8-element piece t%8 of rows t/8 + 32i (i = 0..3) of both tiles
-  const int pc = tid & 7, pr = tid >> 3;
+  const int pc = tid % PPR, pr = tid / PPR;
   const act_t<DT>* ag[4];
   const uint16_t* bg[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int row = pr + 32 * i;
+    const int row = pr + RPP * (i % PASSES);
     ag[i] = A + (size_t)min(m0 + row, M - 1) * K + 8 * pc;
     bg[i] = (row < 64 ? b_lo + (size_t)row * K : b_hi + (size_t)(row - 64) * K) + 8 * pc;
   }
@@ -209,9 +225,9 @@ __global__ __launch_bounds__(256, DT == KIE_BF16 ? 1 : 2) void pf_gemm(const act
   const int arow0 = 64 * wm + r;
   const int brow0 = EPI == EPI_SWIGLU ? 32 * wn + r : 64 * wn + r;
   const int bstep = EPI == EPI_SWIGLU ? 64 : 32;  // B row offset of column block 1 (up rows for SwiGLU)
-  const int soff = pr * kLS + 8 * pc;              // this thread's staging offset (row pr, piece pc)
+  const int soff = pr * LS + 8 * pc;              // this thread's staging offset (row pr, piece pc)
   f16x_t acc[2][2] = {};
-  const int nk = K / kBK;
+  const int nk = K / BK;
   constexpr bool F32A = DT == KIE_BF16;  // fp32 A pieces: two 16-byte vectors each
   uint4 a00, a01, a10, a11, a20, a21, a30, a31, rb0, rb1, rb2, rb3;
   a01 = a11 = a21 = a31 = make_uint4(0, 0, 0, 0);
@@ -220,49 +236,57 @@ __global__ __launch_bounds__(256, DT == KIE_BF16 ? 1 : 2) void pf_gemm(const act
   do {                                                      \
     a00 = KIE_PF_LDA(0, k0, 0);                             \
     a10 = KIE_PF_LDA(1, k0, 0);                             \
-    a20 = KIE_PF_LDA(2, k0, 0);                             \
-    a30 = KIE_PF_LDA(3, k0, 0);                             \
     if constexpr (F32A) {                                   \
       a01 = KIE_PF_LDA(0, k0, 1);                           \
       a11 = KIE_PF_LDA(1, k0, 1);                           \
-      a21 = KIE_PF_LDA(2, k0, 1);                           \
-      a31 = KIE_PF_LDA(3, k0, 1);                           \
     }                                                       \
     rb0 = *reinterpret_cast<const uint4*>(bg[0] + (k0));    \
     rb1 = *reinterpret_cast<const uint4*>(bg[1] + (k0));    \
-    rb2 = *reinterpret_cast<const uint4*>(bg[2] + (k0));    \
-    rb3 = *reinterpret_cast<const uint4*>(bg[3] + (k0));    \
+    if constexpr (PASSES > 2) {                            \
+      a20 = KIE_PF_LDA(2, k0, 0);                           \
+      a30 = KIE_PF_LDA(3, k0, 0);                           \
+      if constexpr (F32A) {                                 \
+        a21 = KIE_PF_LDA(2, k0, 1);                         \
+        a31 = KIE_PF_LDA(3, k0, 1);                         \
+      }                                                     \
+      rb2 = *reinterpret_cast<const uint4*>(bg[2] + (k0));  \
+      rb3 = *reinterpret_cast<const uint4*>(bg[3] + (k0));  \
+    }                                                       \
   } while (0)
 #define KIE_PF_STAGE(buf)                                   \
   do {                                                      \
     uint16_t* sa = &lds[buf][soff];                         \
     stage_a<DT>(a00, a01, sa);                              \
-    stage_a<DT>(a10, a11, sa + 32 * kLS);                   \
-    stage_a<DT>(a20, a21, sa + 64 * kLS);                   \
-    stage_a<DT>(a30, a31, sa + 96 * kLS);                   \
-    uint16_t* sb = sa + NT * kTile;                         \
+    stage_a<DT>(a10, a11, sa + RPP * LS);                 \
+    if constexpr (PASSES > 2) {                            \
+      stage_a<DT>(a20, a21, sa + 2 * RPP * LS);           \
+      stage_a<DT>(a30, a31, sa + 3 * RPP * LS);           \
+    }                                                       \
+    uint16_t* sb = sa + NT * TILE;                         \
     *reinterpret_cast<uint4*>(sb) = rb0;                    \
-    *reinterpret_cast<uint4*>(sb + 32 * kLS) = rb1;         \
-    *reinterpret_cast<uint4*>(sb + 64 * kLS) = rb2;         \
-    *reinterpret_cast<uint4*>(sb + 96 * kLS) = rb3;         \
+    *reinterpret_cast<uint4*>(sb + RPP * LS) = rb1;       \
+    if constexpr (PASSES > 2) {                            \
+      *reinterpret_cast<uint4*>(sb + 2 * RPP * LS) = rb2; \
+      *reinterpret_cast<uint4*>(sb + 3 * RPP * LS) = rb3; \
+    }                                                       \
   } while (0)
   KIE_PF_FETCH(0);
   KIE_PF_STAGE(0);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) KIE_PF_FETCH((t + 1) * kBK);
+    if (t + 1 < nk) KIE_PF_FETCH((t + 1) * BK);
     const uint16_t* la = lds[t & 1];
-    const uint16_t* lb = la + NT * kTile;
+    const uint16_t* lb = la + NT * TILE;
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
+    for (int kk = 0; kk < BK / 16; ++kk) {
       const int ko = 16 * kk + 8 * hf;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(lb + brow0 * kLS + ko);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(lb + (brow0 + bstep) * kLS + ko);
+      const uint4 b0 = *reinterpret_cast<const uint4*>(lb + brow0 * LS + ko);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(lb + (brow0 + bstep) * LS + ko);
 #pragma unroll
       for (int tt = NT - 1; tt >= 0; --tt) {
-        const uint16_t* lt = la + tt * kTile;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(lt + arow0 * kLS + ko);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(lt + (arow0 + 32) * kLS + ko);
+        const uint16_t* lt = la + tt * TILE;
+        const uint4 a0 = *reinterpret_cast<const uint4*>(lt + arow0 * LS + ko);
+        const uint4 a1 = *reinterpret_cast<const uint4*>(lt + (arow0 + 32) * LS + ko);
         acc[0][0] = mma<DT>(a0, b0, acc[0][0]);
         acc[0][1] = mma<DT>(a0, b1, acc[0][1]);
         acc[1][0] = mma<DT>(a1, b0, acc[1][0]);
@@ -536,8 +560,8 @@ __global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, 
 bool prefill_supported(const kie_config& c) {
   const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
   return (c.dtype == KIE_F16 || c.dtype == KIE_BF16) && (c.head_dim == 64 || c.head_dim == 128) &&
-         c.d_model % kTN == 0 && qd % kTN == 0 && kvd % kTN == 0 && c.d_ffn % kTN == 0 && c.d_model % kBK == 0 &&
-         qd % kBK == 0 && c.d_ffn % kBK == 0;
+         c.d_model % kTN == 0 && qd % kTN == 0 && kvd % kTN == 0 && c.d_ffn % kTN == 0 && c.d_model % kBKMax == 0 &&
+         qd % kBKMax == 0 && c.d_ffn % kBKMax == 0;
 }
 
 size_t prefill_act_bytes(const kie_config& c) { return c.dtype == KIE_BF16 ? 4 : 2; }

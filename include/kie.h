@@ -146,7 +146,8 @@ kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
  * positions run as dense matrix-core products where the shape allows.
  * Starts a new sequence: the KV cache is rewritten from position 0.
  *   prompt_host[n_prompt]: token ids in [0, vocab), 1 <= n_prompt <= max_seq.
- *   next_token_host: receives the greedy token after the last prompt position.
+ *   next_token_host: receives the token after the last prompt position (greedy,
+ *   or drawn as kie_set_sampling chose).
  *   logits_dev: NULL, or device float[vocab] receiving the logits of the last
  *   prompt position.
  * After success the engine holds pos = n_prompt and the new token pending. */
@@ -154,8 +155,10 @@ kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prom
                        int32_t* next_token_host, float* logits_dev);
 
 /* How kie_prefill() runs the prompt.  KIE_PREFILL_AUTO (default): positions
- * 0 .. n_prompt-2 as dense products on the matrix cores (fp16 models whose
- * projection widths are multiples of 128; others fall back), then the last
+ * 0 .. n_prompt-2 as dense products on the matrix cores (GEMMs and flash
+ * attention; fp16 activations for fp16 models, fp32 activations split into
+ * three bf16 terms for bf16 models; shapes whose projection widths are
+ * multiples of 128 -- others fall back to the decode loop), then the last
  * position as one forced step of the persistent decode kernel, which yields
  * the logits and the first token.  KIE_PREFILL_DECODE_LOOP: every prompt
  * position as a forced step of the persistent decode kernel.  The pages put

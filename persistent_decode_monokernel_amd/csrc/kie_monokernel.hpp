@@ -22,8 +22,12 @@
 //     WO      x_mid = x + Wo a           (rows split over work-groups)
 //     GATEUP  h = silu(Wg n) * (Wu n), n = RMSNorm(x_mid)*g
 //     DOWN    x_next = x_mid + Wd h
-//   LM head:  logits rows, per-work-group (max, index) partial
+//   LM head:  logits rows, per-work-group (max, index) partial (and, when
+//             sampling, the work-group's 64 best rows as a sorted list)
 //   argmax:   every work-group reduces all partials -> same next token; EOS test
+//   sampling: (instead of the argmax token) work-groups 0..31 merge groups of
+//             8 lists, work-group 0 merges the groups, draws and publishes
+//             the token, the others poll it
 //
 // Code-generation note.  All stages are inlined into one kernel.  Each stage
 // re-derives the thread index and the parameter pointer through an empty asm
@@ -1267,7 +1271,8 @@ __device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr,
   stamp(tr, P.L * kStagesPerLayer + 1, 2, c.t, t_lo);
 }
 
-// Gather the per-work-group (max, index) partials -> the greedy token.  Every
+// Gather the per-work-group (max, index) partials -> the greedy token (also
+// the end-of-step marker when sampling chooses the token instead).  Every
 // work-group reduces the same values in the same order, so all agree.
 __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* X, int& tok, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);

@@ -109,3 +109,27 @@ def test_sampling_arguments_checked():
     eng.set_sampling(0.0, 0, 0.0)  # greedy: the other arguments are ignored
     eng.set_sampling(0.8, 64, 1.0, 2**64 - 1)
     eng.close()
+
+
+@pytest.mark.parametrize("shape,grid", [(synth.TINY, 60), (synth.TINY, 97), (BIGV, 255)])
+def test_sampling_on_subset_grids(shape, grid):
+    """Work-group 0's merge of the group lists takes a different branch for <= 8,
+    <= 16 and <= 32 groups, and a grid that 8 does not divide leaves padding
+    lists in the last group."""
+    T, k, p, seed = 1.0, 64, 0.97, 21
+    w = synth.make_weights(shape, 17, device="cuda", gain_jitter=0.1)
+    prompt = synth.make_prompt(shape, 10, 18).tolist()
+    eng = kie.Engine(shape, max_seq=40)
+    eng.load_weights(w)
+    eng.set_grid(grid)
+    eng.set_sampling(T, k, p, seed)
+    tok0, lg0 = eng.prefill(prompt, want_logits=True)
+    toks, lgs, st = eng.decode(24, want_logits=True)
+    assert st == kie.KIE_OK
+    eng.close()
+    seq = [tok0] + toks
+    gpu = torch.cat([lg0[None].cpu(), lgs.cpu()])
+    positions = list(range(len(prompt) - 1, len(prompt) - 1 + len(seq)))
+    agree, border = check_sampled(seq, gpu, positions, T, k, p, seed, f"{shape.name} grid {grid}")
+    print(f"{shape.name} grid {grid}: {agree} agree, {border} borderline, {len(set(seq))} distinct")
+    assert border <= 1 and len(set(seq)) > 1

@@ -277,22 +277,32 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
     if (t + 1 < nk) KIE_PF_FETCH((t + 1) * BK);
     const uint16_t* la = lds[t & 1];
     const uint16_t* lb = la + NT * TILE;
+    // every operand of the k-tile is read before the first product, so the
+    // LDS latency is paid once per tile
+    constexpr int KS = BK / 16;
+    uint4 ob[KS][2], oa[KS][NT][2];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
       const int ko = 16 * kk + 8 * hf;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(lb + brow0 * LS + ko);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(lb + (brow0 + bstep) * LS + ko);
+      ob[kk][0] = *reinterpret_cast<const uint4*>(lb + brow0 * LS + ko);
+      ob[kk][1] = *reinterpret_cast<const uint4*>(lb + (brow0 + bstep) * LS + ko);
 #pragma unroll
-      for (int tt = NT - 1; tt >= 0; --tt) {
+      for (int tt = 0; tt < NT; ++tt) {
         const uint16_t* lt = la + tt * TILE;
-        const uint4 a0 = *reinterpret_cast<const uint4*>(lt + arow0 * LS + ko);
-        const uint4 a1 = *reinterpret_cast<const uint4*>(lt + (arow0 + 32) * LS + ko);
-        acc[0][0] = mma<DT>(a0, b0, acc[0][0]);
-        acc[0][1] = mma<DT>(a0, b1, acc[0][1]);
-        acc[1][0] = mma<DT>(a1, b0, acc[1][0]);
-        acc[1][1] = mma<DT>(a1, b1, acc[1][1]);
+        oa[kk][tt][0] = *reinterpret_cast<const uint4*>(lt + arow0 * LS + ko);
+        oa[kk][tt][1] = *reinterpret_cast<const uint4*>(lt + (arow0 + 32) * LS + ko);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int tt = NT - 1; tt >= 0; --tt) {
+        acc[0][0] = mma<DT>(oa[kk][tt][0], ob[kk][0], acc[0][0]);
+        acc[0][1] = mma<DT>(oa[kk][tt][0], ob[kk][1], acc[0][1]);
+        acc[1][0] = mma<DT>(oa[kk][tt][1], ob[kk][0], acc[1][0]);
+        acc[1][1] = mma<DT>(oa[kk][tt][1], ob[kk][1], acc[1][1]);
+      }
     if (t + 1 < nk) KIE_PF_STAGE((t + 1) & 1);
     __syncthreads();
   }

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t
 // Rows of A beyond M re-read row M-1 and are not stored.  K % 64 == 0.
 // 72 KB of LDS per work-group (fp16: two per CU), 80 KB (bf16, three A term
 // planes: two per CU).
-enum : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+enum : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_PART = 3 };
 constexpr int kTM = 128, kTN = 128;
 template <int DT>
 constexpr int kBK = DT == KIE_BF16 ? 32 : 64;  // k-tile width (measured best per dtype)
@@ -227,7 +227,12 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
   const int bstep = EPI == EPI_SWIGLU ? 64 : 32;  // B row offset of column block 1 (up rows for SwiGLU)
   const int soff = pr * LS + 8 * pc;              // this thread's staging offset (row pr, piece pc)
   f16x_t acc[2][2] = {};
-  const int nk = K / BK;
+  // split-K (EPI_PART): slice z of gridDim.z takes k-tiles [kt0, kt0 + nk) and
+  // writes its partial product to C + z * M * ldc; otherwise one slice
+  const int nk_all = K / BK;
+  const int kt0 = (int)((long)nk_all * blockIdx.z / gridDim.z);
+  const int nk = (int)((long)nk_all * (blockIdx.z + 1) / gridDim.z) - kt0;
+  if constexpr (EPI == EPI_PART) C += (size_t)blockIdx.z * M * ldc;
   constexpr bool F32A = DT == KIE_BF16;  // fp32 A pieces: two 16-byte vectors each
   uint4 a00, a01, a10, a11, a20, a21, a30, a31, rb0, rb1, rb2, rb3;
   a01 = a11 = a21 = a31 = make_uint4(0, 0, 0, 0);
@@ -270,11 +275,11 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
       *reinterpret_cast<uint4*>(sb + 3 * RPP * LS) = rb3; \
     }                                                       \
   } while (0)
-  KIE_PF_FETCH(0);
+  KIE_PF_FETCH(kt0 * BK);
   KIE_PF_STAGE(0);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) KIE_PF_FETCH((t + 1) * BK);
+    if (t + 1 < nk) KIE_PF_FETCH((kt0 + t + 1) * BK);
     const uint16_t* la = lds[t & 1];
     const uint16_t* lb = la + NT * TILE;
     // every operand of the k-tile is read before the first product, so the
@@ -327,12 +332,38 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
           if constexpr (EPI == EPI_ADD) {
             cp[0] += acc[i][0][e];
             cp[32] += acc[i][1][e];
-          } else {
+          } else {  // EPI_STORE, EPI_PART
             cp[0] = acc[i][0][e];
             cp[32] = acc[i][1][e];
           }
         }
       }
+}
+
+// Split-K reduction: C[m][n] (+)= sum over z = 0 .. S-1 of P[z][m][n], the
+// slices added in order (deterministic).  Four columns per thread; N % 4 == 0.
+template <bool ADD>
+__global__ __launch_bounds__(256) void pf_splitk(const float* P, int S, int M, int N, float* C, int ldc) {
+  const int q = blockIdx.x * 256 + threadIdx.x, nq = N >> 2;
+  if (q >= M * nq) return;
+  const int m = q / nq, n = (q % nq) * 4;
+  float4 a = *reinterpret_cast<const float4*>(P + (size_t)m * N + n);
+  for (int z = 1; z < S; ++z) {
+    const float4 b = *reinterpret_cast<const float4*>(P + ((size_t)z * M + m) * N + n);
+    a.x += b.x;
+    a.y += b.y;
+    a.z += b.z;
+    a.w += b.w;
+  }
+  float4* c = reinterpret_cast<float4*>(C + (size_t)m * ldc + n);
+  if (ADD) {
+    const float4 o = *c;
+    a.x += o.x;
+    a.y += o.y;
+    a.z += o.z;
+    a.w += o.w;
+  }
+  *c = a;
 }
 
 // ---- rotary embedding, KV append ------------------------------------------
@@ -576,6 +607,13 @@ bool prefill_supported(const kie_config& c) {
 
 size_t prefill_act_bytes(const kie_config& c) { return c.dtype == KIE_BF16 ? 4 : 2; }
 
+size_t prefill_part_floats(const kie_config& c, int chunk) {
+  const size_t n = (size_t)c.n_heads * c.head_dim + 2ull * c.n_kv_heads * c.head_dim;
+  const size_t widest = n > (size_t)c.d_model ? n : (size_t)c.d_model;
+  const size_t need = 4ull * chunk * widest, cap = 1024ull * kTM * kTN;
+  return need < cap ? need : cap;
+}
+
 namespace {
 
 template <int DT>
@@ -589,13 +627,36 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
   act_t<DT>* Xn = static_cast<act_t<DT>*>(x.Xn);
   act_t<DT>* Aa = static_cast<act_t<DT>*>(x.A);
   act_t<DT>* Hh = static_cast<act_t<DT>*>(x.H);
+  // C (+)= A W^T for EPI_STORE / EPI_ADD.  With fewer than 512 output tiles
+  // (two work-groups per CU) the k-loop is split into S <= 4 slices whose
+  // partial products the reduction adds in order; S * tiles < 1024 bounds the
+  // partial buffer (x.P) at 1024 tiles of 128 x 128.
+  auto gemm = [&](bool add, const act_t<DT>* A, int K, const GemmB& b, int N, float* C, int ldc) {
+    const int tiles = (N / kTN) * mt, nk = K / kBK<DT>;
+    int S = tiles >= 512 ? 1 : (512 + tiles - 1) / tiles;
+    S = S > 4 ? 4 : S;
+    S = S > nk ? nk : S;
+    if (S == 1) {
+      if (add)
+        pf_gemm<EPI_ADD, DT><<<dim3(N / kTN, mt), blk, 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
+      else
+        pf_gemm<EPI_STORE, DT><<<dim3(N / kTN, mt), blk, 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
+      return;
+    }
+    pf_gemm<EPI_PART, DT><<<dim3(N / kTN, mt, S), blk, 0, st>>>(A, M, K, b, x.P, N, nullptr, 0);
+    const int q = (M * N / 4 + 255) / 256;
+    if (add)
+      pf_splitk<true><<<q, blk, 0, st>>>(x.P, S, M, N, C, ldc);
+    else
+      pf_splitk<false><<<q, blk, 0, st>>>(x.P, S, M, N, C, ldc);
+  };
   pf_embed<DT><<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
   for (int l = 0; l < c.n_layers; ++l) {
     const uint16_t* const* w = x.wtab + (size_t)l * W_PER_LAYER;
     const size_t plane = (size_t)l * c.n_kv_heads * c.max_seq * c.head_dim;
     pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_ATTN_NORM], c.rms_eps, M, d, Xn);
     const GemmB bqkv{{w[W_Q], w[W_K], w[W_V]}, {qd, qd + kvd, ldq}};
-    pf_gemm<EPI_STORE, DT><<<dim3(ldq / kTN, mt), blk, 0, st>>>(Xn, M, d, bqkv, x.QKV, ldq, nullptr, 0);
+    gemm(false, Xn, d, bqkv, ldq, x.QKV, ldq);
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
     pf_rope_kv<DT><<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope,
                                                             p0, c.max_seq, x.kc + plane, x.vc + plane);
@@ -607,13 +668,11 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
     else
       pf_attn<64, DT><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane,
                                           x.vc + plane, Aa);
-    pf_gemm<EPI_ADD, DT><<<dim3(d / kTN, mt), blk, 0, st>>>(Aa, M, qd, GemmB{{w[W_O]}, {d, d, d}}, x.X, d, nullptr,
-                                                            0);
+    gemm(true, Aa, qd, GemmB{{w[W_O]}, {d, d, d}}, d, x.X, d);
     pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, Xn);
     pf_gemm<EPI_SWIGLU, DT><<<dim3(F / 64, mt), blk, 0, st>>>(Xn, M, d, GemmB{{w[W_GATE], w[W_UP]}, {F, F, F}},
                                                               nullptr, 0, Hh, F);
-    pf_gemm<EPI_ADD, DT><<<dim3(d / kTN, mt), blk, 0, st>>>(Hh, M, F, GemmB{{w[W_DOWN]}, {d, d, d}}, x.X, d,
-                                                            nullptr, 0);
+    gemm(true, Hh, F, GemmB{{w[W_DOWN]}, {d, d, d}}, d, x.X, d);
   }
   return hipGetLastError();
 }

@@ -23,6 +23,7 @@ struct PrefillCtx {
   float* QKV;                   // [chunk][qd + 2 kvd] (q rotated in place)     fp16 models,
   void* A;                      // [chunk][qd] attention output                 fp32 for
   void* H;                      // [chunk][F] SwiGLU output                     bf16 models)
+  float* P;                     // split-K partial products (prefill_part_floats)
 };
 
 // Shapes the prompt path handles (fp16 or bf16 weights, head_dim 64 or 128;
@@ -31,6 +32,9 @@ bool prefill_supported(const kie_config& c);
 
 // Bytes of one activation element between the prompt-path kernels.
 size_t prefill_act_bytes(const kie_config& c);
+
+// fp32 elements of the split-K partial-product buffer for chunks of `chunk`.
+size_t prefill_part_floats(const kie_config& c, int chunk);
 
 // Positions p0 .. p0+M-1 (tokens tok_dev[0 .. M-1], device) through every
 // layer: KV cache rows written, residual left in ctx.X.  M <= kPfChunk.

@@ -79,7 +79,7 @@ XchLayout xch_layout(const kie_config& c) {
 
 struct Layout {
   size_t params, rope, lw, kc, vc, xch, ctl, tok, forced, total;
-  size_t pf_x, pf_xn, pf_qkv, pf_a, pf_h;  // matrix-core prompt path (0 bytes when unsupported)
+  size_t pf_x, pf_xn, pf_qkv, pf_a, pf_h, pf_p;  // matrix-core prompt path (0 bytes when unsupported)
   int pf_chunk;
   size_t kv_plane_bytes;
   XchLayout xl;
@@ -113,6 +113,7 @@ Layout make_layout(const kie_config& c) {
     y.pf_qkv = take(pc * (qd + 2 * kvd) * 4);
     y.pf_a = take(pc * qd * ab);
     y.pf_h = take(pc * c.d_ffn * ab);
+    y.pf_p = take(y.pf_chunk > 0 ? prefill_part_floats(c, y.pf_chunk) * 4 : 0);
   }
   y.total = o;
   return y;
@@ -470,6 +471,7 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
     x.QKV = reinterpret_cast<float*>(e->ws + e->lay.pf_qkv);
     x.A = e->ws + e->lay.pf_a;
     x.H = e->ws + e->lay.pf_h;
+    x.P = reinterpret_cast<float*>(e->ws + e->lay.pf_p);
     first = n_prompt - 1;
     const int chunk = e->prefill_chunk > 0 ? e->prefill_chunk : e->lay.pf_chunk;
     for (int p0 = 0; p0 < first; p0 += chunk) {

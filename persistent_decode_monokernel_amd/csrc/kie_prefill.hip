@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int
 //     read from LDS in that same row order.
 // Rows past the work-group's last key re-read that key (finite values, masked).
 template <int HD, int DT>
-__global__ __launch_bounds__(256) void pf_attn(const float* QKV, int M, int hq, int hkv, int p0, int max_seq,
+__global__ __launch_bounds__(256, 2) void pf_attn(const float* QKV, int M, int hq, int hkv, int p0, int max_seq,
                                                const uint16_t* kc, const uint16_t* vc, act_t<DT>* Aout) {
   constexpr int KS = HD + 8;  // K tile row stride (halves): 16-byte aligned rows, 4-bank skew
   constexpr int VS = 36;      // V^T tile row stride (halves): 8-byte reads of 32 rows hit distinct banks

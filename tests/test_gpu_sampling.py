@@ -133,3 +133,62 @@ def test_sampling_on_subset_grids(shape, grid):
     agree, border = check_sampled(seq, gpu, positions, T, k, p, seed, f"{shape.name} grid {grid}")
     print(f"{shape.name} grid {grid}: {agree} agree, {border} borderline, {len(set(seq))} distinct")
     assert border <= 1 and len(set(seq)) > 1
+
+
+BF16_SHAPE = synth.ModelShape("g2_hd128_bf16", 3, 1024, 8, 4, 128, 2048, 2048, synth.BF16)
+
+
+def test_sampled_tokens_match_oracle_bf16():
+    """bf16 kernel instances (three-term activations), oracle cache stored in bf16."""
+    T, k, p, seed = 0.9, 32, 0.9, 5
+    w, prompt, seq, gpu = run(BF16_SHAPE, T, k, p, seed, P=20, n=30)
+    P = len(prompt)
+    positions = list(range(P - 1, P - 1 + len(seq)))
+    agree, border = check_sampled(seq, gpu, positions, T, k, p, seed, "bf16")
+    cache = oracle.KVCache(BF16_SHAPE.n_layers, BF16_SHAPE.n_kv_heads, BF16_SHAPE.head_dim, store_dtype=torch.bfloat16)
+    ora = oracle.forward(cpu_copy(w), BF16_SHAPE, prompt + seq[:-1], cache, logits_rows=positions)
+    err = check_logits(gpu, ora, "bf16")
+    print(f"bf16: {agree} agree, {border} borderline, max |dlogit| {err:.2e}")
+    assert border <= 1 and len(set(seq)) > 1
+
+
+def test_sampled_eos_stops_after_emitting_it():
+    """The stop test applies to the drawn token: with the k-th drawn token as
+    EOS id, the run emits exactly k+1 tokens (the EOS token included)."""
+    s = synth.TINY
+    w = synth.make_weights(s, 23, device="cuda")
+    prompt = synth.make_prompt(s, 8, 24).tolist()
+    eng = kie.Engine(s, max_seq=64)
+    eng.load_weights(w)
+    eng.set_sampling(1.0, 64, 1.0, 77)
+    eng.prefill(prompt)
+    ref, _, _ = eng.decode(20)
+    k = next(i for i in range(3, 20) if ref[i] not in ref[:i])  # first fresh token from the 4th on
+    eng.prefill(prompt)
+    toks, _, st = eng.decode(20, eos_id=ref[k])
+    eng.close()
+    assert st == kie.KIE_OK and toks == ref[:k + 1]
+
+
+def test_sampling_with_decode_loop_prefill():
+    """In the decode-loop prompt mode only the last prompt step draws; the
+    token and its continuation equal the matrix-core mode's."""
+    s = synth.TINY
+    w = synth.make_weights(s, 29, device="cuda")
+    prompt = synth.make_prompt(s, 30, 30).tolist()
+    out = []
+    for mode in (kie.KIE_PREFILL_AUTO, kie.KIE_PREFILL_DECODE_LOOP):
+        eng = kie.Engine(s, max_seq=64)
+        eng.load_weights(w)
+        eng.set_prefill_mode(mode)
+        eng.set_sampling(0.8, 40, 0.95, 3)
+        t0, lg = eng.prefill(prompt, want_logits=True)
+        toks, lgs, st = eng.decode(12, want_logits=True)
+        assert st == kie.KIE_OK
+        out.append(([t0] + toks, torch.cat([lg[None].cpu(), lgs.cpu()])))
+        eng.close()
+    (sa, la), (sb, lb) = out
+    positions = list(range(len(prompt) - 1, len(prompt) + 12))
+    for seq, lg in out:  # each mode's draws follow the rule on its own logits
+        check_sampled(seq, lg, positions, 0.8, 40, 0.95, 3, "decode-loop prefill")
+    assert (la - lb).abs().max().item() <= 2e-2

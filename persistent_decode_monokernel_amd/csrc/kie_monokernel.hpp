@@ -642,7 +642,11 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
           float sd = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) sd += q[h][e] * kf[e];
-          sd = (hd == 128 ? sum16(sd) : sum8(sd)) * scale;
+          // rows of 16 lanes (hd 128) take one more DPP step than rows of 8;
+          // a select instead of a branch keeps the heads' chains interleaved
+          sd = sum8(sd);
+          const float sd16 = sd + dpp<DPP_MIRROR>(sd);
+          sd = (hd == 128 ? sd16 : sd) * scale;
           const float mn = fmaxf(mx[h], sd);
           const float fo = safe_exp_diff(mx[h], mn), fp = fast_exp2(sd - mn);
           ls[h] = ls[h] * fo + fp;

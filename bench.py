@@ -66,8 +66,8 @@ def bytes_per_launch(s, pos0: int, n_steps: int) -> int:
 # kernel sources hash to the value they were taken at.
 MEASURED_TRAFFIC = {
     # kie_decode(1024) after a 512-token prefill, FETCH_SIZE x 2.0, WRITE_SIZE x 1.0
-    "2b": {"src_sha": "6386f5d6772b9f52", "steps": 1024,
-           "fetch_bytes": 1856837451 * 1024 * 2, "write_bytes": 33793986 * 1024},
+    "2b": {"src_sha": "52a12879a002613b", "steps": 1024,
+           "fetch_bytes": 1856886984 * 1024 * 2, "write_bytes": 33793986 * 1024},
 }
 
 KERNEL_SRC_DIR = os.path.join(ROOT, "persistent_decode_monokernel_amd", "csrc")

@@ -386,7 +386,7 @@ def main():
         pmc_summary(args.pmc_summary, copy_bytes=args.copy_bytes)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+        print(json.dumps({"error": "kie runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not an implemented path", "n_gpus": args.gpus}))
         sys.exit(2)
 

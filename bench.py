@@ -498,6 +498,7 @@ def main():
         "prefill_s": prefill_s,
         "status": st,
     }
+    eng.close()  # release the engine while the runtime is up, not during interpreter teardown
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(s, w, P, args.cpu_budget)

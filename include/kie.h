@@ -132,12 +132,22 @@ size_t kie_workspace_bytes(const kie_config* cfg);
  * ws_bytes >= kie_workspace_bytes(cfg), 256-byte aligned, owned by the caller
  * and kept alive until kie_destroy().  hip_stream: a hipStream_t, or NULL for
  * the default stream; every call of this engine runs on it.  Writes the rotary
- * table into the workspace.  On success *out is a new handle. */
+ * table into the workspace.  On success *out is a new handle.
+ * Source: the pages define no API.  They state the problem this call sets up --
+ * one request (batch 1) served by one program resident on the GPU
+ * (revietech.ru page, section "Chto takoye monokernel") -- and the rest follows
+ * the stated target's boundary (create / load weights / prefill / decode /
+ * destroy, device memory owned by the caller). */
 kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes,
                       void* hip_stream, kie_engine** out);
 
 /* Register the weights (device pointers, see kie_weights).  Resets the
- * sequence: a kie_prefill() or kie_import_kv() must follow before decoding. */
+ * sequence: a kie_prefill() or kie_import_kv() must follow before decoding.
+ * Errors: KIE_ERR_ARG for a null or misaligned (not 16-byte) pointer.
+ * Source: the pages define no API; the weights are streamed from device
+ * memory layer by layer on every token (revietech.ru page, section "Tsifry
+ * proizvoditelnosti": batch-1 decode is bound by HBM bandwidth), so they stay
+ * resident and borrowed, as the stated target's boundary has it. */
 kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
 
 /* Run the prompt through the model (see kie_set_prefill_mode for how): the
@@ -221,11 +231,16 @@ kie_status kie_set_sampling(kie_engine* e, float temperature, int32_t top_k, flo
  * n_generated and the last emitted token is pending, so decoding can go on.
  * On KIE_ERR_TIMEOUT they hold the completed steps too, but the step that
  * timed out may have left a partial KV-cache row: the sequence must be
- * restarted by kie_prefill() or kie_import_kv() (KIE_ERR_STATE until then). */
+ * restarted by kie_prefill() or kie_import_kv() (KIE_ERR_STATE until then).
+ * Source: one resident kernel runs every step -- layers, LM-head sampling and
+ * the end-of-sequence check -- without returning to the CPU or launching a
+ * kernel per token (revietech.ru page, section "Chto takoye monokernel");
+ * n_steps and the host arrays are the stated target's boundary. */
 kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id, int32_t* tokens_host,
                       int32_t* n_generated, float* logits_dev);
 
-/* Release the handle.  NULL-safe.  Frees no caller memory. */
+/* Release the handle.  NULL-safe.  Frees no caller memory.  The pages define
+ * no API; this closes the stated target's create / destroy pair. */
 void kie_destroy(kie_engine* e);
 
 /* ---- sequence state: checkpoint / resume -------------------------------- */

@@ -281,10 +281,34 @@ static bool grid_fits(const kie_config& c, const Layout& lay, int grid) {
          (uint64_t)c.d_ffn * grid < (1ull << 32);
 }
 
-extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes, void* hip_stream,
-                                 kie_engine** out) {
-  if (!out) return KIE_ERR_ARG;
-  *out = nullptr;
+// Rotary table, built in double precision (angle(p, i) = p * base^(-2i/hd)),
+// copied to the device in pieces through a stack buffer (no host allocation).
+static hipError_t write_rope(const kie_config& c, char* dst_dev, hipStream_t st) {
+  const int half = c.head_dim / 2;
+  constexpr int kChunk = 4096;  // floats per piece
+  float buf[kChunk];
+  const size_t total = (size_t)c.max_seq * half * 2;
+  for (size_t at = 0; at < total; at += kChunk) {
+    const size_t n = total - at < (size_t)kChunk ? total - at : (size_t)kChunk;
+    for (size_t k = 0; k < n; k += 2) {
+      const size_t e = (at + k) / 2;
+      const int p = (int)(e / half), i = (int)(e % half);
+      const double ang = (double)p * std::pow((double)c.rope_base, -2.0 * i / c.head_dim);
+      buf[k] = (float)std::cos(ang);
+      buf[k + 1] = (float)std::sin(ang);
+    }
+    hipError_t he = hipMemcpyAsync(dst_dev + at * sizeof(float), buf, n * sizeof(float), hipMemcpyHostToDevice, st);
+    if (he == hipSuccess) he = hipStreamSynchronize(st);  // buf is reused by the next piece
+    if (he != hipSuccess) return he;
+  }
+  return hipSuccess;
+}
+
+// Engine construction shared by kie_create and kie_create_static: `e` is
+// default-constructed storage the caller owns; with_events creates the HIP
+// events that time each persistent launch.
+static kie_status create_impl(kie_engine* e, const kie_config* cfg, void* workspace_dev, size_t ws_bytes,
+                              void* hip_stream, bool with_events) {
   const kie_status v = kie_config_validate(cfg);
   if (v != KIE_OK) return v;
   if (!workspace_dev || (reinterpret_cast<uintptr_t>(workspace_dev) & 255) != 0) return KIE_ERR_ARG;
@@ -299,8 +323,6 @@ extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, siz
   KIE_HIP(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
   if (!coop) return KIE_ERR_UNSUPPORTED;
 
-  kie_engine* e = new (std::nothrow) kie_engine();
-  if (!e) return KIE_ERR_ARG;
   e->cfg = *cfg;
   e->lay = lay;
   e->lds = lds_plan(*cfg);
@@ -313,34 +335,38 @@ extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, siz
   hipError_t he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, e->lds.bytes);
   int per_cu = 0;
   if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, e->lds.bytes);
-  if (he != hipSuccess || per_cu < 1) {
-    delete e;
-    return he != hipSuccess ? hip_fail(he, "occupancy") : KIE_ERR_UNSUPPORTED;
-  }
+  if (he != hipSuccess) return hip_fail(he, "occupancy");
+  if (per_cu < 1) return KIE_ERR_UNSUPPORTED;
   // One resident work-group per compute unit.
   e->grid = e->cu_count < kMaxWG ? e->cu_count : kMaxWG;
-  if (!grid_fits(*cfg, lay, e->grid)) {
-    delete e;
-    return KIE_ERR_UNSUPPORTED;
-  }
+  if (!grid_fits(*cfg, lay, e->grid)) return KIE_ERR_UNSUPPORTED;
 
-  // Rotary table, built in double precision: angle(p, i) = p * base^(-2i/hd).
-  const int half = cfg->head_dim / 2;
-  std::vector<float> rope((size_t)cfg->max_seq * half * 2);
-  for (int p = 0; p < cfg->max_seq; ++p)
-    for (int i = 0; i < half; ++i) {
-      const double ang = (double)p * std::pow((double)cfg->rope_base, -2.0 * i / cfg->head_dim);
-      rope[((size_t)p * half + i) * 2] = (float)std::cos(ang);
-      rope[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
-    }
-  he = hipMemcpyAsync(e->ws + lay.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice, e->stream);
+  he = write_rope(*cfg, e->ws + lay.rope, e->stream);
   if (he == hipSuccess) he = launch_fill(reinterpret_cast<uint32_t*>(e->ws + lay.ctl), CTL_WORDS, 0u, e->stream);
-  if (he == hipSuccess) he = hipEventCreate(&e->ev0);
-  if (he == hipSuccess) he = hipEventCreate(&e->ev1);
+  if (he == hipSuccess && with_events) he = hipEventCreate(&e->ev0);
+  if (he == hipSuccess && with_events) he = hipEventCreate(&e->ev1);
   if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
-  if (he != hipSuccess) {
-    kie_destroy(e);
-    return hip_fail(he, "create");
+  if (he != hipSuccess) return hip_fail(he, "create");
+  return KIE_OK;
+}
+
+static void release_events(kie_engine* e) {
+  if (e->ev0) (void)hipEventDestroy(e->ev0);
+  if (e->ev1) (void)hipEventDestroy(e->ev1);
+  e->ev0 = e->ev1 = nullptr;
+}
+
+extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes, void* hip_stream,
+                                 kie_engine** out) {
+  if (!out) return KIE_ERR_ARG;
+  *out = nullptr;
+  kie_engine* e = new (std::nothrow) kie_engine();
+  if (!e) return KIE_ERR_ARG;
+  const kie_status st = create_impl(e, cfg, workspace_dev, ws_bytes, hip_stream, true);
+  if (st != KIE_OK) {
+    release_events(e);
+    delete e;
+    return st;
   }
   *out = e;
   return KIE_OK;
@@ -348,8 +374,7 @@ extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, siz
 
 extern "C" void kie_destroy(kie_engine* e) {
   if (!e) return;
-  if (e->ev0) (void)hipEventDestroy(e->ev0);
-  if (e->ev1) (void)hipEventDestroy(e->ev1);
+  release_events(e);
   delete e;
 }
 
@@ -424,15 +449,15 @@ static kie_status run_persistent(kie_engine* e, Params& P, int* done, int* last)
   e->params_host = P;  // stays valid until the copy below has run (the call synchronises)
   KIE_HIP(hipMemcpyAsync(dev_params, &e->params_host, sizeof(Params), hipMemcpyHostToDevice, e->stream));
   void* args[] = {&dev_params};
-  KIE_HIP(hipEventRecord(e->ev0, e->stream));
+  if (e->ev0) KIE_HIP(hipEventRecord(e->ev0, e->stream));
   KIE_HIP(hipLaunchCooperativeKernel(monokernel_fn(e->cfg), dim3(e->grid), dim3(kThreads), args,
                                      (unsigned)e->lds.bytes, e->stream));
-  KIE_HIP(hipEventRecord(e->ev1, e->stream));
+  if (e->ev1) KIE_HIP(hipEventRecord(e->ev1, e->stream));
   uint32_t ctl[4] = {0, 0, 0, 0};
   KIE_HIP(hipMemcpyAsync(ctl, P.ctl, sizeof(ctl), hipMemcpyDeviceToHost, e->stream));
   KIE_HIP(hipStreamSynchronize(e->stream));
   float ms = 0.f;
-  if (hipEventElapsedTime(&ms, e->ev0, e->ev1) == hipSuccess) e->last_ms = ms;
+  if (e->ev0 && e->ev1 && hipEventElapsedTime(&ms, e->ev0, e->ev1) == hipSuccess) e->last_ms = ms;
   *done = (int)ctl[CTL_DONE];
   *last = (int)ctl[CTL_LAST];
   e->last_steps = *done;

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
@@ -165,6 +166,8 @@ class Engine:
         self.shape = shape
         self.cfg = make_config(shape, max_seq)
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         nbytes = workspace_bytes(self.cfg)
         if nbytes == 0:
             raise KieError(validate(self.cfg), "kie_workspace_bytes")
@@ -184,6 +187,11 @@ class Engine:
             self._h = ctypes.c_void_p()
 
     def __del__(self):
+        # At interpreter exit the HIP runtime and any profiler attached to it
+        # may already be shutting down: release the handle only while the
+        # interpreter is alive (call close() explicitly before exit).
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
@@ -193,13 +201,26 @@ class Engine:
         """w: dict from synth.make_weights (device tensors of the engine dtype)."""
         layers = w["layers"]
         L = len(layers)
+        s = self.shape
+        if L != s.n_layers:
+            raise KieError(KIE_ERR_ARG, f"load_weights: {L} layers for a {s.n_layers}-layer shape")
+        d, qd, kvd, F, V = s.d_model, s.n_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.d_ffn, s.vocab
+        numel = {"tok_emb": V * d, "final_norm": d, "lm_head": V * d, "attn_norm": d, "ffn_norm": d,
+                 "wq": qd * d, "wk": kvd * d, "wv": kvd * d, "wo": d * qd, "w_gate": F * d, "w_up": F * d,
+                 "w_down": d * F}
+        self._check_tensor("tok_emb", w["tok_emb"], numel["tok_emb"])
+        self._check_tensor("final_norm", w["final_norm"], numel["final_norm"])
+        self._check_tensor("lm_head", w["lm_head"], numel["lm_head"])
         arrs = {}
         keep: List[torch.Tensor] = [w["tok_emb"], w["final_norm"], w["lm_head"]]
         for key in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down"):
             ts = [lw[key].contiguous() for lw in layers]
+            for t in ts:
+                self._check_tensor(key, t, numel[key])
             keep.extend(ts)
             arrs[key] = (ctypes.c_void_p * L)(*[_dptr(t) for t in ts])
-        kw = kie_weights(_dptr(w["tok_emb"]), _dptr(w["final_norm"]), _dptr(w["lm_head"]),
+        kw = kie_weights(_dptr(w["tok_emb"].contiguous()), _dptr(w["final_norm"].contiguous()),
+                         _dptr(w["lm_head"].contiguous()),
                          *[ctypes.cast(arrs[k], _PP) for k in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm",
                                                                "w_gate", "w_up", "w_down")])
         _check(lib().kie_load_weights(self._h, ctypes.byref(kw)), "kie_load_weights")
@@ -227,8 +248,24 @@ class Engine:
         out = [toks[i] for i in range(n.value)]
         return out, (lg[: n.value] if lg is not None else None), st
 
+    def _check_tensor(self, what: str, t: torch.Tensor, numel: int, shape=None):
+        """The library reads device memory through raw pointers: reject a tensor
+        on another device, of another dtype or of another size before it does."""
+        if not isinstance(t, torch.Tensor) or t.device != self.device:
+            raise KieError(KIE_ERR_ARG, f"{what}: not a tensor on {self.device}")
+        if t.dtype != self.shape.torch_dtype:
+            raise KieError(KIE_ERR_ARG, f"{what}: dtype {t.dtype}, engine dtype {self.shape.torch_dtype}")
+        if t.numel() != numel or (shape is not None and tuple(t.shape) != tuple(shape)):
+            raise KieError(KIE_ERR_ARG, f"{what}: shape {tuple(t.shape)} does not match the engine's")
+
     def import_kv(self, k: torch.Tensor, v: torch.Tensor, pending: int):
+        s = self.shape
+        if k.dim() != 4:
+            raise KieError(KIE_ERR_ARG, "import_kv: k must be [n_layers][n_kv_heads][n_pos][head_dim]")
         n_pos = int(k.shape[2])
+        want = (s.n_layers, s.n_kv_heads, n_pos, s.head_dim)
+        self._check_tensor("import_kv k", k, int(torch.Size(want).numel()), want)
+        self._check_tensor("import_kv v", v, int(torch.Size(want).numel()), want)
         k = k.contiguous()
         v = v.contiguous()
         _check(lib().kie_import_kv(self._h, ctypes.c_void_p(_dptr(k)), ctypes.c_void_p(_dptr(v)), n_pos,

@@ -29,7 +29,8 @@
  * Conventions shared by every entry point
  *  - Memory.  The caller owns every device buffer: weights and the workspace.
  *    The library never allocates or frees device memory; the opaque engine
- *    handle (host memory) is the only object it owns.
+ *    handle (host memory) is the only object it owns.  (kie_create_static
+ *    uses a static workspace that is part of the loaded library instead.)
  *  - Pointers marked _dev are device pointers, _host are host pointers.
  *  - Matrices are row-major [out][in] (PyTorch nn.Linear layout), elements of
  *    the engine dtype (IEEE fp16 or bf16 as raw 16-bit words).
@@ -140,6 +141,27 @@ size_t kie_workspace_bytes(const kie_config* cfg);
  * destroy, device memory owned by the caller). */
 kie_status kie_create(const kie_config* cfg, void* workspace_dev, size_t ws_bytes,
                       void* hip_stream, kie_engine** out);
+
+/* Bytes of the library's static device workspace (64 MiB) used by
+ * kie_create_static(). */
+#define KIE_STATIC_WORKSPACE_BYTES (64u << 20)
+
+/* kie_create() for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * engine's workspace is a static device array inside the library instead of a
+ * caller buffer, and the handle lives in static storage.  The call allocates
+ * nothing (no hipMalloc / hipFree, no host heap) and creates no HIP events
+ * (kie_info.last_kernel_ms stays 0 for such an engine).
+ *   KIE_ERR_CAPACITY when kie_workspace_bytes(cfg) > KIE_STATIC_WORKSPACE_BYTES.
+ *   KIE_ERR_STATE while this GPU's static engine exists (one per GPU: every GPU
+ *   the library runs on holds its own static workspace, of that size, until
+ *   the process ends).
+ * The engine is then used and released (kie_destroy) like any other; the
+ * workspace keeps the last engine's contents, and everything a launch needs
+ * cleared is cleared by the library before it.  Engines of one GPU share the
+ * array: a static engine must not run while another static engine of the same
+ * GPU is alive, and calls that overlap on one GPU race. */
+kie_status kie_create_static(const kie_config* cfg, void* hip_stream, kie_engine** out);
 
 /* Register the weights (device pointers, see kie_weights).  Resets the
  * sequence: a kie_prefill() or kie_import_kv() must follow before decoding.

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -206,6 +207,7 @@ struct kie_engine {
   int samp_k = 0;         // sampling (kie_set_sampling); 0 = greedy
   float samp_scale = 0.f, samp_top_p = 1.f;
   uint64_t samp_seed = 0;
+  bool is_static = false;  // static storage on the static workspace (kie_create_static)
 };
 
 extern "C" const char* kie_status_string(kie_status s) {
@@ -372,9 +374,71 @@ extern "C" kie_status kie_create(const kie_config* cfg, void* workspace_dev, siz
   return KIE_OK;
 }
 
+// ---- the static workspace (kie_create_static) -----------------------------
+//
+// For callers that cannot allocate device memory.  The workspace is this
+// file-scope device array: every GPU the library runs on holds its own copy
+// (KIE_STATIC_WORKSPACE_BYTES) until the process ends.  In host code the
+// array's name is only a host-side handle; its device address on each GPU is
+// looked up once per device with hipGetSymbolAddress and kept in
+// g_scratch_dev, which is what every launch and copy uses.  The engine handle
+// lives in static storage too, one per device.
+static __device__ __align__(256) unsigned char scratch[KIE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch` on each GPU (null until looked up)
+alignas(kie_engine) unsigned char g_static_store[kMaxDevices][sizeof(kie_engine)];
+bool g_static_live[kMaxDevices];
+}  // namespace
+
+extern "C" kie_status kie_create_static(const kie_config* cfg, void* hip_stream, kie_engine** out) {
+  if (!out) return KIE_ERR_ARG;
+  *out = nullptr;
+  const kie_status v = kie_config_validate(cfg);
+  if (v != KIE_OK) return v;
+  const size_t need = make_layout(*cfg).total;
+  if (need > (size_t)KIE_STATIC_WORKSPACE_BYTES) {
+    if (getenv("KIE_VERBOSE"))
+      fprintf(stderr, "kie_create_static: workspace of %zu bytes exceeds the static %zu bytes\n", need,
+              (size_t)KIE_STATIC_WORKSPACE_BYTES);
+    return KIE_ERR_CAPACITY;
+  }
+  int dev = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return KIE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_live[dev]) return KIE_ERR_STATE;  // this GPU's static engine is still in use
+  if (!g_scratch_dev[dev]) {  // once per device, with that device current
+    void* p = nullptr;
+    KIE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255) != 0) return KIE_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  kie_engine* e = new (g_static_store[dev]) kie_engine();  // placement: no allocation
+  e->is_static = true;
+  const kie_status st = create_impl(e, cfg, g_scratch_dev[dev], (size_t)KIE_STATIC_WORKSPACE_BYTES, hip_stream,
+                                    false);
+  if (st != KIE_OK) {
+    e->~kie_engine();
+    return st;
+  }
+  g_static_live[dev] = true;
+  *out = e;
+  return KIE_OK;
+}
+
 extern "C" void kie_destroy(kie_engine* e) {
   if (!e) return;
   release_events(e);
+  if (e->is_static) {
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    const int dev = e->device;
+    e->~kie_engine();
+    if (dev >= 0 && dev < kMaxDevices) g_static_live[dev] = false;
+    return;
+  }
   delete e;
 }
 

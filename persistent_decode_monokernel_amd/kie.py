@@ -29,6 +29,7 @@ KIE_F16 = 1
 KIE_BF16 = 2
 KIE_PREFILL_AUTO = 0
 KIE_PREFILL_DECODE_LOOP = 1
+KIE_STATIC_WORKSPACE_BYTES = 64 << 20  # include/kie.h
 
 
 class KieError(RuntimeError):
@@ -77,6 +78,8 @@ SIGNATURES = {
     "kie_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kie_config)]),
     "kie_create": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                   ctypes.POINTER(ctypes.c_void_p)]),
+    "kie_create_static": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_void_p)]),
     "kie_load_weights": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kie_weights)]),
     "kie_prefill": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
@@ -162,7 +165,9 @@ class Engine:
     construction unless given).
     """
 
-    def __init__(self, shape, max_seq: int, device="cuda", stream=None):
+    def __init__(self, shape, max_seq: int, device="cuda", stream=None, static: bool = False):
+        """static=True: the engine runs on the library's static workspace
+        (kie_create_static), and no workspace tensor is allocated."""
         self.shape = shape
         self.cfg = make_config(shape, max_seq)
         self.device = torch.device(device)
@@ -171,12 +176,19 @@ class Engine:
         nbytes = workspace_bytes(self.cfg)
         if nbytes == 0:
             raise KieError(validate(self.cfg), "kie_workspace_bytes")
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         h = ctypes.c_void_p()
-        with torch.cuda.device(self.device):
-            _check(lib().kie_create(ctypes.byref(self.cfg), ctypes.c_void_p(_dptr(self.workspace)), nbytes,
-                                    ctypes.c_void_p(_stream_handle(self.stream)), ctypes.byref(h)), "kie_create")
+        if static:
+            self.workspace = None
+            with torch.cuda.device(self.device):
+                _check(lib().kie_create_static(ctypes.byref(self.cfg), ctypes.c_void_p(_stream_handle(self.stream)),
+                                               ctypes.byref(h)), "kie_create_static")
+        else:
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            with torch.cuda.device(self.device):
+                _check(lib().kie_create(ctypes.byref(self.cfg), ctypes.c_void_p(_dptr(self.workspace)), nbytes,
+                                        ctypes.c_void_p(_stream_handle(self.stream)), ctypes.byref(h)),
+                       "kie_create")
         self._h = h
         self._weights = None
 

@@ -179,6 +179,31 @@ def gemv_probe_bench(n_copies: int = 16):
             torch.cuda.empty_cache()
 
 
+STREAM_BYTES = 1 << 30  # 1 GiB: four times the memory-side cache
+
+
+def stream_peak(depths=(3,), reps: int = 4, verbose: bool = False) -> float:
+    """Read-stream ceiling (GB/s): the best of kie_stream_probe over `depths`
+    (non-temporal dwordx4 loads in flight per thread) on a 1 GiB buffer."""
+    import torch
+
+    from persistent_decode_monokernel_amd import kie
+
+    buf = torch.ones(STREAM_BYTES // 2, dtype=torch.float16, device="cuda")
+    kie.stream_probe(buf, depth=depths[0], reps=1)  # warm-up
+    best = 0.0
+    for d in depths:
+        ms, read = kie.stream_probe(buf, depth=d, reps=reps)
+        gbs = read / (ms / 1e3) / 1e9
+        best = max(best, gbs)
+        if verbose:
+            print(json.dumps({"stream_probe_depth": d, "in_flight_per_cu_KiB": 8 * d, "bytes": read,
+                              "kernel_ms": ms, "GB/s": gbs, "frac_of_8000": gbs / HBM_PEAK_GBS}), flush=True)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
 def ttft_bench(name: str, modes=("auto", "decode_loop"), chunks=(0,)):
     """Time to first token: wall time of kie_prefill (prompt already on the
     host, weights resident) for the workload's prompt, per prefill mode (and
@@ -367,6 +392,8 @@ def main():
                     help="only summarise rocprofv3 --pmc counter CSVs")
     ap.add_argument("--copy-bytes", type=int, default=0, help="bytes read (= written) by the copy probe")
     ap.add_argument("--gemv", action="store_true", help="only run the isolated GEMV probe workload")
+    ap.add_argument("--stream", action="store_true",
+                    help="only run the read-stream probe (1, 2, 3, 4, 6, 8 loads in flight per thread)")
     ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")
     ap.add_argument("--pf-chunk", type=int, nargs="+", default=[0],
                     help="with --ttft: matrix-core chunk sizes to time (0 = default)")
@@ -395,6 +422,9 @@ def main():
         return
     if args.gemv:
         gemv_probe_bench()
+        return
+    if args.stream:
+        stream_peak(depths=(1, 2, 3, 4, 6, 8), verbose=True)
         return
     if args.grid_sweep:
         grid_sweep(args.workload, args.grid_sweep, args.steps)
@@ -499,6 +529,12 @@ def main():
         "status": st,
     }
     eng.close()  # release the engine while the runtime is up, not during interpreter teardown
+    try:  # the measured read-stream ceiling, next to the published peak
+        peak = stream_peak()
+        out["roofline"]["stream_peak"] = peak
+        out["roofline"]["frac_vs_stream_peak"] = achieved / peak
+    except Exception as e:  # reported, never required
+        log(f"stream probe failed: {e!r}")
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(s, w, P, args.cpu_budget)

@@ -316,6 +316,21 @@ kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_steps);
  * the kernel.  -1 (default) disables it. */
 kie_status kie_set_withhold(kie_engine* e, int32_t wg);
 
+/* Race test: the next persistent launches make work-group `wg` wait `ticks`
+ * of the 100 MHz counter (at most 1e8) before each of its hand-off
+ * publications (QKV, attention partials, merge, Wo, gate/up, down), so every
+ * consumer of its words sees them arrive late.  The results must not change
+ * (tests compare tokens and logits bit for bit).  wg = -1 turns it off. */
+kie_status kie_set_delay(kie_engine* e, int32_t wg, uint64_t ticks);
+
+/* Race test of the exchange-set recycling: after a launch that completed S >= 2
+ * steps, the two exchange sets not used by its last step must hold the NaN
+ * pattern in every word (one was recycled during the last step, the other
+ * during the step before it, or never used).  *dirty_words receives the count
+ * of words that do not (0 when the invariant holds).  KIE_ERR_STATE if the last
+ * launch completed fewer than 2 steps.  Copies the sets to the host. */
+kie_status kie_check_idle_sets(const kie_engine* e, uint64_t* dirty_words);
+
 /* Per-token timeline.  kie_trace_words(e) = uint64 words a trace buffer
  * needs: (n_layers*6 + 2) slots x grid work-groups x 4 stamps.  After
  * kie_set_trace(e, buf, step), every persistent launch of the engine stamps
@@ -355,6 +370,24 @@ kie_status kie_check_tiling(const kie_config* cfg, int32_t grid, int32_t full);
 kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
                           const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
                           void* hip_stream, float* kernel_ms);
+
+/* ---- read-stream probe --------------------------------------------------- */
+
+/* The HBM read-stream ceiling the decode kernel's GEMVs are measured against:
+ * batch-1 decode is bound by memory bandwidth (revietech.ru page, section
+ * "Tsifry proizvoditelnosti"), and what a kernel can actually stream is below
+ * the published peak.  ONE grid-wide launch (one work-group of 512 threads per
+ * compute unit) reads buf_dev (bytes, 16-byte aligned; choose it larger than
+ * the 256 MB memory-side cache) reps times with the decode kernel's load form
+ * (non-temporal dwordx4), `depth` loads in flight per thread (1, 2, 3, 4, 6 or
+ * 8: 8 KiB to 64 KiB per compute unit).  Each work-group reads whole passes of
+ * 512 vectors of its contiguous share; bytes read = grid * 512 * 16 *
+ * floor(bytes / 16 / grid / 512) * reps.  sink_dev: device uint32[1024] the
+ * kernel may write (keeps the loads; normally untouched).  *kernel_ms: launch
+ * time (HIP events on hip_stream).  KIE_ERR_ARG for a bad depth or pointer,
+ * KIE_ERR_CAPACITY when the buffer gives a work-group fewer than `depth` passes. */
+kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, int32_t reps,
+                            uint32_t* sink_dev, void* hip_stream, float* kernel_ms);
 
 #ifdef __cplusplus
 }

@@ -79,6 +79,15 @@ __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Race test: the chosen work-group holds back every hand-off publication by
+// a fixed time (the host sets it), so consumers see its words arrive late.
+__device__ __forceinline__ void publish_delay(CParams& P) {
+  if ((int)blockIdx.x == P.delay_wg) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < P.delay_ticks) __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 // Issue the first kDepth vectors of the next GEMV stage into the ring.
 __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np);
 
@@ -481,6 +490,7 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
   };
   if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, l > 0, tr, slot)) return false;
   uint32_t* dst = X + P.xl.qkv + (size_t)l * N;
+  publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads) xst32(dst + r0 + r, __float_as_uint(c.s.yv[r]));
   stamp(tr, slot, 3, c.t);
   return true;
@@ -670,6 +680,7 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
       stamp(tr, slot, 2, t);
       __syncthreads();
       // fold the groups and publish (m, l, o) of heads hb .. hb+HB-1 for this chunk
+      publish_delay(P);
       uint32_t* att = X + P.xl.att;
       for (int idx = t; idx < HB * hd; idx += kThreads) {
         const int h = idx / hd, e = idx % hd;
@@ -756,6 +767,7 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
     ls = sum64_tail(ls * f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = sum64_tail(o[e] * f);
+    if (ok) publish_delay(P);
     if (lane == 63 && ok) {
       const float inv = 1.0f / ls;
       uint32_t* dst = X + P.xl.a + (size_t)l * hq * hd + (size_t)h * hd + sl * 8;
@@ -788,6 +800,7 @@ __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* 
   const StagePlan np = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, false, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xmid + (size_t)l * d;
+  publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
   ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
@@ -815,6 +828,7 @@ __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32
   const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.h + (size_t)l * F;
+  publish_delay(P);
   for (int f = c.t; f < nf; f += kThreads) {
     const float gt = c.s.yv[f], up = c.s.yv[nf + f];
     xst32(dst + f0 + f, __float_as_uint(gt / (1.0f + expf(-gt)) * up));
@@ -843,6 +857,7 @@ __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t
                                    : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VF>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xout + (size_t)l * d;
+  publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
   ring_prefetch(ring, np);
@@ -1080,6 +1095,7 @@ __device__ KIE_INLINE bool group_merge(const Params* Pp, char* smem, uint32_t* X
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) k8[w] = lk[w * kCand + lane];
     merge_tree<kWaves>(k8, lane, group_list_desc(g));
+    publish_delay(P);
     xst64(X + P.xl.cand2 + ((size_t)g * kCand + lane) * 2, pack2f(key_value(k8[0]), __int_as_float(key_index(k8[0]))));
   }
   __syncthreads();
@@ -1185,6 +1201,7 @@ __device__ KIE_INLINE bool sampled_token(const Params* Pp, char* smem, uint32_t*
   if ((int)blockIdx.x < ((int)gridDim.x + 7) / 8 && !group_merge(Pp, smem, X)) return false;
   if (blockIdx.x == 0) {
     if (!gather_sample(Pp, smem, X, pos, tok, tr)) return false;
+    publish_delay(cparams(Pp));
     if (threadIdx.x == 0) xst64(X + cparams(Pp).xl.stok, pack2f(__int_as_float(tok), 0.f));
     return true;
   }
@@ -1234,8 +1251,10 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
       bi = v0 + r;
     }
   }
-  if (P.samp_k > 0)
+  if (P.samp_k > 0) {
+    publish_delay(P);
     publish_candidates(c.s.yv, v1 - v0, v0, X + P.xl.cand + (size_t)c.wg * kCand * 2, c.wg, c.t, c.s.red);
+  }
   block_argmax(bv, bi, c.s, c.t);
   best_v = bv;
   best_i = bi;
@@ -1244,12 +1263,15 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
 }
 
 // Reset this work-group's share of exchange set `Xr` to the NaN pattern, with
-// threads [t_lo, kThreads).  Xr is the set of the previous step: every
-// work-group finished reading it before publishing its partial of that step,
-// and this work-group has consumed all those partials.  The next writes into
-// Xr happen two steps later, by work-groups that have seen this work-group's
-// next partial, which is published only after these stores were performed
-// stores.
+// threads [t_lo, kThreads).  Xr is the set of step s-1 while this is step s.
+// Why no work-group still reads it: every work-group owns at least one row of
+// every vector a step-s hand-off polls (the host keeps the grid at most
+// d_model and d_ffn wide), so this work-group could only reach step s's
+// recycling after every other work-group published step-s words, i.e. after
+// each had left step s-1 -- including the argmax and sampling words it reads
+// in step s-1's tail, after publishing its own partial.  Set Xr is written
+// again at step s+2, by work-groups that have gathered this work-group's step
+// s+1 partial, which is published only after these stores were performed.
 __device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr, int nch_prev, int t_lo,
                                      uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
@@ -1354,6 +1376,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     }
     // publish this step's partial once everything this step wrote is performed
     drain_stores();
+    publish_delay(cparams(Pp));
     __syncthreads();
     if (t == 0 && wg != Pp->withhold_wg) xst64(X + Pp->xl.arg + 2 * wg, pack2f(bv, __int_as_float(bi)));
     // the upper half of the work-group recycles the previous step's exchange

@@ -66,6 +66,10 @@ struct Params {
   const int* forced;          // prompt tokens (prefill) or null
   // launch
   int pos0, n_steps, eos_id, in_tok, abort_after, lm_last_only, withhold_wg;
+  // race test: work-group delay_wg waits delay_ticks (100 MHz) before it
+  // publishes any hand-off output (-1: off)
+  int delay_wg;
+  uint64_t delay_ticks;
   // sampling: samp_k = 0 greedy; else top-k (<= kCand), log2(e) / temperature,
   // nucleus mass, Philox4x32-10 key
   int samp_k;

@@ -25,6 +25,7 @@ const void* monokernel_fn_bf16_g2(int vd, int vf);
 const void* monokernel_fn_bf16_g4(int vd, int vf);
 const void* monokernel_fn_bf16_g8(int vd, int vf);
 const void* gemv_probe_fn(int dtype);
+const void* stream_probe_fn(int depth);
 hipError_t launch_fill(uint32_t* p, uint64_t n, uint32_t v, hipStream_t st);
 }  // namespace kie
 
@@ -195,6 +196,8 @@ struct kie_engine {
   uint64_t timeout = kDefaultTimeout;
   int abort_after = -1;
   int withhold_wg = -1;
+  int delay_wg = -1;          // race test: work-group whose publications are delayed
+  uint64_t delay_ticks = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float last_ms = 0.f;
   int last_steps = 0;
@@ -271,6 +274,9 @@ static kie_status hip_fail(hipError_t e, const char* what) {
 // and the index arithmetic stays within 32 bits.
 static bool grid_fits(const kie_config& c, const Layout& lay, int grid) {
   if (grid < 1 || grid > kMaxWG || grid > kThreads / 2) return false;
+  // every work-group owns a row of each vector a hand-off polls: the
+  // exchange-set recycling relies on it
+  if (grid > c.d_model || grid > c.d_ffn) return false;
   auto fits = [&](long long rows, int K) {
     const int vpr = K / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
     return rows <= kYCap && rows * nwr <= kRedCap;
@@ -490,6 +496,8 @@ static Params base_params(const kie_engine* e) {
   P.tok_out = reinterpret_cast<int*>(e->ws + e->lay.tok);
   P.abort_after = -1;
   P.withhold_wg = e->withhold_wg;
+  P.delay_wg = e->delay_wg;
+  P.delay_ticks = e->delay_ticks;
   P.timeout = e->timeout;
   P.trace = e->trace;
   P.trace_step = e->trace_step;
@@ -736,6 +744,35 @@ extern "C" kie_status kie_set_withhold(kie_engine* e, int32_t wg) {
   return KIE_OK;
 }
 
+extern "C" kie_status kie_set_delay(kie_engine* e, int32_t wg, uint64_t ticks) {
+  if (!e || wg < -1) return KIE_ERR_ARG;
+  if (ticks > 100000000ull) return KIE_ERR_ARG;  // at most 1 s per publication
+  e->delay_wg = wg;
+  e->delay_ticks = ticks;
+  return KIE_OK;
+}
+
+// After a launch of S >= 2 completed steps, the exchange sets of steps S-2
+// and S-3 (set indices (S-2) % 3 and S % 3) must hold the NaN pattern in every
+// word: the first was recycled during step S-1, the second during step S-2
+// (or never used).  Counts the words that do not.
+extern "C" kie_status kie_check_idle_sets(const kie_engine* e, uint64_t* dirty_words) {
+  if (!e || !dirty_words) return KIE_ERR_ARG;
+  const int S = e->last_steps;
+  if (S < 2) return KIE_ERR_STATE;
+  const size_t words = e->lay.xl.words;
+  std::vector<uint32_t> host(words);
+  uint64_t dirty = 0;
+  for (int set : {(S - 2) % kRingSets, S % kRingSets}) {
+    const char* src = e->ws + e->lay.xch + (size_t)set * words * 4;
+    KIE_HIP(hipMemcpyAsync(host.data(), src, words * 4, hipMemcpyDeviceToHost, e->stream));
+    KIE_HIP(hipStreamSynchronize(e->stream));
+    for (uint32_t w : host) dirty += w != kSent;
+  }
+  *dirty_words = dirty;
+  return KIE_OK;
+}
+
 extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
                                      const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
                                      void* hip_stream, float* kernel_ms) {
@@ -776,6 +813,39 @@ extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t co
   (void)hipEventDestroy(a);
   (void)hipEventDestroy(b);
   if (he != hipSuccess) return hip_fail(he, "gemv probe");
+  if (kernel_ms) *kernel_ms = ms;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, int32_t reps,
+                                       uint32_t* sink_dev, void* hip_stream, float* kernel_ms) {
+  if (!buf_dev || !sink_dev || reps < 1 || (reinterpret_cast<uintptr_t>(buf_dev) & 15)) return KIE_ERR_ARG;
+  const void* fn = stream_probe_fn(depth);
+  if (!fn) return KIE_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  int dev = 0;
+  KIE_HIP(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  KIE_HIP(hipGetDeviceProperties(&prop, dev));
+  const int grid = prop.multiProcessorCount < kMaxWG ? prop.multiProcessorCount : kMaxWG;
+  // every work-group reads whole passes of 512 vectors, at least `depth` of them
+  if (bytes / 16 < (uint64_t)grid * kThreads * (uint64_t)depth) return KIE_ERR_CAPACITY;
+  const uint4* buf = reinterpret_cast<const uint4*>(buf_dev);
+  uint64_t nvec = bytes / 16;
+  int rp = reps;
+  void* args[] = {&buf, &nvec, &rp, &sink_dev};
+  hipEvent_t a, b;
+  KIE_HIP(hipEventCreate(&a));
+  KIE_HIP(hipEventCreate(&b));
+  hipError_t he = hipEventRecord(a, st);
+  if (he == hipSuccess) he = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, st);
+  if (he == hipSuccess) he = hipEventRecord(b, st);
+  if (he == hipSuccess) he = hipStreamSynchronize(st);
+  float ms = 0.f;
+  if (he == hipSuccess) he = hipEventElapsedTime(&ms, a, b);
+  (void)hipEventDestroy(a);
+  (void)hipEventDestroy(b);
+  if (he != hipSuccess) return hip_fail(he, "stream probe");
   if (kernel_ms) *kernel_ms = ms;
   return KIE_OK;
 }

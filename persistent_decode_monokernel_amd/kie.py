@@ -94,9 +94,13 @@ SIGNATURES = {
     "kie_set_poll_timeout": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64]),
     "kie_set_abort_after": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_withhold": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_delay": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64]),
+    "kie_check_idle_sets": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64)]),
     "kie_trace_words": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kie_set_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
     "kie_check_tiling": (ctypes.c_int, [ctypes.POINTER(kie_config), ctypes.c_int32, ctypes.c_int32]),
+    "kie_stream_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
     "kie_gemv_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
@@ -336,6 +340,16 @@ class Engine:
     def set_withhold(self, wg: int):
         _check(lib().kie_set_withhold(self._h, int(wg)), "kie_set_withhold")
 
+    def set_delay(self, wg: int, ticks: int):
+        """Race test: work-group wg holds back each hand-off publication by ticks (100 MHz)."""
+        _check(lib().kie_set_delay(self._h, int(wg), int(ticks)), "kie_set_delay")
+
+    def idle_sets_dirty_words(self) -> int:
+        """Words of the two idle exchange sets that are not the NaN pattern after the last launch."""
+        n = ctypes.c_uint64(0)
+        _check(lib().kie_check_idle_sets(self._h, ctypes.byref(n)), "kie_check_idle_sets")
+        return int(n.value)
+
 
 def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None) -> Tuple[torch.Tensor, float]:
     """y[i] = W[i % n_copies] @ x[i] in one persistent launch.  Returns (y fp32, kernel ms)."""
@@ -348,3 +362,19 @@ def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None) -> Tuple[torch.Ten
                                 ctypes.c_void_p(_dptr(y)), x.shape[0], dtype,
                                 ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(ms)), "kie_gemv_probe")
     return y, ms.value
+
+
+def stream_probe(buf: torch.Tensor, depth: int = 3, reps: int = 4, stream=None) -> Tuple[float, int]:
+    """Read-stream probe over the bytes of a device tensor.  Returns (kernel ms,
+    bytes read)."""
+    sink = torch.zeros(1024, dtype=torch.int32, device=buf.device)
+    ms = ctypes.c_float(0)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().kie_stream_probe(ctypes.c_void_p(_dptr(buf)), nbytes, int(depth), int(reps),
+                                  ctypes.c_void_p(_dptr(sink)), ctypes.c_void_p(_stream_handle(stream)),
+                                  ctypes.byref(ms)), "kie_stream_probe")
+    grid = torch.cuda.get_device_properties(buf.device).multi_processor_count
+    grid = min(grid, 1024)
+    npass = nbytes // 16 // grid // 512
+    read = grid * 512 * 16 * (npass // depth * depth) * reps  # whole rounds of `depth` passes
+    return ms.value, read

@@ -5,6 +5,7 @@ time, written from the model definition (not from the oracle's tensor code):
 no matrices, no broadcasting, no library softmax.  Used only by the tests.
 """
 import math
+import struct
 
 
 def _f(t):
@@ -44,8 +45,24 @@ def rot(vec, pos, base):
     return out
 
 
-def model_logits(w, shape, tokens):
-    """Logits at every position of ``tokens`` (a full causal pass), as lists."""
+def round_store(x, fmt):
+    """x rounded to a 16-bit storage format ("bf16" or "f16") and back: first to
+    the nearest float32, then to the nearest 16-bit value, ties to even (the
+    route a float64 -> float32 -> 16-bit conversion takes)."""
+    f = struct.unpack("<f", struct.pack("<f", x))[0]
+    if fmt == "f16":
+        return struct.unpack("<e", struct.pack("<e", f))[0]
+    u = struct.unpack("<I", struct.pack("<f", f))[0]
+    lsb = (u >> 16) & 1
+    u = ((u + 0x7FFF + lsb) >> 16) << 16
+    return struct.unpack("<f", struct.pack("<I", u & 0xFFFFFFFF))[0]
+
+
+def model_logits(w, shape, tokens, store=None):
+    """Logits at every position of ``tokens`` (a full causal pass), as lists.
+
+    store: None keeps cached keys and values exact; "bf16" / "f16" rounds each
+    cached element (keys after rotation) to that format, and nothing else."""
     s = shape
     E = _f(w["tok_emb"])
     layers = [{k: _f(v) for k, v in lw.items()} for lw in w["layers"]]
@@ -64,8 +81,13 @@ def model_logits(w, shape, tokens):
             k = mv(lw["wk"], xn)
             v = mv(lw["wv"], xn)
             for g in range(hkv):
-                Kc[l][g].append(rot(k[g * hd:(g + 1) * hd], pos, s.rope_base))
-                Vc[l][g].append(v[g * hd:(g + 1) * hd])
+                kr = rot(k[g * hd:(g + 1) * hd], pos, s.rope_base)
+                vr = v[g * hd:(g + 1) * hd]
+                if store is not None:
+                    kr = [round_store(e, store) for e in kr]
+                    vr = [round_store(e, store) for e in vr]
+                Kc[l][g].append(kr)
+                Vc[l][g].append(vr)
             att = []
             for h in range(hq):
                 g = h // group

@@ -240,6 +240,61 @@ def test_cache_storage_dtype_rounds_each_appended_row(dt):
     assert torch.allclose(full[len(prompt):], lgs, atol=1e-12)
 
 
+@pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
+def test_cache_storage_dtype_matches_bruteforce(dt):
+    """The 16-bit cache mode rounds exactly the cached keys (after rotation) and
+    values, and nothing else: the scalar-loop model rounding only those
+    elements gives the same logits at every position.  Rounding the query, the
+    attention output or the key before rotation moves them well past 1e-11."""
+    w = _mini_weights(seed=23, std=0.5)
+    toks = [4, 11, 0, 19, 7, 7, 2, 13]
+    assert _store_pin_error(w, toks, dt) < 1e-11
+
+
+def _store_pin_error(w, toks, dt):
+    fmt = "bf16" if dt == torch.bfloat16 else "f16"
+    lg = oracle.forward(w, MINI, toks, oracle.KVCache(MINI.n_layers, MINI.n_kv_heads, MINI.head_dim, store_dtype=dt))
+    ref = torch.tensor(BF.model_logits(w, MINI, toks, store=fmt), dtype=F64)
+    return float((lg - ref).abs().max())
+
+
+def _rounded(t):
+    return t.to(torch.bfloat16).to(F64)
+
+
+def _attention_rounds_query(q, K, V, q_pos0):
+    return _ORIG_ATT(_rounded(q), K, V, q_pos0)
+
+
+def _attention_rounds_output(q, K, V, q_pos0):
+    return _rounded(_ORIG_ATT(q, K, V, q_pos0))
+
+
+def _rope_rounds_key_input(x, cos, sin):
+    if x.shape[-2] == MINI.n_kv_heads:  # the key projection (the query has more heads)
+        x = _rounded(x)
+    return _ORIG_ROPE(x, cos, sin)
+
+
+_ORIG_ROPE = D.apply_rope
+STORE_MUTATIONS = {
+    "query_rounded": ("attention", _attention_rounds_query),
+    "attention_output_rounded": ("attention", _attention_rounds_output),
+    "key_rounded_before_rotation": ("apply_rope", _rope_rounds_key_input),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STORE_MUTATIONS))
+def test_cache_storage_pin_catches_extra_rounding(name, monkeypatch):
+    w = _mini_weights(seed=23, std=0.5)
+    toks = [4, 11, 0, 19, 7, 7, 2, 13]
+    assert _store_pin_error(w, toks, torch.bfloat16) < 1e-11
+    attr, fn = STORE_MUTATIONS[name]
+    monkeypatch.setattr(D, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    assert _store_pin_error(w, toks, torch.bfloat16) > 1e-6, f"planted mistake {name} went unnoticed"
+
+
 def test_teacher_forced_from_imported_cache():
     shape = synth.small_shape(n_layers=2, d_model=32, n_heads=4, n_kv_heads=4, head_dim=8, d_ffn=64, vocab=50)
     w = synth.make_weights(shape, 8, std=0.2)

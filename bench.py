@@ -345,34 +345,50 @@ def timeline(wl, step: int = 10, n_decode: int = 32, samp=None):
           f"= {tot_wait / tot_span:.0%}")
 
 
-def cpu_baseline(shape, w_gpu, n_prompt: int, budget_s: float = 15.0):
-    """Time the CPU oracle's incremental decode (as it stands) on a bounded sample."""
-    import torch
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    import oracle
+
+def cpu_baseline(shape, w_gpu, n_prompt: int, budget_s: float = 15.0):
+    """Time the fp32 C++ oracle (as it stands) on a bounded sample: incremental
+    greedy decode steps after a synthetic cache of the workload's prompt length."""
+    from oracle.cpu_decoder import CpuDecoder
     from persistent_decode_monokernel_amd import synth
 
-    log("cpu baseline: copying weights to host")
-    wc = synth.weights_to(w_gpu, "cpu")
+    nproc = len(os.sched_getaffinity(0))
+    threads = min(nproc, 16)  # one GPU's share of the host
+    log(f"cpu baseline: widening weights to host fp32 ({threads} threads of {nproc})")
+    dec = CpuDecoder(shape, w_gpu, max_seq=n_prompt + 64, n_threads=threads)
     k, v = synth.make_kv(shape, n_prompt, seed=11)  # context of the workload's prompt length
-    cache = oracle.KVCache.from_tensors(k, v)
-    tok = 1
+    dec.set_cache(k, v)
+    del k, v
     t0 = time.time()
-    oracle.forward(wc, shape, [tok], cache)
+    tok, _ = dec.step(1, want_logits=False)
     first = time.time() - t0
-    n = max(1, min(16, int(budget_s / max(first, 1e-3)) - 1))
+    n = max(1, min(60, int(budget_s / max(first, 1e-3)) - 1))
     log(f"cpu baseline: first token {first:.2f}s, timing {n} more")
     t0 = time.time()
     for _ in range(n):
-        oracle.forward(wc, shape, [tok], cache)
+        tok, _ = dec.step(tok, want_logits=False)
     el = time.time() - t0
+    dec.close()
     return {
         "value": n / el,
         "unit": "tokens/s",
-        "cores": torch.get_num_threads(),
-        "kind": "oracle",
-        "sample": f"{n} incremental decode steps of the same model (fp64 oracle) after a synthetic "
-                  f"{n_prompt}-position KV cache, positions {n_prompt + 1}..{n_prompt + n}",
+        "cores": threads,
+        "nproc": nproc,
+        "cpu_model": _cpu_model(),
+        "kind": "oracle (fp32 C++, std::thread over matrix rows)",
+        "sample": f"{n} incremental greedy decode steps of the same model after a synthetic "
+                  f"{n_prompt}-position KV cache (one untimed step), positions {n_prompt + 1}..{n_prompt + n} "
+                  f"counted from 0",
     }
 
 

@@ -10,6 +10,25 @@ LOGIT_TOL = 2e-2     # max |logit_gpu - logit_oracle| over vocab and steps
 MARGIN = 0.05        # tokens must agree where the oracle's top1 - top2 exceeds this
 
 
+KV_TOL = 2e-2        # max |cache row - oracle row| beyond one storage ulp (values ~N(0, 1))
+
+
+def stored_rows_excess(gpu: torch.Tensor, ora: torch.Tensor) -> float:
+    """How far two caches of rows stored in a 16-bit format differ beyond one
+    ulp of that format: max(|g - o| - ulp) over elements, ulp the format's
+    spacing at the larger of |g|, |o|.  Each side rounds its own unrounded
+    value (fp32 on the GPU, fp64 in the oracle) to the format; when those lie
+    on either side of a rounding boundary the stored values differ by one ulp
+    however close the unrounded values were, so correctly rounded rows of
+    values within e of each other differ by at most e + 1 ulp."""
+    mant = {torch.float16: 10, torch.bfloat16: 7}[gpu.dtype]
+    g = gpu.detach().to("cpu", torch.float64)
+    o = ora.detach().to("cpu", torch.float64)
+    _, e = torch.frexp(torch.maximum(g.abs(), o.abs()))  # |x| in [2^(e-1), 2^e)
+    ulp = torch.ldexp(torch.ones_like(g), e - 1 - mant)
+    return float(((g - o).abs() - ulp).max())
+
+
 def top2_margin(logits: torch.Tensor) -> torch.Tensor:
     """top1 - top2 per row."""
     v = torch.topk(logits, 2, dim=-1).values

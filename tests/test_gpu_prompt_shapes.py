@@ -24,11 +24,10 @@ import torch
 
 import oracle
 from persistent_decode_monokernel_amd import kie, synth
-from tests.gpu_util import check_tokens_and_logits, cpu_copy
+from tests.gpu_util import KV_TOL, check_tokens_and_logits, cpu_copy, stored_rows_excess
 
 pytestmark = pytest.mark.gpu
 
-KV_TOL = 2e-2  # max |cache row - oracle row|; bf16 rows: the oracle's cache stores bf16 too
 
 S2 = dataclasses.replace(synth.M2B, name="2b_2layers", n_layers=2)
 S8 = dataclasses.replace(synth.M8B, name="8b_2layers", n_layers=2)
@@ -69,10 +68,11 @@ def run_prompt(shape, workload: str, n_decode: int, seg: int = 1024):
     ora = torch.cat(rows)
     print(f"[prompt shapes] oracle pass {time.time() - t0:.1f}s", flush=True)
     err, dec = check_tokens_and_logits(seq, gpu, ora, f"{shape.name} P={P}")
-    kerr = max((k[l].double() - cache.k[l][:, :P]).abs().max().item() for l in range(shape.n_layers))
-    verr = max((v[l].double() - cache.v[l][:, :P]).abs().max().item() for l in range(shape.n_layers))
+    # the oracle's cache holds the rows rounded to the storage format as well
+    kerr = max(stored_rows_excess(k[l], cache.k[l][:, :P]) for l in range(shape.n_layers))
+    verr = max(stored_rows_excess(v[l], cache.v[l][:, :P]) for l in range(shape.n_layers))
     print(f"{shape.name} P={P}: max |dlogit| {err:.2e} (decisive {dec}/{len(seq)}), "
-          f"cache |dk| {kerr:.2e} |dv| {verr:.2e}")
+          f"cache |dk|, |dv| beyond one storage ulp {kerr:.2e}, {verr:.2e}")
     assert kerr <= KV_TOL and verr <= KV_TOL, (kerr, verr)
 
 

@@ -179,10 +179,11 @@ def gemv_probe_bench(n_copies: int = 16):
             torch.cuda.empty_cache()
 
 
+HANDOFFS = {"nan": 0, "counters": 1}  # kie.KIE_HANDOFF_NAN_POLL, kie.KIE_HANDOFF_COUNTERS
 STREAM_BYTES = 1 << 30  # 1 GiB: four times the memory-side cache
 
 
-def stream_peak(depths=(3,), reps: int = 4, verbose: bool = False) -> float:
+def stream_peak(depths=(3,), reps: int = 16, verbose: bool = False) -> float:
     """Read-stream ceiling (GB/s): the best of kie_stream_probe over `depths`
     (non-temporal dwordx4 loads in flight per thread) on a 1 GiB buffer."""
     import torch
@@ -202,6 +203,53 @@ def stream_peak(depths=(3,), reps: int = 4, verbose: bool = False) -> float:
     del buf
     torch.cuda.empty_cache()
     return best
+
+
+def ablation(name: str, steps: int = 64):
+    """Launch tax and hand-off protocol: the same greedy decode of `steps` tokens
+    after the workload's prompt, run (a) as the persistent kernel with NaN-polled
+    hand-offs, (b) as the persistent kernel with atomic arrival counters, (c) as
+    one launch per stage per token from a host loop, (d) as those launches
+    replayed from a HIP graph.  Kernel time per token from HIP events on the
+    engine stream; `floor` = the token's algorithmic bytes at the measured
+    read-stream ceiling, and `sync share` = 1 - floor / time, the part of the
+    token not explained by streaming its bytes."""
+    import torch
+
+    from persistent_decode_monokernel_amd import kie, synth
+
+    wl = synth.WORKLOADS[name]
+    s = wl.shape
+    dev = torch.device("cuda:0")
+    w = synth.make_weights(s, wl.weight_seed, device=dev)
+    prompt = synth.make_prompt(s, wl.n_prompt, wl.prompt_seed).tolist()
+    peak = stream_peak()
+    nbytes = bytes_per_launch(s, wl.n_prompt, steps)
+    floor_us = nbytes / steps / (peak * 1e9) * 1e6
+    configs = [("persistent, NaN-polled hand-offs", kie.KIE_LAUNCH_PERSISTENT, kie.KIE_HANDOFF_NAN_POLL),
+               ("persistent, atomic arrival counters", kie.KIE_LAUNCH_PERSISTENT, kie.KIE_HANDOFF_COUNTERS),
+               ("one launch per stage, host loop", kie.KIE_LAUNCH_PER_STAGE, kie.KIE_HANDOFF_NAN_POLL),
+               ("one launch per stage, HIP graph", kie.KIE_LAUNCH_PER_STAGE_GRAPH, kie.KIE_HANDOFF_NAN_POLL)]
+    ref = None
+    for label, mode, handoff in configs:
+        eng = kie.Engine(s, max_seq=wl.n_prompt + 2 * steps + 1, device=dev)
+        eng.load_weights(w)
+        eng.set_handoff(handoff)
+        eng.set_launch_mode(mode)
+        eng.prefill(prompt)
+        eng.decode(8)  # warm-up in the same mode
+        toks, _, st = eng.decode(steps)
+        ms = eng.info().last_kernel_ms
+        eng.close()
+        if ref is None:
+            ref = toks
+        us = ms * 1e3 / steps
+        print(json.dumps({"ablation": label, "workload": name, "steps": steps, "us_per_token": us,
+                          "tokens_per_s": 1e6 / us, "launches_per_token": 1.0 / steps if mode == 0 else
+                          6 * s.n_layers + 2, "floor_us": floor_us, "sync_share": 1.0 - floor_us / us,
+                          "same_tokens": toks == ref, "status": st}), flush=True)
+    del w
+    torch.cuda.empty_cache()
 
 
 def ttft_bench(name: str, modes=("auto", "decode_loop"), chunks=(0,)):
@@ -276,7 +324,7 @@ def grid_sweep(name: str, grids, steps=None):
 STAGES = ("qkv", "attention", "merge", "wo", "gate/up", "down")
 
 
-def timeline(wl, step: int = 10, n_decode: int = 32, samp=None):
+def timeline(wl, step: int = 10, n_decode: int = 32, samp=None, handoff: int = 0, split: bool = False):
     """Per-token timeline of one decode step (the step-th of a kie_decode(n_decode)
     launch after the workload's prompt): for every stage, the median over
     work-groups of the time from stage entry until its input had arrived (the
@@ -295,6 +343,8 @@ def timeline(wl, step: int = 10, n_decode: int = 32, samp=None):
     P = wl.n_prompt
     eng = kie.Engine(s, max_seq=P + n_decode, device=dev)
     eng.load_weights(w)
+    eng.set_handoff(handoff)
+    eng.set_split(split)
     if samp is not None:
         eng.set_sampling(samp[0], int(samp[1]), samp[2], wl.prompt_seed)
     eng.prefill(synth.make_prompt(s, P, wl.prompt_seed).tolist())
@@ -317,7 +367,9 @@ def timeline(wl, step: int = 10, n_decode: int = 32, samp=None):
         waits, comps, tails, spans, busy = [], [], [], [], []
         for l in range(1, L):
             x = tr[6 * l + k]
-            ok = (x[:, 3] - x[:, 0]) > (0.5 if k in (1, 2) else -1.0)  # attention/merge: work-groups with units
+            # work-groups that ran the stage (a stage a work-group's role skips is not stamped);
+            # attention/merge: those with units
+            ok = (x[:, 0] > 0) & ((x[:, 3] - x[:, 0]) > (0.5 if k in (1, 2) else -1.0))
             x = x[ok]
             busy.append(len(x))
             done = x[:, 2] if k != 2 else x[:, 3]  # the merge stamps no separate "arithmetic done"
@@ -408,6 +460,12 @@ def main():
                     help="only summarise rocprofv3 --pmc counter CSVs")
     ap.add_argument("--copy-bytes", type=int, default=0, help="bytes read (= written) by the copy probe")
     ap.add_argument("--gemv", action="store_true", help="only run the isolated GEMV probe workload")
+    ap.add_argument("--handoff", default="nan", choices=sorted(HANDOFFS),
+                    help="hand-off protocol: NaN-polled data (default) or atomic arrival counters (comparison)")
+    ap.add_argument("--split", action="store_true",
+                    help="role split: attention block and feed-forward block on separate halves of the grid")
+    ap.add_argument("--ablation", action="store_true",
+                    help="only compare the persistent kernel (NaN polls, arrival counters) with one launch per stage")
     ap.add_argument("--stream", action="store_true",
                     help="only run the read-stream probe (1, 2, 3, 4, 6, 8 loads in flight per thread)")
     ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")
@@ -442,6 +500,9 @@ def main():
     if args.stream:
         stream_peak(depths=(1, 2, 3, 4, 6, 8), verbose=True)
         return
+    if args.ablation:
+        ablation(args.workload, args.steps or 64)
+        return
     if args.grid_sweep:
         grid_sweep(args.workload, args.grid_sweep, args.steps)
         return
@@ -451,7 +512,8 @@ def main():
     if args.timeline is not None:
         from persistent_decode_monokernel_amd import synth
 
-        timeline(synth.WORKLOADS[args.workload], step=args.timeline, samp=args.sampling)
+        timeline(synth.WORKLOADS[args.workload], step=args.timeline, samp=args.sampling,
+                 handoff=HANDOFFS[args.handoff], split=args.split)
         return
 
     import torch
@@ -470,6 +532,8 @@ def main():
     prompt = synth.make_prompt(s, P, wl.prompt_seed).tolist()
     eng = kie.Engine(s, max_seq=P + max(K, Wm, 1), device=dev)
     eng.load_weights(w)
+    eng.set_handoff(HANDOFFS[args.handoff])
+    eng.set_split(args.split)
     samp = None
     if args.sampling is not None:
         samp = {"temperature": args.sampling[0], "top_k": int(args.sampling[1]), "top_p": args.sampling[2],
@@ -519,7 +583,9 @@ def main():
             "workload": f"{wl.name}: {s.n_layers}L d{s.d_model} GQA {s.n_heads}/{s.n_kv_heads}x{s.head_dim} "
                         f"F{s.d_ffn} V{s.vocab}, prompt {P}, decode {K}, batch 1, "
                         + ("greedy" if samp is None else
-                           f"sampled (T {samp['temperature']}, top-k {samp['top_k']}, top-p {samp['top_p']})"),
+                           f"sampled (T {samp['temperature']}, top-k {samp['top_k']}, top-p {samp['top_p']})")
+                        + ("" if args.handoff == "nan" else f", {args.handoff} hand-offs")
+                        + (", role split" if args.split else ""),
             "prompt": P,
             "decode_tokens": K,
             "batch": 1,

@@ -318,10 +318,59 @@ kie_status kie_set_withhold(kie_engine* e, int32_t wg);
 
 /* Race test: the next persistent launches make work-group `wg` wait `ticks`
  * of the 100 MHz counter (at most 1e8) before each of its hand-off
- * publications (QKV, attention partials, merge, Wo, gate/up, down), so every
+ * publications (QKV, attention partials, merge, Wo, gate/up, down, the LM
+ * head's argmax partial and sampling lists, the sampled token), so every
  * consumer of its words sees them arrive late.  The results must not change
  * (tests compare tokens and logits bit for bit).  wg = -1 turns it off. */
 kie_status kie_set_delay(kie_engine* e, int32_t wg, uint64_t ticks);
+
+/* Hand-off protocol of the next persistent launches (a measurement switch).
+ * Source: revietech.ru, "Kog vyzhimayet maksimum iz GPU: 3000 tokenov/s",
+ * section "Chto takoye monokernel", the synchronisation paragraph: work-groups
+ * poll buffers pre-filled with NaN instead of counting arrivals with atomics.
+ *   KIE_HANDOFF_NAN_POLL (default): the data is its own flag; a consumer polls
+ *     exactly the words it needs.
+ *   KIE_HANDOFF_COUNTERS: the alternative that passage sets aside, for
+ *     comparison.  After each stage every work-group waits until its own
+ *     stores are performed and adds one to the stage's counter (an agent-scope
+ *     atomic); consumers wait until all work-groups have arrived, then read.
+ * Results are bit-identical in both modes.  KIE_ERR_ARG for another mode. */
+#define KIE_HANDOFF_NAN_POLL 0
+#define KIE_HANDOFF_COUNTERS 1
+kie_status kie_set_handoff(kie_engine* e, int32_t mode);
+
+/* How kie_decode runs its steps (a measurement switch).
+ * Source: revietech.ru, "Kog vyzhimayet maksimum iz GPU: 3000 tokenov/s",
+ * section "Chto takoye monokernel": every separate kernel launch costs a fixed
+ * setup time, which the single resident kernel removes.
+ *   KIE_LAUNCH_PERSISTENT (default): one persistent launch for all steps.
+ *   KIE_LAUNCH_PER_STAGE: the same stage code as one launch per stage per
+ *     token (6 per layer, the LM head, the token), queued from a host loop.
+ *   KIE_LAUNCH_PER_STAGE_GRAPH: the same launches captured once into a HIP
+ *     graph and replayed as one graph launch (capture before the timing).
+ * The per-stage modes take greedy decode with eos_id < 0 and no fault
+ * injection (else KIE_ERR_UNSUPPORTED); tokens and logits equal the
+ * persistent kernel's bit for bit.  KIE_ERR_ARG for another mode. */
+#define KIE_LAUNCH_PERSISTENT 0
+#define KIE_LAUNCH_PER_STAGE 1
+#define KIE_LAUNCH_PER_STAGE_GRAPH 2
+kie_status kie_set_launch_mode(kie_engine* e, int32_t mode);
+
+/* Work-group roles of the next persistent launches.
+ * Source: revietech.ru, "Kog vyzhimayet maksimum iz GPU: 3000 tokenov/s",
+ * sections "Chto takoye monokernel" (decode is bound by memory bandwidth and
+ * by synchronisation) and "Arkhitektura i osobennosti" (the kernel chooses
+ * which compute units do what).
+ *   on = 0 (default): every stage runs on the whole grid.
+ *   on = 1: the attention block (QKV, attention, merge, Wo) runs on half the
+ *     work-groups and the feed-forward block (gate/up, down) on the other
+ *     half, 16 of each per XCD; the LM head and the token on all.  Each half
+ *     issues the weights of its next stage while the other half works.
+ * Results are bit-identical either way.  KIE_ERR_UNSUPPORTED when the grid is
+ * not a multiple of 16 or the shape's rows do not tile half of it (also from
+ * a later kie_set_grid); KIE_ERR_ARG for another value.  The per-stage launch
+ * modes do not take it (KIE_ERR_UNSUPPORTED from kie_decode). */
+kie_status kie_set_split(kie_engine* e, int32_t on);
 
 /* Race test of the exchange-set recycling: after a launch that completed S >= 2
  * steps, the two exchange sets not used by its last step must hold the NaN

@@ -88,6 +88,24 @@ __device__ __forceinline__ void publish_delay(CParams& P) {
   }
 }
 
+// Work-group roles.  Without the role split every stage runs on the whole
+// grid.  With it, the attention block runs on the work-groups whose index has
+// bit 3 clear and the feed-forward block on those with it set: consecutive
+// work-groups go to the 8 XCDs in turn, so each XCD holds 16 of each.  While
+// one half works on its stages the other has already issued the weights of its
+// next stage, so its polls do not queue behind its own weight loads.  gw / gn:
+// index and count within the stage's group.
+__device__ __forceinline__ bool stage_group(CParams& P, int grp, int wg, int nb, int& gw, int& gn) {
+  if (!P.split) {
+    gw = wg;
+    gn = nb;
+    return true;
+  }
+  gw = ((wg >> 4) << 3) | (wg & 7);
+  gn = nb >> 1;
+  return ((wg >> 3) & 1) == grp;
+}
+
 // Issue the first kDepth vectors of the next GEMV stage into the ring.
 __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np);
 
@@ -135,6 +153,42 @@ __device__ __forceinline__ Sc stage_ctx(const Params* Pp, char* smem) {
 
 // Work-group-wide "any thread failed" with a barrier.
 __device__ __forceinline__ bool any_failed(bool failed) { return __syncthreads_or(failed ? 1 : 0) != 0; }
+
+// Arrival-counter hand-off (the comparison protocol; off by default).  Counter
+// k of an exchange set starts at kSent like every other word; each work-group
+// adds one once all its outputs of stage k are performed, so the counter reads
+// kSent + grid when every work-group has arrived.
+__device__ __forceinline__ void arrive(CParams& P, uint32_t* X, int k, int t) {
+  if (P.handoff != kHandoffCounters) return;
+  drain_stores();
+  __syncthreads();
+  if (t == 0)
+    __hip_atomic_fetch_add((KIE_GLOBAL uint32_t*)(X + P.xl.cnt + k), 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait (thread 0 polls, the work-group follows) until every work-group has
+// arrived at counter k.  Ends with a barrier in counter mode.
+__device__ __forceinline__ bool await_all(CParams& P, uint32_t* X, int k, const Watch& w, int t) {
+  if (P.handoff != kHandoffCounters) return true;
+  bool ok = true;
+  if (t == 0) {
+    const uint32_t* p = X + P.xl.cnt + k;
+    const uint32_t want = kSent + (uint32_t)gridDim.x;
+    if (xld32(p) != want) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      int n = 0;
+      for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        if (xld32(p) == want) break;
+        if (w.expired(t0, n)) {
+          ok = false;
+          break;
+        }
+      }
+    }
+  }
+  return !any_failed(!ok);
+}
 
 // Deterministic block sum (fixed order); every thread receives the total.
 __device__ __forceinline__ float block_sum(float v, float* misc, int t) {
@@ -474,15 +528,21 @@ __device__ __forceinline__ StagePlan plan_stage(CParams& P, int l, int st, int t
 template <int DT, int VD>
 __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  int gw, gn;
+  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
+    arrive(P, X, l * kStagesPerLayer + 0, c.t);
+    return true;
+  }
   const int slot = l * kStagesPerLayer + 0;
   stamp(tr, slot, 0, c.t);
-  CParams& P = c.P;
   const int hd = P.hd, d = P.d;
   const int nq = P.hq * hd, nk = P.hkv * hd;
   const int N = nq + 2 * nk;
-  const int r0 = split_lo(N, c.nb, c.wg), r1 = split_lo(N, c.nb, c.wg + 1);
-  const StagePlan pl = plan_stage(P, l, GS_QKV, c.t, c.wg, c.nb);
+  const int r0 = split_lo(N, gn, gw), r1 = split_lo(N, gn, gw + 1);
+  const StagePlan pl = plan_stage(P, l, GS_QKV, c.t, gw, gn);
   auto prep = [&]() -> bool {
+    if (l > 0 && !await_all(P, X, (l - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
     if (l > 0 && !poll_f32(X + P.xl.xout + (size_t)(l - 1) * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_ATTN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
@@ -492,6 +552,7 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
   uint32_t* dst = X + P.xl.qkv + (size_t)l * N;
   publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads) xst32(dst + r0 + r, __float_as_uint(c.s.yv[r]));
+  arrive(P, X, l * kStagesPerLayer + 0, c.t);
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -524,6 +585,11 @@ template <int DT, int G>
 __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
+  int gw, gn;
+  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
+    arrive(P, X, l * kStagesPerLayer + 1, c.t);
+    return true;
+  }
   const int slot = l * kStagesPerLayer + 1;
   stamp(tr, slot, 0, c.t);
   const int t = c.t;
@@ -545,7 +611,8 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
   float* go = gml + PP * HB * 2;                          // [PP][HB][hd] per-group o
   constexpr int APF = 2;                                  // passes prefetched into registers
   const uint32_t* src = X + P.xl.qkv + (size_t)l * N;
-  for (int u = c.wg; u < units; u += c.nb) {
+  if (gw < units && !await_all(P, X, l * kStagesPerLayer + 0, c.w, t)) return false;
+  for (int u = gw; u < units; u += gn) {
     const int g = u % hkv, ch = u / hkv;
     const int j0 = ch * CL, j1 = min(n, j0 + CL);
     const bool has_new = pos >= j0 && pos < j1;
@@ -717,6 +784,7 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
       __syncthreads();
     }
   }
+  arrive(P, X, l * kStagesPerLayer + 1, t);
   stamp(tr, slot, 3, t);
   return true;
 }
@@ -726,17 +794,23 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
 template <int DT>
 __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  int gw, gn;
+  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
+    arrive(P, X, l * kStagesPerLayer + 2, c.t);
+    return true;
+  }
   const int slot = l * kStagesPerLayer + 2;
   stamp(tr, slot, 0, c.t);
-  CParams& P = c.P;
   const int hd = P.hd, hq = P.hq;
   int CL, nch;
   attn_chunking(P, pos + 1, CL, nch);
   const int spl = hd >> 3;
   const int units = hq * spl;
   const int wave = c.t >> 6, lane = c.t & 63;
+  if (gw < units && !await_all(P, X, l * kStagesPerLayer + 1, c.w, c.t)) return false;
   bool ok = true;
-  for (int u = c.wg + wave * c.nb; u < units; u += c.nb * kWaves) {
+  for (int u = gw + wave * gn; u < units; u += gn * kWaves) {
     const int h = u / spl, sl = u % spl;
     float m = -INFINITY, ls = 0.f, o[8];
 #pragma unroll
@@ -778,6 +852,7 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
     }
   }
   const bool failed = any_failed(!ok);
+  if (!failed) arrive(P, X, l * kStagesPerLayer + 2, c.t);
   stamp(tr, slot, 3, c.t);
   return !failed;
 }
@@ -786,24 +861,35 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
 template <int DT, int VD>
 __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  int gw, gn;
+  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
+    arrive(P, X, l * kStagesPerLayer + 3, c.t);
+    return true;
+  }
   const int slot = l * kStagesPerLayer + 3;
   stamp(tr, slot, 0, c.t);
-  CParams& P = c.P;
   const int d = P.d, K = P.hq * P.hd;
-  const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
-  const StagePlan pl = plan_stage(P, l, GS_WO, c.t, c.wg, c.nb);
+  const int r0 = split_lo(d, gn, gw), r1 = split_lo(d, gn, gw + 1);
+  const StagePlan pl = plan_stage(P, l, GS_WO, c.t, gw, gn);
   auto prep = [&]() -> bool {
+    if (!await_all(P, X, l * kStagesPerLayer + 2, c.w, c.t)) return false;
     const bool r = poll_to16<DT>(X + P.xl.a + (size_t)l * K, K, c.s.xn, c.w, c.t);
     stamp(tr, slot, 1, c.t);
     return r;
   };
-  const StagePlan np = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
+  // the next stage this work-group runs: gate/up, or under the role split
+  // the next layer's QKV (the LM head after the last layer)
+  const StagePlan np = !P.split          ? plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb)
+                       : l + 1 < P.L     ? plan_stage(P, l + 1, GS_QKV, c.t, gw, gn)
+                                         : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, false, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xmid + (size_t)l * d;
   publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
-  ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
+  arrive(P, X, l * kStagesPerLayer + 3, c.t);
+  if (!P.per_stage) ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -812,28 +898,38 @@ __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* 
 template <int DT, int VD>
 __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  int gw, gn;
+  if (!stage_group(P, kGroupFfn, c.wg, c.nb, gw, gn)) {
+    arrive(P, X, l * kStagesPerLayer + 4, c.t);
+    return true;
+  }
   const int slot = l * kStagesPerLayer + 4;
   stamp(tr, slot, 0, c.t);
-  CParams& P = c.P;
   const int d = P.d, F = P.F;
-  const int f0 = split_lo(F, c.nb, c.wg), f1 = split_lo(F, c.nb, c.wg + 1);
+  const int f0 = split_lo(F, gn, gw), f1 = split_lo(F, gn, gw + 1);
   const int nf = f1 - f0;
-  const StagePlan pl = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
+  const StagePlan pl = plan_stage(P, l, GS_GATEUP, c.t, gw, gn);
   auto prep = [&]() -> bool {
+    if (!await_all(P, X, l * kStagesPerLayer + 3, c.w, c.t)) return false;
     if (!poll_f32(X + P.xl.xmid + (size_t)l * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_FFN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
     return true;
   };
-  const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
-  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
+  const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, gw, gn);
+  // the ring holds this stage's first vectors (issued by Wo, or under the role
+  // split by the previous layer's down stage; not before layer 0)
+  const bool prefilled = !P.split || l > 0;
+  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, prefilled, tr, slot)) return false;
   uint32_t* dst = X + P.xl.h + (size_t)l * F;
   publish_delay(P);
   for (int f = c.t; f < nf; f += kThreads) {
     const float gt = c.s.yv[f], up = c.s.yv[nf + f];
     xst32(dst + f0 + f, __float_as_uint(gt / (1.0f + expf(-gt)) * up));
   }
-  ring_prefetch(ring, np);
+  arrive(P, X, l * kStagesPerLayer + 4, c.t);
+  if (!P.per_stage) ring_prefetch(ring, np);
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -842,25 +938,34 @@ __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32
 template <int DT, int VF>
 __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  int gw, gn;
+  if (!stage_group(P, kGroupFfn, c.wg, c.nb, gw, gn)) {
+    arrive(P, X, l * kStagesPerLayer + 5, c.t);
+    return true;
+  }
   const int slot = l * kStagesPerLayer + 5;
   stamp(tr, slot, 0, c.t);
-  CParams& P = c.P;
   const int d = P.d, F = P.F;
-  const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
-  const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
+  const int r0 = split_lo(d, gn, gw), r1 = split_lo(d, gn, gw + 1);
+  const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, gw, gn);
   auto prep = [&]() -> bool {
+    if (!await_all(P, X, l * kStagesPerLayer + 4, c.w, c.t)) return false;
     const bool r = poll_to16<DT>(X + P.xl.h + (size_t)l * F, F, c.s.xn, c.w, c.t);
     stamp(tr, slot, 1, c.t);
     return r;
   };
-  const StagePlan np = l + 1 < P.L ? plan_stage(P, l + 1, GS_QKV, c.t, c.wg, c.nb)
+  // the next stage this work-group runs: the next layer's QKV, or under the
+  // role split its gate/up (the LM head after the last layer)
+  const StagePlan np = l + 1 < P.L ? plan_stage(P, l + 1, P.split ? GS_GATEUP : GS_QKV, c.t, gw, gn)
                                    : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VF>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xout + (size_t)l * d;
   publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
-  ring_prefetch(ring, np);
+  arrive(P, X, l * kStagesPerLayer + 5, c.t);
+  if (!P.per_stage) ring_prefetch(ring, np);
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -1235,6 +1340,7 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
   const int v0 = split_lo(V, c.nb, c.wg), v1 = split_lo(V, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
+    if (!await_all(P, X, (P.L - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
     if (!poll_f32(X + P.xl.xout + (size_t)(P.L - 1) * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, P.final_norm, d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
@@ -1308,6 +1414,7 @@ __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* 
   float gv = -INFINITY;
   int gi = 0x7FFFFFFF;
   bool ok = true;
+  if (!await_all(P, X, P.L * kStagesPerLayer, c.w, c.t)) return false;
   for (int w = c.t; w < c.nb && c.t < kThreads / 2; w += kThreads / 2) {
     uint64_t v = 0;
     if (ok && poll64(X + P.xl.arg + 2 * w, v, c.w, Ready32x2{})) {
@@ -1379,6 +1486,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     publish_delay(cparams(Pp));
     __syncthreads();
     if (t == 0 && wg != Pp->withhold_wg) xst64(X + Pp->xl.arg + 2 * wg, pack2f(bv, __int_as_float(bi)));
+    arrive(cparams(Pp), X, L * kStagesPerLayer, t);
     // the upper half of the work-group recycles the previous step's exchange
     // set while the lower half gathers the partials (grid <= kThreads / 2)
     if (s >= 1) {
@@ -1409,6 +1517,84 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
 }
 
 // ---------------------------------------------------------------------------
+// The same stages as separate launches (the launch-tax comparison): launch
+// (s, l, st) runs stage st of layer l of decode step s (st 0..5 = qkv, attn,
+// merge, wo, gate/up, down; 6 = LM head and the argmax partial; 7 = exchange
+// recycling and the token).  Each launch starts after the previous one has
+// finished, so every poll finds its words already written; what the
+// persistent kernel keeps on chip across stages (the residual row in LDS, the
+// next stage's first weight vectors in registers) is reloaded here.  Greedy
+// decode only, no end-of-sequence stop (the host checks both).
+// ---------------------------------------------------------------------------
+template <int DT, int G, int VD, int VF>
+__global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __restrict__ Pp, int s, int l, int st) {
+  extern __shared__ __align__(16) char smem[];
+  const Sc c = stage_ctx(Pp, smem);
+  CParams& P = c.P;
+  const int pos = P.pos0 + s;
+  uint32_t* X = P.xch + (size_t)(s % kRingSets) * P.xl.words;
+  uint4 ring[kDepth];
+  auto load_embedding = [&]() {
+    const int tok = P.forced ? P.forced[s] : s == 0 ? P.in_tok : Pp->tok_out[s - 1];
+    const uint16_t* er = P.tok_emb + (size_t)tok * P.d;
+    for (int i = c.t; i < P.d; i += kThreads) c.s.xres[i] = to_f32<DT>(er[i]);
+    __syncthreads();
+  };
+  auto own_prefetch = [&](int lay, int gs) { ring_prefetch(ring, plan_stage(P, lay, gs, c.t, c.wg, c.nb)); };
+  bool ok = true;
+  switch (st) {
+    case 0:
+      if (l == 0) load_embedding();
+      else own_prefetch(l, GS_QKV);
+      ok = st_qkv<DT, VD>(Pp, smem, l, X, nullptr, ring);
+      break;
+    case 1: ok = st_attn<DT, G>(Pp, smem, l, pos, X, nullptr); break;
+    case 2: ok = st_merge<DT>(Pp, smem, l, pos, X, nullptr); break;
+    case 3:  // the residual x_l that the Wo outputs add to
+      if (l == 0) load_embedding();
+      else ok = poll_f32(X + P.xl.xout + (size_t)(l - 1) * P.d, P.d, c.s.xres, c.w, c.t);
+      ok = ok && st_wo<DT, VD>(Pp, smem, l, X, nullptr, ring);
+      break;
+    case 4:
+      own_prefetch(l, GS_GATEUP);
+      ok = st_gateup<DT, VD>(Pp, smem, l, X, nullptr, ring);
+      break;
+    case 5:  // the residual x_mid that the down outputs add to
+      ok = poll_f32(X + P.xl.xmid + (size_t)l * P.d, P.d, c.s.xres, c.w, c.t);
+      own_prefetch(l, GS_DOWN);
+      ok = ok && st_down<DT, VF>(Pp, smem, l, X, nullptr, ring);
+      break;
+    case 6: {
+      own_prefetch(0, GS_LM);
+      float bv = 0.f;
+      int bi = 0;
+      float* lg = P.logits ? P.logits + (size_t)s * P.V : nullptr;
+      ok = st_lmhead<DT, VD>(Pp, smem, X, lg, bv, bi, nullptr, ring);
+      drain_stores();
+      __syncthreads();
+      if (ok && c.t == 0) xst64(X + P.xl.arg + 2 * c.wg, pack2f(bv, __int_as_float(bi)));
+      break;
+    }
+    default: {
+      if (s >= 1) {
+        int CL, nch;
+        attn_chunking(P, pos, CL, nch);
+        reset_set(Pp, smem, P.xch + (size_t)((s + 2) % kRingSets) * P.xl.words, nch, kThreads / 2, nullptr);
+      }
+      int tok = 0;
+      ok = gather_token(Pp, smem, X, tok, nullptr);
+      if (ok && c.wg == 0 && c.t == 0) {
+        Pp->tok_out[s] = tok;
+        Pp->ctl[CTL_DONE] = (uint32_t)(s + 1);
+        Pp->ctl[CTL_LAST] = (uint32_t)tok;
+      }
+      break;
+    }
+  }
+  (void)ok;  // a failed poll has recorded its status in the control words
+}
+
+// ---------------------------------------------------------------------------
 // Isolated GEMV probe: y[i] = W[i % ncopy] x[i], rows split over the grid,
 // one launch for all vectors.  Same engine as the decode stages.
 // ---------------------------------------------------------------------------
@@ -1421,11 +1607,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
   float* yv = red + kRedCap;
   const int nb = gridDim.x, wg = blockIdx.x;
   const int r0 = split_lo(rows, nb, wg), r1 = split_lo(rows, nb, wg + 1);
+  auto plan_of = [&](int iv, int t) {
+    StagePlan pl = plan_rows(r1 - r0, cols, t);
+    pl.seg0 = W + (size_t)(iv % ncopy) * rows * cols + (size_t)r0 * cols;
+    return pl;
+  };
+  // As between the decode stages, the last ring block of product iv issues
+  // the first vectors of product iv+1, so the weight stream runs on.
+  uint4 ring[kDepth];
   for (int iv = 0; iv < nvec; ++iv) {
     const int t = opaque_v((int)threadIdx.x);
-    const uint16_t* Wc = W + (size_t)(iv % ncopy) * rows * cols;
-    StagePlan pl = plan_rows(r1 - r0, cols, t);
-    pl.seg0 = Wc + (size_t)r0 * cols;
+    const StagePlan pl = plan_of(iv, t);
+    const StagePlan nx = iv + 1 < nvec ? plan_of(iv + 1, t) : StagePlan{};
     auto prep = [&]() -> bool {  // the probe's input is 16-bit already: bf16 residuals are zero
       const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
       constexpr int AW = kActWords<DT>;
@@ -1436,8 +1629,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
       __syncthreads();
       return true;
     };
-    uint4 ring[kDepth];
-    gemv_any<DT>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
+    gemv_any<DT>(pl, prep, xs, red, yv, t, ring, iv > 0, nx);
     for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
     __syncthreads();
   }

@@ -24,6 +24,14 @@ const void* monokernel_fn_bf16_g1(int vd, int vf);
 const void* monokernel_fn_bf16_g2(int vd, int vf);
 const void* monokernel_fn_bf16_g4(int vd, int vf);
 const void* monokernel_fn_bf16_g8(int vd, int vf);
+const void* stage_kernel_fn_f16_g1(int vd, int vf);
+const void* stage_kernel_fn_f16_g2(int vd, int vf);
+const void* stage_kernel_fn_f16_g4(int vd, int vf);
+const void* stage_kernel_fn_f16_g8(int vd, int vf);
+const void* stage_kernel_fn_bf16_g1(int vd, int vf);
+const void* stage_kernel_fn_bf16_g2(int vd, int vf);
+const void* stage_kernel_fn_bf16_g4(int vd, int vf);
+const void* stage_kernel_fn_bf16_g8(int vd, int vf);
 const void* gemv_probe_fn(int dtype);
 const void* stream_probe_fn(int depth);
 hipError_t launch_fill(uint32_t* p, uint64_t n, uint32_t v, hipStream_t st);
@@ -73,6 +81,7 @@ XchLayout xch_layout(const kie_config& c) {
   x.cand = take(2ull * kMaxWG * kCand);
   x.cand2 = take(2ull * (kMaxWG / 8) * kCand);
   x.stok = take(2);
+  x.cnt = take(L * kStagesPerLayer + 1);
   x.dense = o;
   x.att = take(L * c.n_heads * (uint64_t)attn_cmax(c) * (c.head_dim + 4));
   x.words = align_up(o, 64);
@@ -175,6 +184,19 @@ const void* monokernel_fn(const kie_config& c) {
   return nullptr;
 }
 
+// The per-stage instance of the same shape (one launch per stage).
+const void* stage_kernel_fn(const kie_config& c) {
+  const int G = c.n_heads / c.n_kv_heads, vd = width_class(c.d_model), vf = width_class(c.d_ffn);
+  const bool f16 = c.dtype == KIE_F16;
+  switch (G) {
+    case 1: return f16 ? stage_kernel_fn_f16_g1(vd, vf) : stage_kernel_fn_bf16_g1(vd, vf);
+    case 2: return f16 ? stage_kernel_fn_f16_g2(vd, vf) : stage_kernel_fn_bf16_g2(vd, vf);
+    case 4: return f16 ? stage_kernel_fn_f16_g4(vd, vf) : stage_kernel_fn_bf16_g4(vd, vf);
+    case 8: return f16 ? stage_kernel_fn_f16_g8(vd, vf) : stage_kernel_fn_bf16_g8(vd, vf);
+  }
+  return nullptr;
+}
+
 }  // namespace
 
 struct kie_engine {
@@ -197,6 +219,9 @@ struct kie_engine {
   int abort_after = -1;
   int withhold_wg = -1;
   int delay_wg = -1;          // race test: work-group whose publications are delayed
+  int handoff = kHandoffNan;  // hand-off protocol of the persistent launches
+  int launch_mode = KIE_LAUNCH_PERSISTENT;  // kie_decode: persistent kernel or one launch per stage
+  int split = 0;              // role split of the work-groups (attention block / feed-forward block)
   uint64_t delay_ticks = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float last_ms = 0.f;
@@ -345,6 +370,8 @@ static kie_status create_impl(kie_engine* e, const kie_config* cfg, void* worksp
   if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, e->lds.bytes);
   if (he != hipSuccess) return hip_fail(he, "occupancy");
   if (per_cu < 1) return KIE_ERR_UNSUPPORTED;
+  he = hipFuncSetAttribute(stage_kernel_fn(*cfg), hipFuncAttributeMaxDynamicSharedMemorySize, e->lds.bytes);
+  if (he != hipSuccess) return hip_fail(he, "stage kernel");
   // One resident work-group per compute unit.
   e->grid = e->cu_count < kMaxWG ? e->cu_count : kMaxWG;
   if (!grid_fits(*cfg, lay, e->grid)) return KIE_ERR_UNSUPPORTED;
@@ -497,6 +524,8 @@ static Params base_params(const kie_engine* e) {
   P.abort_after = -1;
   P.withhold_wg = e->withhold_wg;
   P.delay_wg = e->delay_wg;
+  P.handoff = e->handoff;
+  P.split = e->split;
   P.delay_ticks = e->delay_ticks;
   P.timeout = e->timeout;
   P.trace = e->trace;
@@ -537,6 +566,85 @@ static kie_status run_persistent(kie_engine* e, Params& P, int* done, int* last)
   if (st == 0) return KIE_OK;
   if (st == KIE_ERR_ABORTED) return KIE_ERR_ABORTED;
   return KIE_ERR_TIMEOUT;
+}
+
+// kie_decode's steps as one launch per stage (stage_kernel): 6 per layer, the
+// LM head, and the token.  Plain launches in a host loop, or the same launches
+// captured once into a HIP graph and replayed (capture and instantiation happen
+// before the timed region).  The events bracket only the launches.
+static kie_status run_per_stage(kie_engine* e, Params& P, int* done, int* last) {
+  const int L = e->cfg.n_layers;
+  KIE_HIP(launch_fill(P.ctl, CTL_WORDS, 0u, e->stream));
+  KIE_HIP(launch_fill(P.xch, (uint64_t)kRingSets * P.xl.words, kSent, e->stream));
+  Params* dev_params = reinterpret_cast<Params*>(e->ws + e->lay.params);
+  e->params_host = P;
+  KIE_HIP(hipMemcpyAsync(dev_params, &e->params_host, sizeof(Params), hipMemcpyHostToDevice, e->stream));
+  const void* fn = stage_kernel_fn(e->cfg);
+  auto launch_all = [&](hipStream_t stream) -> hipError_t {
+    for (int s = 0; s < P.n_steps; ++s)
+      for (int k = 0; k < L * kStagesPerLayer + 2; ++k) {
+        int ss = s, l = k < L * kStagesPerLayer ? k / kStagesPerLayer : 0;
+        int st = k < L * kStagesPerLayer ? k % kStagesPerLayer : 6 + (k - L * kStagesPerLayer);
+        void* args[] = {&dev_params, &ss, &l, &st};
+        const hipError_t he = hipLaunchKernel(fn, dim3(e->grid), dim3(kThreads), args, (size_t)e->lds.bytes,
+                                              stream);
+        if (he != hipSuccess) return he;
+      }
+    return hipSuccess;
+  };
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  hipError_t he = hipSuccess;
+  if (e->launch_mode == KIE_LAUNCH_PER_STAGE_GRAPH) {
+    // captured on a stream of its own (the engine's may be the null stream,
+    // which cannot be captured), replayed on the engine's
+    hipStream_t cs = nullptr;
+    he = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (he == hipSuccess) he = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (he == hipSuccess) {
+      const hipError_t hl = launch_all(cs);
+      he = hipStreamEndCapture(cs, &graph);
+      if (he == hipSuccess) he = hl;
+    }
+    if (cs) (void)hipStreamDestroy(cs);
+    if (he == hipSuccess) he = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  }
+  if (he == hipSuccess && e->ev0) he = hipEventRecord(e->ev0, e->stream);
+  if (he == hipSuccess) he = exec ? hipGraphLaunch(exec, e->stream) : launch_all(e->stream);
+  if (he == hipSuccess && e->ev1) he = hipEventRecord(e->ev1, e->stream);
+  uint32_t ctl[4] = {0, 0, 0, 0};
+  if (he == hipSuccess) he = hipMemcpyAsync(ctl, P.ctl, sizeof(ctl), hipMemcpyDeviceToHost, e->stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(e->stream);
+  if (exec) (void)hipGraphExecDestroy(exec);
+  if (graph) (void)hipGraphDestroy(graph);
+  KIE_HIP(he);
+  float ms = 0.f;
+  if (e->ev0 && e->ev1 && hipEventElapsedTime(&ms, e->ev0, e->ev1) == hipSuccess) e->last_ms = ms;
+  *done = (int)ctl[CTL_DONE];
+  *last = (int)ctl[CTL_LAST];
+  e->last_steps = *done;
+  return ctl[CTL_STATUS] == 0 ? KIE_OK : KIE_ERR_TIMEOUT;
+}
+
+// The role split needs a grid of whole 16-work-group blocks (8 of each role
+// per block, one per XCD) and a tiling that fits half the grid.
+static bool split_fits(const kie_engine* e, int grid) {
+  return grid >= 16 && grid % 16 == 0 && grid_fits(e->cfg, e->lay, grid / 2) &&
+         kie_check_tiling(&e->cfg, grid / 2, 0) == KIE_OK;
+}
+
+extern "C" kie_status kie_set_split(kie_engine* e, int32_t on) {
+  if (!e || (on != 0 && on != 1)) return KIE_ERR_ARG;
+  if (on && !split_fits(e, e->grid)) return KIE_ERR_UNSUPPORTED;
+  e->split = on;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_launch_mode(kie_engine* e, int32_t mode) {
+  if (!e || (mode != KIE_LAUNCH_PERSISTENT && mode != KIE_LAUNCH_PER_STAGE && mode != KIE_LAUNCH_PER_STAGE_GRAPH))
+    return KIE_ERR_ARG;
+  e->launch_mode = mode;
+  return KIE_OK;
 }
 
 extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prompt,
@@ -607,6 +715,7 @@ extern "C" kie_status kie_set_grid(kie_engine* e, int32_t grid) {
   if (grid == 0) grid = full;
   if (grid > full) return KIE_ERR_ARG;
   if (!grid_fits(e->cfg, e->lay, grid) || kie_check_tiling(&e->cfg, grid, 0) != KIE_OK) return KIE_ERR_UNSUPPORTED;
+  if (e->split && !split_fits(e, grid)) return KIE_ERR_UNSUPPORTED;
   e->grid = grid;
   return KIE_OK;
 }
@@ -656,7 +765,17 @@ extern "C" kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id,
   P.logits = logits_dev;
   P.abort_after = abort_after;
   int done = 0, last = 0;
-  const kie_status st = run_persistent(e, P, &done, &last);
+  const bool per_stage = e->launch_mode != KIE_LAUNCH_PERSISTENT;
+  if (per_stage) {
+    // greedy, fixed step count, default hand-offs, no timeline
+    if (e->samp_k > 0 || P.eos_id >= 0 || abort_after >= 0 || e->withhold_wg >= 0 || e->split)
+      return KIE_ERR_UNSUPPORTED;
+    P.per_stage = 1;
+    P.handoff = kHandoffNan;
+    P.trace = nullptr;
+    P.delay_wg = -1;
+  }
+  const kie_status st = per_stage ? run_per_stage(e, P, &done, &last) : run_persistent(e, P, &done, &last);
   if (st == KIE_ERR_HIP) return st;
   if (done > 0) {
     KIE_HIP(hipMemcpy(tokens_host, P.tok_out, (size_t)done * 4, hipMemcpyDeviceToHost));
@@ -741,6 +860,12 @@ extern "C" kie_status kie_set_abort_after(kie_engine* e, int32_t abort_after_ste
 extern "C" kie_status kie_set_withhold(kie_engine* e, int32_t wg) {
   if (!e || wg < -1) return KIE_ERR_ARG;
   e->withhold_wg = wg;
+  return KIE_OK;
+}
+
+extern "C" kie_status kie_set_handoff(kie_engine* e, int32_t mode) {
+  if (!e || (mode != KIE_HANDOFF_NAN_POLL && mode != KIE_HANDOFF_COUNTERS)) return KIE_ERR_ARG;
+  e->handoff = mode == KIE_HANDOFF_COUNTERS ? kHandoffCounters : kHandoffNan;
   return KIE_OK;
 }
 

@@ -29,6 +29,11 @@ KIE_F16 = 1
 KIE_BF16 = 2
 KIE_PREFILL_AUTO = 0
 KIE_PREFILL_DECODE_LOOP = 1
+KIE_HANDOFF_NAN_POLL = 0
+KIE_HANDOFF_COUNTERS = 1
+KIE_LAUNCH_PERSISTENT = 0
+KIE_LAUNCH_PER_STAGE = 1
+KIE_LAUNCH_PER_STAGE_GRAPH = 2
 KIE_STATIC_WORKSPACE_BYTES = 64 << 20  # include/kie.h
 
 
@@ -95,6 +100,9 @@ SIGNATURES = {
     "kie_set_abort_after": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_withhold": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_delay": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64]),
+    "kie_set_handoff": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_launch_mode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kie_set_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_check_idle_sets": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64)]),
     "kie_trace_words": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kie_set_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
@@ -343,6 +351,18 @@ class Engine:
     def set_delay(self, wg: int, ticks: int):
         """Race test: work-group wg holds back each hand-off publication by ticks (100 MHz)."""
         _check(lib().kie_set_delay(self._h, int(wg), int(ticks)), "kie_set_delay")
+
+    def set_handoff(self, mode: int):
+        """KIE_HANDOFF_NAN_POLL (default) or KIE_HANDOFF_COUNTERS (comparison protocol)."""
+        _check(lib().kie_set_handoff(self._h, int(mode)), "kie_set_handoff")
+
+    def set_launch_mode(self, mode: int):
+        """KIE_LAUNCH_PERSISTENT (default), KIE_LAUNCH_PER_STAGE or KIE_LAUNCH_PER_STAGE_GRAPH."""
+        _check(lib().kie_set_launch_mode(self._h, int(mode)), "kie_set_launch_mode")
+
+    def set_split(self, on: bool):
+        """Role split: attention block and feed-forward block on separate halves of the grid."""
+        _check(lib().kie_set_split(self._h, 1 if on else 0), "kie_set_split")
 
     def idle_sets_dirty_words(self) -> int:
         """Words of the two idle exchange sets that are not the NaN pattern after the last launch."""

@@ -240,6 +240,18 @@ def test_cache_storage_dtype_rounds_each_appended_row(dt):
     assert torch.allclose(full[len(prompt):], lgs, atol=1e-12)
 
 
+@pytest.mark.parametrize("dt,fmt", [(torch.float16, "f16"), (torch.bfloat16, "bf16")])
+def test_bruteforce_storage_rounding_matches_torch(dt, fmt):
+    """The scalar model's 16-bit rounding (float64 -> float32 -> 16 bits, ties to
+    even) agrees with PyTorch's conversion, including values that round
+    differently directly and through float32."""
+    g = torch.Generator().manual_seed(0)
+    xs = (torch.randn(20000, dtype=F64, generator=g) * 10).tolist()
+    xs += [1 + 2**-8 + 2**-30, 1 + 2**-11 + 2**-40, 65504.0, 1e-8, -0.0]
+    ref = torch.tensor(xs, dtype=F64).to(dt).to(F64).tolist()
+    assert [BF.round_store(x, fmt) for x in xs] == ref
+
+
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16])
 def test_cache_storage_dtype_matches_bruteforce(dt):
     """The 16-bit cache mode rounds exactly the cached keys (after rotation) and

@@ -1607,18 +1607,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
   float* yv = red + kRedCap;
   const int nb = gridDim.x, wg = blockIdx.x;
   const int r0 = split_lo(rows, nb, wg), r1 = split_lo(rows, nb, wg + 1);
-  auto plan_of = [&](int iv, int t) {
-    StagePlan pl = plan_rows(r1 - r0, cols, t);
-    pl.seg0 = W + (size_t)(iv % ncopy) * rows * cols + (size_t)r0 * cols;
-    return pl;
-  };
-  // As between the decode stages, the last ring block of product iv issues
-  // the first vectors of product iv+1, so the weight stream runs on.
-  uint4 ring[kDepth];
   for (int iv = 0; iv < nvec; ++iv) {
     const int t = opaque_v((int)threadIdx.x);
-    const StagePlan pl = plan_of(iv, t);
-    const StagePlan nx = iv + 1 < nvec ? plan_of(iv + 1, t) : StagePlan{};
+    const uint16_t* Wc = W + (size_t)(iv % ncopy) * rows * cols;
+    StagePlan pl = plan_rows(r1 - r0, cols, t);
+    pl.seg0 = Wc + (size_t)r0 * cols;
     auto prep = [&]() -> bool {  // the probe's input is 16-bit already: bf16 residuals are zero
       const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
       constexpr int AW = kActWords<DT>;
@@ -1629,7 +1622,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
       __syncthreads();
       return true;
     };
-    gemv_any<DT>(pl, prep, xs, red, yv, t, ring, iv > 0, nx);
+    uint4 ring[kDepth];
+    gemv_any<DT>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
     for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
     __syncthreads();
   }

@@ -270,15 +270,18 @@ def ttft_bench(name: str, modes=("auto", "decode_loop"), chunks=(0,)):
         eng.load_weights(w)
         eng.set_prefill_mode(kie.KIE_PREFILL_AUTO if mode == "auto" else kie.KIE_PREFILL_DECODE_LOOP)
         eng.set_prefill_chunk(chunk)
-        eng.prefill(prompt[:64])  # warm-up
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        tok, _ = eng.prefill(prompt)
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
+        eng.prefill(prompt if mode == "auto" else prompt[:64])  # warm-up
+        runs = []
+        for _ in range(3 if mode == "auto" else 1):  # the median of three (one for the slow loop)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            tok, _ = eng.prefill(prompt)
+            torch.cuda.synchronize()
+            runs.append(time.perf_counter() - t0)
+        dt = sorted(runs)[len(runs) // 2]
         flops = 2.0 * synth.param_count(s) * wl.n_prompt
-        print(json.dumps({"ttft_ms": dt * 1e3, "workload": name, "prompt": wl.n_prompt, "mode": mode,
-                          "chunk": chunk if mode == "auto" else None,
+        print(json.dumps({"ttft_ms": dt * 1e3, "runs_ms": [r * 1e3 for r in runs], "workload": name,
+                          "prompt": wl.n_prompt, "mode": mode, "chunk": chunk if mode == "auto" else None,
                           "prompt_tokens_per_s": wl.n_prompt / dt, "dense_TFLOP_per_s": flops / dt / 1e12,
                           "first_token": tok}), flush=True)
         eng.close()
@@ -324,7 +327,7 @@ def grid_sweep(name: str, grids, steps=None):
 STAGES = ("qkv", "attention", "merge", "wo", "gate/up", "down")
 
 
-def timeline(wl, step: int = 10, n_decode: int = 32, samp=None, handoff: int = 0, split: bool = False):
+def timeline(wl, step: int = 10, n_decode: int = 32, samp=None, handoff: int = 0):
     """Per-token timeline of one decode step (the step-th of a kie_decode(n_decode)
     launch after the workload's prompt): for every stage, the median over
     work-groups of the time from stage entry until its input had arrived (the
@@ -344,7 +347,6 @@ def timeline(wl, step: int = 10, n_decode: int = 32, samp=None, handoff: int = 0
     eng = kie.Engine(s, max_seq=P + n_decode, device=dev)
     eng.load_weights(w)
     eng.set_handoff(handoff)
-    eng.set_split(split)
     if samp is not None:
         eng.set_sampling(samp[0], int(samp[1]), samp[2], wl.prompt_seed)
     eng.prefill(synth.make_prompt(s, P, wl.prompt_seed).tolist())
@@ -437,7 +439,8 @@ def cpu_baseline(shape, w_gpu, n_prompt: int, budget_s: float = 15.0):
         "cores": threads,
         "nproc": nproc,
         "cpu_model": _cpu_model(),
-        "kind": "oracle (fp32 C++, std::thread over matrix rows)",
+        "kind": "oracle",
+        "implementation": "fp32 C++ decoder (oracle/cpu_decoder.cpp), std::thread over matrix rows",
         "sample": f"{n} incremental greedy decode steps of the same model after a synthetic "
                   f"{n_prompt}-position KV cache (one untimed step), positions {n_prompt + 1}..{n_prompt + n} "
                   f"counted from 0",
@@ -462,8 +465,6 @@ def main():
     ap.add_argument("--gemv", action="store_true", help="only run the isolated GEMV probe workload")
     ap.add_argument("--handoff", default="nan", choices=sorted(HANDOFFS),
                     help="hand-off protocol: NaN-polled data (default) or atomic arrival counters (comparison)")
-    ap.add_argument("--split", action="store_true",
-                    help="role split: attention block and feed-forward block on separate halves of the grid")
     ap.add_argument("--ablation", action="store_true",
                     help="only compare the persistent kernel (NaN polls, arrival counters) with one launch per stage")
     ap.add_argument("--stream", action="store_true",
@@ -513,7 +514,7 @@ def main():
         from persistent_decode_monokernel_amd import synth
 
         timeline(synth.WORKLOADS[args.workload], step=args.timeline, samp=args.sampling,
-                 handoff=HANDOFFS[args.handoff], split=args.split)
+                 handoff=HANDOFFS[args.handoff])
         return
 
     import torch
@@ -533,7 +534,6 @@ def main():
     eng = kie.Engine(s, max_seq=P + max(K, Wm, 1), device=dev)
     eng.load_weights(w)
     eng.set_handoff(HANDOFFS[args.handoff])
-    eng.set_split(args.split)
     samp = None
     if args.sampling is not None:
         samp = {"temperature": args.sampling[0], "top_k": int(args.sampling[1]), "top_p": args.sampling[2],
@@ -584,8 +584,7 @@ def main():
                         f"F{s.d_ffn} V{s.vocab}, prompt {P}, decode {K}, batch 1, "
                         + ("greedy" if samp is None else
                            f"sampled (T {samp['temperature']}, top-k {samp['top_k']}, top-p {samp['top_p']})")
-                        + ("" if args.handoff == "nan" else f", {args.handoff} hand-offs")
-                        + (", role split" if args.split else ""),
+                        + ("" if args.handoff == "nan" else f", {args.handoff} hand-offs"),
             "prompt": P,
             "decode_tokens": K,
             "batch": 1,

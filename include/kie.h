@@ -172,10 +172,12 @@ kie_status kie_create_static(const kie_config* cfg, void* hip_stream, kie_engine
  * resident and borrowed, as the stated target's boundary has it. */
 kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
 
-/* Run the prompt through the model (see kie_set_prefill_mode for how): the
- * last prompt position, and by default only it, is a step of the persistent
- * decode kernel with the prompt token fed instead of a sampled one; earlier
- * positions run as dense matrix-core products where the shape allows.
+/* Run the prompt through the model (see kie_set_prefill_mode for how).  By
+ * default, where the shape allows (2 or more positions), every prompt position
+ * runs as dense matrix-core products, and one launch of the persistent kernel
+ * then runs only the LM head and the token choice on the last position's
+ * residual.  Otherwise every position is a step of the persistent decode
+ * kernel with the prompt token fed instead of a sampled one.
  * Starts a new sequence: the KV cache is rewritten from position 0.
  *   prompt_host[n_prompt]: token ids in [0, vocab), 1 <= n_prompt <= max_seq.
  *   next_token_host: receives the token after the last prompt position (greedy,
@@ -186,13 +188,14 @@ kie_status kie_load_weights(kie_engine* e, const kie_weights* w);
 kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int32_t n_prompt,
                        int32_t* next_token_host, float* logits_dev);
 
-/* How kie_prefill() runs the prompt.  KIE_PREFILL_AUTO (default): positions
- * 0 .. n_prompt-2 as dense products on the matrix cores (GEMMs and flash
- * attention; fp16 activations for fp16 models, fp32 activations split into
- * three bf16 terms for bf16 models; shapes whose projection widths are
- * multiples of 128 -- others fall back to the decode loop), then the last
- * position as one forced step of the persistent decode kernel, which yields
- * the logits and the first token.  KIE_PREFILL_DECODE_LOOP: every prompt
+/* How kie_prefill() runs the prompt.  KIE_PREFILL_AUTO (default): every
+ * position as dense products on the matrix cores (GEMMs and flash attention;
+ * fp16 activations for fp16 models, fp32 activations split into three bf16
+ * terms for bf16 models; shapes whose projection widths are multiples of 128
+ * and prompts of 2 or more positions -- others fall back to the decode loop),
+ * then one launch of the persistent kernel that runs only the LM head and the
+ * token choice on the last position, which yields the logits and the first
+ * token.  KIE_PREFILL_DECODE_LOOP: every prompt
  * position as a forced step of the persistent decode kernel.  The pages put
  * prompt processing inside the resident program (revietech.ru page, section
  * "Chto takoye monokernel"); both modes leave the same sequence state (up to
@@ -334,6 +337,11 @@ kie_status kie_set_delay(kie_engine* e, int32_t wg, uint64_t ticks);
  *     comparison.  After each stage every work-group waits until its own
  *     stores are performed and adds one to the stage's counter (an agent-scope
  *     atomic); consumers wait until all work-groups have arrived, then read.
+ * The counter protocol is a separate kernel instance, built for the shapes it
+ * is measured on (4 query heads per KV head, model width and d_ffn both in
+ * the four-vectors-per-lane GEMV class: the ~2B and ~8B shapes among them);
+ * KIE_ERR_UNSUPPORTED for other shapes.  An
+ * LM-head-only launch of kie_prefill always uses the default protocol.
  * Results are bit-identical in both modes.  KIE_ERR_ARG for another mode. */
 #define KIE_HANDOFF_NAN_POLL 0
 #define KIE_HANDOFF_COUNTERS 1
@@ -355,22 +363,6 @@ kie_status kie_set_handoff(kie_engine* e, int32_t mode);
 #define KIE_LAUNCH_PER_STAGE 1
 #define KIE_LAUNCH_PER_STAGE_GRAPH 2
 kie_status kie_set_launch_mode(kie_engine* e, int32_t mode);
-
-/* Work-group roles of the next persistent launches.
- * Source: revietech.ru, "Kog vyzhimayet maksimum iz GPU: 3000 tokenov/s",
- * sections "Chto takoye monokernel" (decode is bound by memory bandwidth and
- * by synchronisation) and "Arkhitektura i osobennosti" (the kernel chooses
- * which compute units do what).
- *   on = 0 (default): every stage runs on the whole grid.
- *   on = 1: the attention block (QKV, attention, merge, Wo) runs on half the
- *     work-groups and the feed-forward block (gate/up, down) on the other
- *     half, 16 of each per XCD; the LM head and the token on all.  Each half
- *     issues the weights of its next stage while the other half works.
- * Results are bit-identical either way.  KIE_ERR_UNSUPPORTED when the grid is
- * not a multiple of 16 or the shape's rows do not tile half of it (also from
- * a later kie_set_grid); KIE_ERR_ARG for another value.  The per-stage launch
- * modes do not take it (KIE_ERR_UNSUPPORTED from kie_decode). */
-kie_status kie_set_split(kie_engine* e, int32_t on);
 
 /* Race test of the exchange-set recycling: after a launch that completed S >= 2
  * steps, the two exchange sets not used by its last step must hold the NaN

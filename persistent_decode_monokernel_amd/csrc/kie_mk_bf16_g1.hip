@@ -4,15 +4,15 @@
 
 namespace kie {
 const void* monokernel_fn_bf16_g1(int vd, int vf) {
-  if (vd == 0 && vf == 1) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 0, 1>);
-  if (vd == 0 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 0, 2>);
-  if (vd == 0 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 0, 4>);
-  if (vd == 1 && vf == 1) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 1, 1>);
-  if (vd == 1 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 1, 2>);
-  if (vd == 1 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 1, 4>);
-  if (vd == 2 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 2, 2>);
-  if (vd == 2 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 2, 4>);
-  if (vd == 4 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 4, 4>);
+  if (vd == 0 && vf == 1) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 0, 1, false>);
+  if (vd == 0 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 0, 2, false>);
+  if (vd == 0 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 0, 4, false>);
+  if (vd == 1 && vf == 1) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 1, 1, false>);
+  if (vd == 1 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 1, 2, false>);
+  if (vd == 1 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 1, 4, false>);
+  if (vd == 2 && vf == 2) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 2, 2, false>);
+  if (vd == 2 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 2, 4, false>);
+  if (vd == 4 && vf == 4) return reinterpret_cast<const void*>(&monokernel<KIE_BF16, 1, 4, 4, false>);
   return nullptr;
 }
 

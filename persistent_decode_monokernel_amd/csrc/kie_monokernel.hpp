@@ -88,24 +88,6 @@ __device__ __forceinline__ void publish_delay(CParams& P) {
   }
 }
 
-// Work-group roles.  Without the role split every stage runs on the whole
-// grid.  With it, the attention block runs on the work-groups whose index has
-// bit 3 clear and the feed-forward block on those with it set: consecutive
-// work-groups go to the 8 XCDs in turn, so each XCD holds 16 of each.  While
-// one half works on its stages the other has already issued the weights of its
-// next stage, so its polls do not queue behind its own weight loads.  gw / gn:
-// index and count within the stage's group.
-__device__ __forceinline__ bool stage_group(CParams& P, int grp, int wg, int nb, int& gw, int& gn) {
-  if (!P.split) {
-    gw = wg;
-    gn = nb;
-    return true;
-  }
-  gw = ((wg >> 4) << 3) | (wg & 7);
-  gn = nb >> 1;
-  return ((wg >> 3) & 1) == grp;
-}
-
 // Issue the first kDepth vectors of the next GEMV stage into the ring.
 __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np);
 
@@ -158,8 +140,9 @@ __device__ __forceinline__ bool any_failed(bool failed) { return __syncthreads_o
 // k of an exchange set starts at kSent like every other word; each work-group
 // adds one once all its outputs of stage k are performed, so the counter reads
 // kSent + grid when every work-group has arrived.
+template <bool HO>
 __device__ __forceinline__ void arrive(CParams& P, uint32_t* X, int k, int t) {
-  if (P.handoff != kHandoffCounters) return;
+  if constexpr (!HO) return;
   drain_stores();
   __syncthreads();
   if (t == 0)
@@ -168,8 +151,9 @@ __device__ __forceinline__ void arrive(CParams& P, uint32_t* X, int k, int t) {
 }
 // Wait (thread 0 polls, the work-group follows) until every work-group has
 // arrived at counter k.  Ends with a barrier in counter mode.
+template <bool HO>
 __device__ __forceinline__ bool await_all(CParams& P, uint32_t* X, int k, const Watch& w, int t) {
-  if (P.handoff != kHandoffCounters) return true;
+  if constexpr (!HO) return true;
   bool ok = true;
   if (t == 0) {
     const uint32_t* p = X + P.xl.cnt + k;
@@ -525,24 +509,19 @@ __device__ __forceinline__ StagePlan plan_stage(CParams& P, int l, int st, int t
 // QKV projection: rows [r0, r1) of the stacked [Wq; Wk; Wv] (contiguous row
 // segments of the three matrices), published unrotated in fp32.  Input x_l:
 // LDS xres (layer 0: the embedding) or polled from the previous layer's xout.
-template <int DT, int VD>
+template <int DT, int VD, bool HO>
 __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
-  int gw, gn;
-  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
-    arrive(P, X, l * kStagesPerLayer + 0, c.t);
-    return true;
-  }
   const int slot = l * kStagesPerLayer + 0;
   stamp(tr, slot, 0, c.t);
   const int hd = P.hd, d = P.d;
   const int nq = P.hq * hd, nk = P.hkv * hd;
   const int N = nq + 2 * nk;
-  const int r0 = split_lo(N, gn, gw), r1 = split_lo(N, gn, gw + 1);
-  const StagePlan pl = plan_stage(P, l, GS_QKV, c.t, gw, gn);
+  const int r0 = split_lo(N, c.nb, c.wg), r1 = split_lo(N, c.nb, c.wg + 1);
+  const StagePlan pl = plan_stage(P, l, GS_QKV, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
-    if (l > 0 && !await_all(P, X, (l - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
+    if (l > 0 && !await_all<HO>(P, X, (l - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
     if (l > 0 && !poll_f32(X + P.xl.xout + (size_t)(l - 1) * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_ATTN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
@@ -552,7 +531,7 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
   uint32_t* dst = X + P.xl.qkv + (size_t)l * N;
   publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads) xst32(dst + r0 + r, __float_as_uint(c.s.yv[r]));
-  arrive(P, X, l * kStagesPerLayer + 0, c.t);
+  arrive<HO>(P, X, l * kStagesPerLayer + 0, c.t);
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -581,15 +560,10 @@ __device__ __forceinline__ float safe_exp_diff(float a, float m) { return a == -
 // Each group keeps the online-softmax state of up to four heads at once, so a
 // K/V row is read once for all of them; the groups' states then meet once in
 // LDS, one thread per (head, dimension) folding them.
-template <int DT, int G>
+template <int DT, int G, bool HO>
 __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
-  int gw, gn;
-  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
-    arrive(P, X, l * kStagesPerLayer + 1, c.t);
-    return true;
-  }
   const int slot = l * kStagesPerLayer + 1;
   stamp(tr, slot, 0, c.t);
   const int t = c.t;
@@ -611,8 +585,8 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
   float* go = gml + PP * HB * 2;                          // [PP][HB][hd] per-group o
   constexpr int APF = 2;                                  // passes prefetched into registers
   const uint32_t* src = X + P.xl.qkv + (size_t)l * N;
-  if (gw < units && !await_all(P, X, l * kStagesPerLayer + 0, c.w, t)) return false;
-  for (int u = gw; u < units; u += gn) {
+  if (c.wg < units && !await_all<HO>(P, X, l * kStagesPerLayer + 0, c.w, t)) return false;
+  for (int u = c.wg; u < units; u += c.nb) {
     const int g = u % hkv, ch = u / hkv;
     const int j0 = ch * CL, j1 = min(n, j0 + CL);
     const bool has_new = pos >= j0 && pos < j1;
@@ -784,22 +758,17 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
       __syncthreads();
     }
   }
-  arrive(P, X, l * kStagesPerLayer + 1, t);
+  arrive<HO>(P, X, l * kStagesPerLayer + 1, t);
   stamp(tr, slot, 3, t);
   return true;
 }
 
 // Merge of the split-KV partials.  Unit (head h, dims 8s..8s+7) runs on one
 // wave; lanes walk the chunks with an online rescaling, then the wave combines.
-template <int DT>
+template <int DT, bool HO>
 __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos, uint32_t* X, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
-  int gw, gn;
-  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
-    arrive(P, X, l * kStagesPerLayer + 2, c.t);
-    return true;
-  }
   const int slot = l * kStagesPerLayer + 2;
   stamp(tr, slot, 0, c.t);
   const int hd = P.hd, hq = P.hq;
@@ -808,9 +777,9 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
   const int spl = hd >> 3;
   const int units = hq * spl;
   const int wave = c.t >> 6, lane = c.t & 63;
-  if (gw < units && !await_all(P, X, l * kStagesPerLayer + 1, c.w, c.t)) return false;
+  if (c.wg < units && !await_all<HO>(P, X, l * kStagesPerLayer + 1, c.w, c.t)) return false;
   bool ok = true;
-  for (int u = gw + wave * gn; u < units; u += gn * kWaves) {
+  for (int u = c.wg + wave * c.nb; u < units; u += c.nb * kWaves) {
     const int h = u / spl, sl = u % spl;
     float m = -INFINITY, ls = 0.f, o[8];
 #pragma unroll
@@ -852,120 +821,96 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
     }
   }
   const bool failed = any_failed(!ok);
-  if (!failed) arrive(P, X, l * kStagesPerLayer + 2, c.t);
+  if (!failed) arrive<HO>(P, X, l * kStagesPerLayer + 2, c.t);
   stamp(tr, slot, 3, c.t);
   return !failed;
 }
 
 // x_mid = x_l + Wo a  (rows split over work-groups)
-template <int DT, int VD>
+template <int DT, int VD, bool HO, bool PS>
 __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
-  int gw, gn;
-  if (!stage_group(P, kGroupAttn, c.wg, c.nb, gw, gn)) {
-    arrive(P, X, l * kStagesPerLayer + 3, c.t);
-    return true;
-  }
   const int slot = l * kStagesPerLayer + 3;
   stamp(tr, slot, 0, c.t);
   const int d = P.d, K = P.hq * P.hd;
-  const int r0 = split_lo(d, gn, gw), r1 = split_lo(d, gn, gw + 1);
-  const StagePlan pl = plan_stage(P, l, GS_WO, c.t, gw, gn);
+  const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
+  const StagePlan pl = plan_stage(P, l, GS_WO, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
-    if (!await_all(P, X, l * kStagesPerLayer + 2, c.w, c.t)) return false;
+    if (!await_all<HO>(P, X, l * kStagesPerLayer + 2, c.w, c.t)) return false;
     const bool r = poll_to16<DT>(X + P.xl.a + (size_t)l * K, K, c.s.xn, c.w, c.t);
     stamp(tr, slot, 1, c.t);
     return r;
   };
-  // the next stage this work-group runs: gate/up, or under the role split
-  // the next layer's QKV (the LM head after the last layer)
-  const StagePlan np = !P.split          ? plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb)
-                       : l + 1 < P.L     ? plan_stage(P, l + 1, GS_QKV, c.t, gw, gn)
-                                         : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
+  const StagePlan np = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, false, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xmid + (size_t)l * d;
   publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
-  arrive(P, X, l * kStagesPerLayer + 3, c.t);
-  if (!P.per_stage) ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
+  arrive<HO>(P, X, l * kStagesPerLayer + 3, c.t);
+  if constexpr (!PS) ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
   stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // h = silu(Wg n) * (Wu n), n = RMSNorm(x_mid) * g_ffn
-template <int DT, int VD>
+template <int DT, int VD, bool HO, bool PS>
 __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
-  int gw, gn;
-  if (!stage_group(P, kGroupFfn, c.wg, c.nb, gw, gn)) {
-    arrive(P, X, l * kStagesPerLayer + 4, c.t);
-    return true;
-  }
   const int slot = l * kStagesPerLayer + 4;
   stamp(tr, slot, 0, c.t);
   const int d = P.d, F = P.F;
-  const int f0 = split_lo(F, gn, gw), f1 = split_lo(F, gn, gw + 1);
+  const int f0 = split_lo(F, c.nb, c.wg), f1 = split_lo(F, c.nb, c.wg + 1);
   const int nf = f1 - f0;
-  const StagePlan pl = plan_stage(P, l, GS_GATEUP, c.t, gw, gn);
+  const StagePlan pl = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
-    if (!await_all(P, X, l * kStagesPerLayer + 3, c.w, c.t)) return false;
+    if (!await_all<HO>(P, X, l * kStagesPerLayer + 3, c.w, c.t)) return false;
     if (!poll_f32(X + P.xl.xmid + (size_t)l * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_FFN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
     return true;
   };
-  const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, gw, gn);
-  // the ring holds this stage's first vectors (issued by Wo, or under the role
-  // split by the previous layer's down stage; not before layer 0)
-  const bool prefilled = !P.split || l > 0;
-  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, prefilled, tr, slot)) return false;
+  const StagePlan np = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
+  if (!gemv_cls<DT, VD>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.h + (size_t)l * F;
   publish_delay(P);
   for (int f = c.t; f < nf; f += kThreads) {
     const float gt = c.s.yv[f], up = c.s.yv[nf + f];
     xst32(dst + f0 + f, __float_as_uint(gt / (1.0f + expf(-gt)) * up));
   }
-  arrive(P, X, l * kStagesPerLayer + 4, c.t);
-  if (!P.per_stage) ring_prefetch(ring, np);
+  arrive<HO>(P, X, l * kStagesPerLayer + 4, c.t);
+  if constexpr (!PS) ring_prefetch(ring, np);
   stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // x_next = x_mid + Wd h
-template <int DT, int VF>
+template <int DT, int VF, bool HO, bool PS>
 __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
-  int gw, gn;
-  if (!stage_group(P, kGroupFfn, c.wg, c.nb, gw, gn)) {
-    arrive(P, X, l * kStagesPerLayer + 5, c.t);
-    return true;
-  }
   const int slot = l * kStagesPerLayer + 5;
   stamp(tr, slot, 0, c.t);
   const int d = P.d, F = P.F;
-  const int r0 = split_lo(d, gn, gw), r1 = split_lo(d, gn, gw + 1);
-  const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, gw, gn);
+  const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
+  const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
-    if (!await_all(P, X, l * kStagesPerLayer + 4, c.w, c.t)) return false;
+    if (!await_all<HO>(P, X, l * kStagesPerLayer + 4, c.w, c.t)) return false;
     const bool r = poll_to16<DT>(X + P.xl.h + (size_t)l * F, F, c.s.xn, c.w, c.t);
     stamp(tr, slot, 1, c.t);
     return r;
   };
-  // the next stage this work-group runs: the next layer's QKV, or under the
-  // role split its gate/up (the LM head after the last layer)
-  const StagePlan np = l + 1 < P.L ? plan_stage(P, l + 1, P.split ? GS_GATEUP : GS_QKV, c.t, gw, gn)
+  const StagePlan np = l + 1 < P.L ? plan_stage(P, l + 1, GS_QKV, c.t, c.wg, c.nb)
                                    : plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
   if (!gemv_cls<DT, VF>(pl, prep, c.s.xn, c.s.red, c.s.yv, c.t, ring, true, tr, slot)) return false;
   uint32_t* dst = X + P.xl.xout + (size_t)l * d;
   publish_delay(P);
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
-  arrive(P, X, l * kStagesPerLayer + 5, c.t);
-  if (!P.per_stage) ring_prefetch(ring, np);
+  arrive<HO>(P, X, l * kStagesPerLayer + 5, c.t);
+  if constexpr (!PS) ring_prefetch(ring, np);
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -1329,7 +1274,7 @@ __device__ KIE_INLINE bool sampled_token(const Params* Pp, char* smem, uint32_t*
 
 // LM head on this work-group's vocabulary rows; logits optionally written.
 // The host guarantees ceil(V / grid) rows fit the LDS partial-sum buffers.
-template <int DT, int VD>
+template <int DT, int VD, bool HO>
 __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, float* logits, float& best_v,
                                      int& best_i, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
@@ -1340,7 +1285,7 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
   const int v0 = split_lo(V, c.nb, c.wg), v1 = split_lo(V, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
   auto prep = [&]() -> bool {
-    if (!await_all(P, X, (P.L - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
+    if (!await_all<HO>(P, X, (P.L - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
     if (!poll_f32(X + P.xl.xout + (size_t)(P.L - 1) * d, d, c.s.xres, c.w, c.t)) return false;
     rmsnorm_to16<DT>(c.s.xres, P.final_norm, d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
@@ -1406,6 +1351,7 @@ __device__ KIE_INLINE void reset_set(const Params* Pp, char* smem, uint32_t* Xr,
 // Gather the per-work-group (max, index) partials -> the greedy token (also
 // the end-of-step marker when sampling chooses the token instead).  Every
 // work-group reduces the same values in the same order, so all agree.
+template <bool HO>
 __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* X, int& tok, uint64_t* tr) {
   const Sc c = stage_ctx(Pp, smem);
   const int slot = c.P.L * kStagesPerLayer + 1;
@@ -1414,7 +1360,7 @@ __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* 
   float gv = -INFINITY;
   int gi = 0x7FFFFFFF;
   bool ok = true;
-  if (!await_all(P, X, P.L * kStagesPerLayer, c.w, c.t)) return false;
+  if (!await_all<HO>(P, X, P.L * kStagesPerLayer, c.w, c.t)) return false;
   for (int w = c.t; w < c.nb && c.t < kThreads / 2; w += kThreads / 2) {
     uint64_t v = 0;
     if (ok && poll64(X + P.xl.arg + 2 * w, v, c.w, Ready32x2{})) {
@@ -1440,7 +1386,9 @@ __device__ KIE_INLINE bool gather_token(const Params* Pp, char* smem, uint32_t* 
 // ---------------------------------------------------------------------------
 // The persistent kernel
 // ---------------------------------------------------------------------------
-template <int DT, int G, int VD, int VF>
+// HO: the arrival-counter hand-off (the comparison protocol) instead of the
+// NaN-polled data alone.
+template <int DT, int G, int VD, int VF, bool HO>
 __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restrict__ Pp) {
   extern __shared__ __align__(16) char smem[];
   const int t = threadIdx.x, wg = blockIdx.x;
@@ -1455,16 +1403,21 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     if (P.forced) tok = P.forced[s];
     uint32_t* X = P.xch + (size_t)(s % kRingSets) * P.xl.words;
     uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace : nullptr;
-    {  // embedding row -> residual stream
+    const bool lm_only = cparams(Pp).lm_only != 0;
+    if (lm_only) {  // the LM head's first weight vectors (no down stage issued them)
+      const Sc c = stage_ctx(Pp, smem);
+      ring_prefetch(ring, plan_stage(c.P, 0, GS_LM, c.t, c.wg, c.nb));
+    } else {  // embedding row -> residual stream
       const Sc c = stage_ctx(Pp, smem);
       const uint16_t* er = c.P.tok_emb + (size_t)tok * c.P.d;
       for (int i = c.t; i < c.P.d; i += kThreads) c.s.xres[i] = to_f32<DT>(er[i]);
       __syncthreads();
     }
-    for (int l = 0; l < L && ok; ++l) {
-      ok = st_qkv<DT, VD>(Pp, smem, l, X, tr, ring) && st_attn<DT, G>(Pp, smem, l, pos, X, tr) &&
-           st_merge<DT>(Pp, smem, l, pos, X, tr) && st_wo<DT, VD>(Pp, smem, l, X, tr, ring) &&
-           st_gateup<DT, VD>(Pp, smem, l, X, tr, ring) && st_down<DT, VF>(Pp, smem, l, X, tr, ring);
+    for (int l = 0; l < L && ok && !lm_only; ++l) {
+      ok = st_qkv<DT, VD, HO>(Pp, smem, l, X, tr, ring) && st_attn<DT, G, HO>(Pp, smem, l, pos, X, tr) &&
+           st_merge<DT, HO>(Pp, smem, l, pos, X, tr) && st_wo<DT, VD, HO, false>(Pp, smem, l, X, tr, ring) &&
+           st_gateup<DT, VD, HO, false>(Pp, smem, l, X, tr, ring) &&
+           st_down<DT, VF, HO, false>(Pp, smem, l, X, tr, ring);
     }
     if (!ok) break;
     float bv = 0.f;
@@ -1475,7 +1428,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       lm = !Q.lm_last_only || s == Q.n_steps - 1;
       if (lm) {
         float* lg = Q.logits ? Q.logits + (size_t)(Q.lm_last_only ? 0 : s) * Q.V : nullptr;
-        if (!st_lmhead<DT, VD>(Pp, smem, X, lg, bv, bi, tr, ring)) {
+        if (!st_lmhead<DT, VD, HO>(Pp, smem, X, lg, bv, bi, tr, ring)) {
           ok = false;
           break;
         }
@@ -1486,7 +1439,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     publish_delay(cparams(Pp));
     __syncthreads();
     if (t == 0 && wg != Pp->withhold_wg) xst64(X + Pp->xl.arg + 2 * wg, pack2f(bv, __int_as_float(bi)));
-    arrive(cparams(Pp), X, L * kStagesPerLayer, t);
+    arrive<HO>(cparams(Pp), X, L * kStagesPerLayer, t);
     // the upper half of the work-group recycles the previous step's exchange
     // set while the lower half gathers the partials (grid <= kThreads / 2)
     if (s >= 1) {
@@ -1494,7 +1447,7 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
       attn_chunking(cparams(Pp), pos, CL, nch);
       reset_set(Pp, smem, Pp->xch + (size_t)((s + 2) % kRingSets) * Pp->xl.words, nch, kThreads / 2, tr);
     }
-    if (!gather_token(Pp, smem, X, tok, tr)) {
+    if (!gather_token<HO>(Pp, smem, X, tok, tr)) {
       ok = false;
       break;
     }
@@ -1546,30 +1499,30 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __rest
     case 0:
       if (l == 0) load_embedding();
       else own_prefetch(l, GS_QKV);
-      ok = st_qkv<DT, VD>(Pp, smem, l, X, nullptr, ring);
+      ok = st_qkv<DT, VD, false>(Pp, smem, l, X, nullptr, ring);
       break;
-    case 1: ok = st_attn<DT, G>(Pp, smem, l, pos, X, nullptr); break;
-    case 2: ok = st_merge<DT>(Pp, smem, l, pos, X, nullptr); break;
+    case 1: ok = st_attn<DT, G, false>(Pp, smem, l, pos, X, nullptr); break;
+    case 2: ok = st_merge<DT, false>(Pp, smem, l, pos, X, nullptr); break;
     case 3:  // the residual x_l that the Wo outputs add to
       if (l == 0) load_embedding();
       else ok = poll_f32(X + P.xl.xout + (size_t)(l - 1) * P.d, P.d, c.s.xres, c.w, c.t);
-      ok = ok && st_wo<DT, VD>(Pp, smem, l, X, nullptr, ring);
+      ok = ok && st_wo<DT, VD, false, true>(Pp, smem, l, X, nullptr, ring);
       break;
     case 4:
       own_prefetch(l, GS_GATEUP);
-      ok = st_gateup<DT, VD>(Pp, smem, l, X, nullptr, ring);
+      ok = st_gateup<DT, VD, false, true>(Pp, smem, l, X, nullptr, ring);
       break;
     case 5:  // the residual x_mid that the down outputs add to
       ok = poll_f32(X + P.xl.xmid + (size_t)l * P.d, P.d, c.s.xres, c.w, c.t);
       own_prefetch(l, GS_DOWN);
-      ok = ok && st_down<DT, VF>(Pp, smem, l, X, nullptr, ring);
+      ok = ok && st_down<DT, VF, false, true>(Pp, smem, l, X, nullptr, ring);
       break;
     case 6: {
       own_prefetch(0, GS_LM);
       float bv = 0.f;
       int bi = 0;
       float* lg = P.logits ? P.logits + (size_t)s * P.V : nullptr;
-      ok = st_lmhead<DT, VD>(Pp, smem, X, lg, bv, bi, nullptr, ring);
+      ok = st_lmhead<DT, VD, false>(Pp, smem, X, lg, bv, bi, nullptr, ring);
       drain_stores();
       __syncthreads();
       if (ok && c.t == 0) xst64(X + P.xl.arg + 2 * c.wg, pack2f(bv, __int_as_float(bi)));
@@ -1582,7 +1535,7 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __rest
         reset_set(Pp, smem, P.xch + (size_t)((s + 2) % kRingSets) * P.xl.words, nch, kThreads / 2, nullptr);
       }
       int tok = 0;
-      ok = gather_token(Pp, smem, X, tok, nullptr);
+      ok = gather_token<false>(Pp, smem, X, tok, nullptr);
       if (ok && c.wg == 0 && c.t == 0) {
         Pp->tok_out[s] = tok;
         Pp->ctl[CTL_DONE] = (uint32_t)(s + 1);

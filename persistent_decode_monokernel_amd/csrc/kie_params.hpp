@@ -20,7 +20,6 @@ constexpr int kPadIdx = 0x40000000;      // sampling: indices of padding candida
 constexpr int kStagesPerLayer = 6;       // qkv, attn, merge, wo, gate/up, down
 constexpr int kTraceStamps = 4;          // per (slot, work-group): entry, input, compute done, exit
 constexpr int kHandoffNan = 0, kHandoffCounters = 1;
-constexpr int kGroupAttn = 0, kGroupFfn = 1;  // work-group roles under the role split
 
 // per-layer weight slots in the device pointer table
 enum : int {
@@ -69,18 +68,10 @@ struct Params {
   const int* forced;          // prompt tokens (prefill) or null
   // launch
   int pos0, n_steps, eos_id, in_tok, abort_after, lm_last_only, withhold_wg;
-  // hand-off protocol: 0 = the data is its own flag (NaN-filled buffers,
-  // consumers poll the words they need); 1 = arrival counters (every
-  // work-group adds one to a stage's counter once its outputs are performed,
-  // consumers wait for all arrivals before reading)
-  int handoff;
-  // 1: the stages run as separate launches (stage_kernel), so no stage
-  // prefetches the next one's weights (its registers do not survive the launch)
-  int per_stage;
-  // 1: role split -- the attention block (QKV, attention, merge, Wo) runs on
-  // the work-groups whose index has bit 3 clear, the feed-forward block
-  // (gate/up, down) on the others; the LM head and the step tail on all
-  int split;
+  // 1: one step that runs only the LM head and the token choice, on a final
+  // residual the host placed in exchange set 0's last-layer xout (the prompt
+  // path's last position); no layers, no embedding
+  int lm_only;
   // race test: work-group delay_wg waits delay_ticks (100 MHz) before it
   // publishes any hand-off output (-1: off)
   int delay_wg;

@@ -24,6 +24,8 @@ const void* monokernel_fn_bf16_g1(int vd, int vf);
 const void* monokernel_fn_bf16_g2(int vd, int vf);
 const void* monokernel_fn_bf16_g4(int vd, int vf);
 const void* monokernel_fn_bf16_g8(int vd, int vf);
+const void* monokernel_counters_fn_f16_g4(int vd, int vf);
+const void* monokernel_counters_fn_bf16_g4(int vd, int vf);
 const void* stage_kernel_fn_f16_g1(int vd, int vf);
 const void* stage_kernel_fn_f16_g2(int vd, int vf);
 const void* stage_kernel_fn_f16_g4(int vd, int vf);
@@ -184,6 +186,13 @@ const void* monokernel_fn(const kie_config& c) {
   return nullptr;
 }
 
+// The arrival-counter instance of a shape, or null where none is built.
+const void* monokernel_counters_fn(const kie_config& c) {
+  const int G = c.n_heads / c.n_kv_heads, vd = width_class(c.d_model), vf = width_class(c.d_ffn);
+  if (G != 4) return nullptr;
+  return c.dtype == KIE_F16 ? monokernel_counters_fn_f16_g4(vd, vf) : monokernel_counters_fn_bf16_g4(vd, vf);
+}
+
 // The per-stage instance of the same shape (one launch per stage).
 const void* stage_kernel_fn(const kie_config& c) {
   const int G = c.n_heads / c.n_kv_heads, vd = width_class(c.d_model), vf = width_class(c.d_ffn);
@@ -221,7 +230,6 @@ struct kie_engine {
   int delay_wg = -1;          // race test: work-group whose publications are delayed
   int handoff = kHandoffNan;  // hand-off protocol of the persistent launches
   int launch_mode = KIE_LAUNCH_PERSISTENT;  // kie_decode: persistent kernel or one launch per stage
-  int split = 0;              // role split of the work-groups (attention block / feed-forward block)
   uint64_t delay_ticks = 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   float last_ms = 0.f;
@@ -366,6 +374,9 @@ static kie_status create_impl(kie_engine* e, const kie_config* cfg, void* worksp
 
   const void* fn = monokernel_fn(*cfg);
   hipError_t he = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, e->lds.bytes);
+  // the arrival-counter instance, where this shape has one
+  if (he == hipSuccess && monokernel_counters_fn(*cfg))
+    he = hipFuncSetAttribute(monokernel_counters_fn(*cfg), hipFuncAttributeMaxDynamicSharedMemorySize, e->lds.bytes);
   int per_cu = 0;
   if (he == hipSuccess) he = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, e->lds.bytes);
   if (he != hipSuccess) return hip_fail(he, "occupancy");
@@ -524,8 +535,6 @@ static Params base_params(const kie_engine* e) {
   P.abort_after = -1;
   P.withhold_wg = e->withhold_wg;
   P.delay_wg = e->delay_wg;
-  P.handoff = e->handoff;
-  P.split = e->split;
   P.delay_ticks = e->delay_ticks;
   P.timeout = e->timeout;
   P.trace = e->trace;
@@ -542,17 +551,25 @@ static Params base_params(const kie_engine* e) {
 
 // Reset control words and exchange sets, launch the persistent kernel, wait,
 // and read back status / steps done / last token.
-static kie_status run_persistent(kie_engine* e, Params& P, int* done, int* last) {
+// x_last (device fp32, d_model values) or null: the final residual an
+// LM-head-only launch starts from, placed in set 0's last-layer xout.
+static kie_status run_persistent(kie_engine* e, Params& P, int* done, int* last, const float* x_last = nullptr) {
   KIE_HIP(launch_fill(P.ctl, CTL_WORDS, 0u, e->stream));
   KIE_HIP(launch_fill(P.xch, (uint64_t)kRingSets * P.xl.words, kSent, e->stream));
+  if (x_last)
+    KIE_HIP(hipMemcpyAsync(P.xch + P.xl.xout + (size_t)(P.L - 1) * P.d, x_last, (size_t)P.d * 4,
+                           hipMemcpyDeviceToDevice, e->stream));
   // The kernel reads its parameters from the workspace (scalar loads).
   Params* dev_params = reinterpret_cast<Params*>(e->ws + e->lay.params);
   e->params_host = P;  // stays valid until the copy below has run (the call synchronises)
   KIE_HIP(hipMemcpyAsync(dev_params, &e->params_host, sizeof(Params), hipMemcpyHostToDevice, e->stream));
   void* args[] = {&dev_params};
   if (e->ev0) KIE_HIP(hipEventRecord(e->ev0, e->stream));
-  KIE_HIP(hipLaunchCooperativeKernel(monokernel_fn(e->cfg), dim3(e->grid), dim3(kThreads), args,
-                                     (unsigned)e->lds.bytes, e->stream));
+  // the arrival-counter instance when chosen (not for an LM-head-only launch:
+  // no stage before it arrives at a counter)
+  const void* fn = e->handoff == kHandoffCounters && !P.lm_only ? monokernel_counters_fn(e->cfg)
+                                                                 : monokernel_fn(e->cfg);
+  KIE_HIP(hipLaunchCooperativeKernel(fn, dim3(e->grid), dim3(kThreads), args, (unsigned)P.lds_bytes, e->stream));
   if (e->ev1) KIE_HIP(hipEventRecord(e->ev1, e->stream));
   uint32_t ctl[4] = {0, 0, 0, 0};
   KIE_HIP(hipMemcpyAsync(ctl, P.ctl, sizeof(ctl), hipMemcpyDeviceToHost, e->stream));
@@ -626,20 +643,6 @@ static kie_status run_per_stage(kie_engine* e, Params& P, int* done, int* last) 
   return ctl[CTL_STATUS] == 0 ? KIE_OK : KIE_ERR_TIMEOUT;
 }
 
-// The role split needs a grid of whole 16-work-group blocks (8 of each role
-// per block, one per XCD) and a tiling that fits half the grid.
-static bool split_fits(const kie_engine* e, int grid) {
-  return grid >= 16 && grid % 16 == 0 && grid_fits(e->cfg, e->lay, grid / 2) &&
-         kie_check_tiling(&e->cfg, grid / 2, 0) == KIE_OK;
-}
-
-extern "C" kie_status kie_set_split(kie_engine* e, int32_t on) {
-  if (!e || (on != 0 && on != 1)) return KIE_ERR_ARG;
-  if (on && !split_fits(e, e->grid)) return KIE_ERR_UNSUPPORTED;
-  e->split = on;
-  return KIE_OK;
-}
-
 extern "C" kie_status kie_set_launch_mode(kie_engine* e, int32_t mode) {
   if (!e || (mode != KIE_LAUNCH_PERSISTENT && mode != KIE_LAUNCH_PER_STAGE && mode != KIE_LAUNCH_PER_STAGE_GRAPH))
     return KIE_ERR_ARG;
@@ -658,9 +661,11 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
   e->have_seq = false;
   KIE_HIP(hipMemcpyAsync(e->ws + e->lay.forced, prompt_host, (size_t)n_prompt * 4, hipMemcpyHostToDevice, e->stream));
   const int* forced = reinterpret_cast<const int*>(e->ws + e->lay.forced);
-  // positions 0 .. n_prompt-2 on the matrix cores (when the shape allows), the
-  // last one -- or all of them -- as forced steps of the persistent kernel
+  // every position on the matrix cores (when the shape allows), then one
+  // persistent launch that runs only the LM head on the last position's
+  // residual; else every position as a forced step of the persistent kernel
   int first = 0;
+  const float* x_last = nullptr;
   if (e->prefill_mode == KIE_PREFILL_AUTO && e->lay.pf_chunk > 0 && n_prompt >= 2) {
     const kie_config& c = e->cfg;
     PrefillCtx x{};
@@ -677,25 +682,32 @@ extern "C" kie_status kie_prefill(kie_engine* e, const int32_t* prompt_host, int
     x.A = e->ws + e->lay.pf_a;
     x.H = e->ws + e->lay.pf_h;
     x.P = reinterpret_cast<float*>(e->ws + e->lay.pf_p);
-    first = n_prompt - 1;
     const int chunk = e->prefill_chunk > 0 ? e->prefill_chunk : e->lay.pf_chunk;
-    for (int p0 = 0; p0 < first; p0 += chunk) {
-      const int M = first - p0 < chunk ? first - p0 : chunk;
+    int M = 0;
+    for (int p0 = 0; p0 < n_prompt; p0 += chunk) {
+      M = n_prompt - p0 < chunk ? n_prompt - p0 : chunk;
       KIE_HIP(prefill_chunk(x, forced + p0, p0, M));
     }
+    x_last = x.X + (size_t)(M - 1) * c.d_model;  // the last chunk's last row
+    first = n_prompt - 1;
   }
   Params P = base_params(e);
-  P.forced = forced + first;
   P.pos0 = first;
-  P.n_steps = n_prompt - first;
   P.eos_id = -1;
   P.in_tok = prompt_host[first];
   P.lm_last_only = 1;
   P.logits = logits_dev;
+  if (x_last) {  // the LM head alone
+    P.lm_only = 1;
+    P.n_steps = 1;
+  } else {
+    P.forced = forced;
+    P.n_steps = n_prompt;
+  }
   int done = 0, last = 0;
-  const kie_status st = run_persistent(e, P, &done, &last);
+  const kie_status st = run_persistent(e, P, &done, &last, x_last);
   if (st != KIE_OK) return st;
-  if (done != n_prompt - first) return KIE_ERR_TIMEOUT;
+  if (done != P.n_steps) return KIE_ERR_TIMEOUT;
   e->pos = n_prompt;
   e->pending = last;
   e->have_seq = true;
@@ -715,7 +727,6 @@ extern "C" kie_status kie_set_grid(kie_engine* e, int32_t grid) {
   if (grid == 0) grid = full;
   if (grid > full) return KIE_ERR_ARG;
   if (!grid_fits(e->cfg, e->lay, grid) || kie_check_tiling(&e->cfg, grid, 0) != KIE_OK) return KIE_ERR_UNSUPPORTED;
-  if (e->split && !split_fits(e, grid)) return KIE_ERR_UNSUPPORTED;
   e->grid = grid;
   return KIE_OK;
 }
@@ -768,10 +779,7 @@ extern "C" kie_status kie_decode(kie_engine* e, int32_t n_steps, int32_t eos_id,
   const bool per_stage = e->launch_mode != KIE_LAUNCH_PERSISTENT;
   if (per_stage) {
     // greedy, fixed step count, default hand-offs, no timeline
-    if (e->samp_k > 0 || P.eos_id >= 0 || abort_after >= 0 || e->withhold_wg >= 0 || e->split)
-      return KIE_ERR_UNSUPPORTED;
-    P.per_stage = 1;
-    P.handoff = kHandoffNan;
+    if (e->samp_k > 0 || P.eos_id >= 0 || abort_after >= 0 || e->withhold_wg >= 0) return KIE_ERR_UNSUPPORTED;
     P.trace = nullptr;
     P.delay_wg = -1;
   }
@@ -865,6 +873,7 @@ extern "C" kie_status kie_set_withhold(kie_engine* e, int32_t wg) {
 
 extern "C" kie_status kie_set_handoff(kie_engine* e, int32_t mode) {
   if (!e || (mode != KIE_HANDOFF_NAN_POLL && mode != KIE_HANDOFF_COUNTERS)) return KIE_ERR_ARG;
+  if (mode == KIE_HANDOFF_COUNTERS && !monokernel_counters_fn(e->cfg)) return KIE_ERR_UNSUPPORTED;
   e->handoff = mode == KIE_HANDOFF_COUNTERS ? kHandoffCounters : kHandoffNan;
   return KIE_OK;
 }

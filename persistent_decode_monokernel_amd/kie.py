@@ -102,7 +102,6 @@ SIGNATURES = {
     "kie_set_delay": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64]),
     "kie_set_handoff": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_set_launch_mode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
-    "kie_set_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kie_check_idle_sets": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64)]),
     "kie_trace_words": (ctypes.c_size_t, [ctypes.c_void_p]),
     "kie_set_trace": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32]),
@@ -359,10 +358,6 @@ class Engine:
     def set_launch_mode(self, mode: int):
         """KIE_LAUNCH_PERSISTENT (default), KIE_LAUNCH_PER_STAGE or KIE_LAUNCH_PER_STAGE_GRAPH."""
         _check(lib().kie_set_launch_mode(self._h, int(mode)), "kie_set_launch_mode")
-
-    def set_split(self, on: bool):
-        """Role split: attention block and feed-forward block on separate halves of the grid."""
-        _check(lib().kie_set_split(self._h, 1 if on else 0), "kie_set_split")
 
     def idle_sets_dirty_words(self) -> int:
         """Words of the two idle exchange sets that are not the NaN pattern after the last launch."""

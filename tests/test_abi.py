@@ -203,3 +203,4 @@ def test_synthetic_inputs_are_seeded():
     assert int(p.min()) >= 0 and int(p.max()) < s.vocab
     k, v = synth.make_kv(s, 8, 3)
     assert k.shape == (s.n_layers, s.n_kv_heads, 8, s.head_dim) and not torch.equal(k, v)
+

@@ -46,4 +46,5 @@ def test_bench_json_line(capsys, monkeypatch):
 
     c = d["cpu_baseline"]
     assert c is not None and c["kind"] == "oracle" and c["value"] > 0 and c["cores"] >= 1
+    assert "C++" in c["implementation"] and c["nproc"] >= c["cores"] and c["cpu_model"]
     assert c["unit"] == "tokens/s" and c["sample"]

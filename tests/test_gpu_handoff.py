@@ -2,8 +2,11 @@
 against the default NaN-polled hand-off: the same kernels do the same
 arithmetic in the same order, only the way consumers learn that their inputs
 are complete differs, so tokens and logits must agree bit for bit -- greedy and
-sampled, on the tiny decoder and the full-depth ~2B one -- and the exchange
-sets must still be recycled to the NaN pattern."""
+sampled, on the full-depth ~2B decoder and reduced-depth ~2B and ~8B-shaped
+ones (the shapes the counter instance is built for) -- and the exchange sets
+must still be recycled to the NaN pattern."""
+import dataclasses
+
 import pytest
 import torch
 
@@ -30,11 +33,12 @@ def _run(shape, w, prompt, n, handoff, max_seq, sampling=None):
         eng.close()
 
 
-@pytest.mark.parametrize("name,n_prompt,n_decode,sampled", [("tiny", 16, 24, False), ("tiny", 16, 24, True),
-                                                           ("2b", 64, 16, False)])
-def test_counters_match_nan_polls_bit_for_bit(name, n_prompt, n_decode, sampled):
+@pytest.mark.parametrize("name,layers,n_prompt,n_decode,sampled", [("2b", None, 64, 16, False),
+                                                                  ("2b", 4, 40, 16, True),
+                                                                  ("8b", 2, 40, 12, False)])
+def test_counters_match_nan_polls_bit_for_bit(name, layers, n_prompt, n_decode, sampled):
     wl = synth.WORKLOADS[name]
-    s = wl.shape
+    s = wl.shape if layers is None else dataclasses.replace(wl.shape, n_layers=layers)
     w = synth.make_weights(s, wl.weight_seed, device=DEV)
     prompt = synth.make_prompt(s, n_prompt, wl.prompt_seed).tolist()
     samp = (0.8, 32, 0.9, 5) if sampled else None
@@ -47,13 +51,18 @@ def test_counters_match_nan_polls_bit_for_bit(name, n_prompt, n_decode, sampled)
 
 
 def test_handoff_argument_checks():
-    s = synth.TINY
+    s = dataclasses.replace(synth.M2B, n_layers=1)
     eng = kie.Engine(s, max_seq=8, device=DEV)
     try:
         for bad in (-1, 2, 7):
-            with pytest.raises(kie.KieError):
-                eng.set_handoff(bad)
+            assert kie.lib().kie_set_handoff(eng._h, bad) == kie.KIE_ERR_ARG
         eng.set_handoff(kie.KIE_HANDOFF_COUNTERS)
+        eng.set_handoff(kie.KIE_HANDOFF_NAN_POLL)
+    finally:
+        eng.close()
+    eng = kie.Engine(synth.TINY, max_seq=8, device=DEV)  # no counter instance for this shape
+    try:
+        assert kie.lib().kie_set_handoff(eng._h, kie.KIE_HANDOFF_COUNTERS) == kie.KIE_ERR_UNSUPPORTED
         eng.set_handoff(kie.KIE_HANDOFF_NAN_POLL)
     finally:
         eng.close()

@@ -65,32 +65,40 @@ def bytes_per_launch(s, pos0: int, n_steps: int) -> int:
 # device-to-device copy of known size (--copy-probe).  Reported only while the
 # kernel sources hash to the value they were taken at.
 MEASURED_TRAFFIC = {
-    # kie_decode(1024) after a 512-token prefill, FETCH_SIZE x 2.0, WRITE_SIZE x 1.0
-    "2b": {"src_sha": "52a12879a002613b", "steps": 1024,
-           "fetch_bytes": 1856886984 * 1024 * 2, "write_bytes": 33793986 * 1024},
+    # (workload, timed steps): the timed kie_decode after the 512-token prefill,
+    # FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 (KiB per dispatch x 1024)
+    ("2b", 1024): {"src_sha": "66bd813344da8999",
+                   "fetch_bytes": 1857109187 * 1024 * 2, "write_bytes": 33028477 * 1024},
+    # the same command as `--gpus 1 --steps 20 --warmup 5`
+    ("2b", 20): {"src_sha": "66bd813344da8999",
+                 "fetch_bytes": 35835152 * 1024 * 2, "write_bytes": 417800 * 1024},
 }
 
 KERNEL_SRC_DIR = os.path.join(ROOT, "persistent_decode_monokernel_amd", "csrc")
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources the decode kernel and its launch code are built from
-    (the prompt-path kernels excluded): stored counter readings count only
+    """Hash of the code the decode kernel and its launch code are built from
+    (the prompt-path kernels excluded; comments and blank space ignored, so a
+    comment edit keeps stored readings): stored counter readings count only
     while it matches."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SRC_DIR)):
         if name.endswith((".hip", ".hpp", ".h")) and not name.startswith("kie_prefill"):
+            with open(os.path.join(KERNEL_SRC_DIR, name)) as f:
+                code = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
             h.update(name.encode())
-            with open(os.path.join(KERNEL_SRC_DIR, name), "rb") as f:
-                h.update(f.read())
+            h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, steps: int):
-    m = MEASURED_TRAFFIC.get(workload)
-    if not m or m["steps"] != steps or m["src_sha"] != kernel_source_hash():
+    m = MEASURED_TRAFFIC.get((workload, steps))
+    if not m or m["src_sha"] != kernel_source_hash():
         return None
     return m["fetch_bytes"] + m["write_bytes"]
 

@@ -136,10 +136,11 @@ __device__ __forceinline__ Sc stage_ctx(const Params* Pp, char* smem) {
 // Work-group-wide "any thread failed" with a barrier.
 __device__ __forceinline__ bool any_failed(bool failed) { return __syncthreads_or(failed ? 1 : 0) != 0; }
 
-// Arrival-counter hand-off (the comparison protocol; off by default).  Counter
-// k of an exchange set starts at kSent like every other word; each work-group
-// adds one once all its outputs of stage k are performed, so the counter reads
-// kSent + grid when every work-group has arrived.
+// Arrival-counter hand-off: the comparison protocol, compiled in only for the
+// kernel instances built with HO = true (both functions are empty otherwise).
+// Counter k of an exchange set starts at kSent like every other word; each
+// work-group adds one once all its outputs of stage k are performed, so the
+// counter reads kSent + grid when every work-group has arrived.
 template <bool HO>
 __device__ __forceinline__ void arrive(CParams& P, uint32_t* X, int k, int t) {
   if constexpr (!HO) return;
@@ -826,7 +827,9 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
   return !failed;
 }
 
-// x_mid = x_l + Wo a  (rows split over work-groups)
+// x_mid = x_l + Wo a  (rows split over work-groups).  PS (here and in the
+// feed-forward stages): the stage runs as a launch of its own (stage_kernel),
+// so it issues no weights for the next stage -- its registers end with it.
 template <int DT, int VD, bool HO, bool PS>
 __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);

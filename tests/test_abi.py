@@ -171,13 +171,13 @@ def test_bytes_per_token_8b():
 
 
 def test_measured_traffic_tracks_sources():
-    m = bench.MEASURED_TRAFFIC["2b"]
-    t = bench.measured_traffic("2b", m["steps"] + 1)
-    assert t is None  # other launch size
-    if m["src_sha"] == bench.kernel_source_hash():
-        assert bench.measured_traffic("2b", m["steps"]) == m["fetch_bytes"] + m["write_bytes"]
-    else:
-        assert bench.measured_traffic("2b", m["steps"]) is None
+    assert bench.MEASURED_TRAFFIC
+    for (wl, steps), m in bench.MEASURED_TRAFFIC.items():
+        assert bench.measured_traffic(wl, steps + 1) is None  # another launch size
+        if m["src_sha"] == bench.kernel_source_hash():
+            assert bench.measured_traffic(wl, steps) == m["fetch_bytes"] + m["write_bytes"]
+        else:
+            assert bench.measured_traffic(wl, steps) is None
 
 
 def test_bench_refuses_several_gpus():

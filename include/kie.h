@@ -356,6 +356,9 @@ kie_status kie_set_handoff(kie_engine* e, int32_t mode);
  *     token (6 per layer, the LM head, the token), queued from a host loop.
  *   KIE_LAUNCH_PER_STAGE_GRAPH: the same launches captured once into a HIP
  *     graph and replayed as one graph launch (capture before the timing).
+ *     Each call creates a capture stream and a graph of 6 x n_layers + 2
+ *     nodes per step (host-side HIP objects, released before it returns): a
+ *     measurement mode, not for callers that cannot allocate.
  * The per-stage modes take greedy decode with eos_id < 0 and no fault
  * injection (else KIE_ERR_UNSUPPORTED); tokens and logits equal the
  * persistent kernel's bit for bit.  KIE_ERR_ARG for another mode. */

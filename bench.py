@@ -79,15 +79,15 @@ KERNEL_SRC_DIR = os.path.join(ROOT, "persistent_decode_monokernel_amd", "csrc")
 
 def kernel_source_hash() -> str:
     """Hash of the code the decode kernel and its launch code are built from
-    (the prompt-path kernels excluded; comments and blank space ignored, so a
-    comment edit keeps stored readings): stored counter readings count only
-    while it matches."""
+    (the prompt-path kernels and the hand-off probe excluded; comments and
+    blank space ignored, so a comment edit keeps stored readings): stored
+    counter readings count only while it matches."""
     import hashlib
     import re
 
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SRC_DIR)):
-        if name.endswith((".hip", ".hpp", ".h")) and not name.startswith("kie_prefill"):
+        if name.endswith((".hip", ".hpp", ".h")) and not name.startswith(("kie_prefill", "kie_handoff_probe")):
             with open(os.path.join(KERNEL_SRC_DIR, name)) as f:
                 code = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
             code = re.sub(r"//[^\n]*", " ", code)
@@ -211,6 +211,67 @@ def stream_peak(depths=(3,), reps: int = 16, verbose: bool = False) -> float:
     del buf
     torch.cuda.empty_cache()
     return best
+
+
+def handoff_probe_bench(runs: int = 5):
+    """Cost of one exchange between work-groups in the decode kernel's form
+    (8-byte agent-scope store, agent-scope polls): a ping between two
+    work-groups on different and on the same XCD, and an all-to-all round over
+    the whole grid, each idle and beside non-temporal streaming of a 1 GiB
+    buffer by the other work-groups and/or by the exchanging work-groups' own
+    waves 1..7.  One JSON line per case: median over `runs` launches."""
+    import statistics
+
+    import torch
+
+    from persistent_decode_monokernel_amd import kie
+
+    buf = torch.ones(STREAM_BYTES // 2, dtype=torch.float16, device="cuda")
+    scratch = torch.zeros(kie.KIE_HANDOFF_PROBE_SCRATCH_BYTES // 8, dtype=torch.int64, device="cuda")
+    where_name = {kie.KIE_PROBE_STREAM_NONE: "none", kie.KIE_PROBE_STREAM_OTHERS: "other work-groups",
+                  kie.KIE_PROBE_STREAM_OWN: "own waves 1..7",
+                  kie.KIE_PROBE_STREAM_OTHERS | kie.KIE_PROBE_STREAM_OWN: "all work-groups"}
+    kie.handoff_probe(kie.KIE_PROBE_PING, rounds=50, scratch=scratch)  # warm-up
+    # a partner on another XCD and one on the same XCD as work-group 0
+    first = kie.handoff_probe(kie.KIE_PROBE_PING, rounds=50, wg_a=0, wg_b=1, scratch=scratch)
+    same = None
+    for b in range(2, min(first.grid, 32)):
+        r = kie.handoff_probe(kie.KIE_PROBE_PING, rounds=20, wg_a=0, wg_b=b, scratch=scratch)
+        if r.xcc_b == r.xcc_a:
+            same = b
+            break
+    cases = [(kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_NONE, 3)]
+    if same is not None:
+        cases.append((kie.KIE_PROBE_PING, same, kie.KIE_PROBE_STREAM_NONE, 3))
+    cases += [(kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OTHERS, 3),
+              (kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OWN, 1),
+              (kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OWN, 3),
+              (kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OWN, 8),
+              (kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OTHERS | kie.KIE_PROBE_STREAM_OWN, 3),
+              (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_NONE, 3),
+              (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_OWN, 1),
+              (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_OWN, 3),
+              (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_OWN, 8)]
+    for kind, b, where, depth in cases:
+        rounds = 400 if kind == kie.KIE_PROBE_PING else 200
+        res = [kie.handoff_probe(kind, rounds=rounds, wg_a=0, wg_b=b, where=where, depth=depth, buf=buf,
+                                 scratch=scratch) for _ in range(runs)]
+        line = {"handoff_probe": "ping" if kind == kie.KIE_PROBE_PING else "all-to-all", "grid": res[0].grid,
+                "rounds": rounds, "streaming": where_name[where],
+                "loads_in_flight_per_thread": depth if where else 0,
+                "us_per_round": statistics.median(r.exchange_us for r in res),
+                "runs_us": [round(r.exchange_us, 3) for r in res],
+                "completed": all(r.completed for r in res)}
+        if kind == kie.KIE_PROBE_PING:
+            line.update({"wg_a": 0, "wg_b": b, "xcd_a": res[0].xcc_a, "xcd_b": res[0].xcc_b,
+                         "same_xcd": res[0].xcc_a == res[0].xcc_b})
+        else:
+            line["slowest_wg_us_per_round"] = statistics.median(r.exchange_max_us for r in res)
+        if where:
+            line["stream_GBps"] = statistics.median(r.stream_gbps for r in res)
+        print(json.dumps(line), flush=True)
+    del buf
+    torch.cuda.empty_cache()
 
 
 def ablation(name: str, steps: int = 64):
@@ -477,6 +538,8 @@ def main():
                     help="only compare the persistent kernel (NaN polls, arrival counters) with one launch per stage")
     ap.add_argument("--stream", action="store_true",
                     help="only run the read-stream probe (1, 2, 3, 4, 6, 8 loads in flight per thread)")
+    ap.add_argument("--handoff-probe", action="store_true",
+                    help="only time work-group exchanges (ping, all-to-all) idle and beside streaming")
     ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")
     ap.add_argument("--pf-chunk", type=int, nargs="+", default=[0],
                     help="with --ttft: matrix-core chunk sizes to time (0 = default)")
@@ -508,6 +571,9 @@ def main():
         return
     if args.stream:
         stream_peak(depths=(1, 2, 3, 4, 6, 8), verbose=True)
+        return
+    if args.handoff_probe:
+        handoff_probe_bench()
         return
     if args.ablation:
         ablation(args.workload, args.steps or 64)

@@ -433,6 +433,55 @@ kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t
 kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, int32_t reps,
                             uint32_t* sink_dev, void* hip_stream, float* kernel_ms);
 
+/* ---- hand-off latency probe ---------------------------------------------- */
+
+/* The cost of one exchange between work-groups, which the persistent kernel
+ * pays at every stage boundary in place of a kernel launch (revietech.ru page,
+ * section "Chto takoye monokernel": the work stays resident and work-groups
+ * synchronise through memory).  ONE cooperative launch of one work-group of
+ * 512 threads per compute unit uses the decode kernel's exchange form: 8-byte
+ * agent-scope stores polled with agent-scope loads, s_sleep 1 between polls.
+ *   KIE_PROBE_PING: work-groups wg_a and wg_b (distinct, < grid) trade
+ *     `rounds` round trips, one thread each: a stores round r, b answers once
+ *     it sees r.  exchange_us = mean round trip.
+ *   KIE_PROBE_ALL_TO_ALL: every work-group publishes round r in its own word
+ *     and waits until all grid words hold r (wave 0; each lane polls grid/64
+ *     words together).  exchange_us = mean over work-groups of the mean round,
+ *     exchange_max_us = the slowest work-group's.  wg_a, wg_b are ignored.
+ * Two untimed rounds come first.  stream_where adds non-temporal dwordx4
+ * streaming of buf_dev (stream_depth = 1, 2, 3, 4 or 8 loads in flight per
+ * thread) by KIE_PROBE_STREAM_OTHERS (all threads of the work-groups that do
+ * not exchange; ping only) and/or KIE_PROBE_STREAM_OWN (waves 1..7 of the
+ * exchanging work-groups), until the exchange ends; stream_gbps = their read
+ * rate over their common window.  buf_dev: 16-byte aligned, at least
+ * grid * 512 * 16 * 33 * stream_depth bytes (KIE_ERR_CAPACITY below), unused
+ * with KIE_PROBE_STREAM_NONE.  scratch_dev: device memory of at least
+ * KIE_HANDOFF_PROBE_SCRATCH_BYTES, cleared by the call.  Each wait gives up
+ * after 10 ms (completed = 0 then).  xcc_a, xcc_b: the accelerator die (XCD)
+ * work-groups a and b (all-to-all: 0 and 1) ran on.  Runs on hip_stream and
+ * synchronises it.  KIE_ERR_ARG for arguments out of range. */
+enum {
+  KIE_PROBE_PING = 0,
+  KIE_PROBE_ALL_TO_ALL = 1,
+  KIE_PROBE_STREAM_NONE = 0,
+  KIE_PROBE_STREAM_OTHERS = 1,
+  KIE_PROBE_STREAM_OWN = 2
+};
+#define KIE_HANDOFF_PROBE_SCRATCH_BYTES (64u * 1024u)
+typedef struct {
+  double exchange_us;
+  double exchange_max_us;
+  double stream_gbps;
+  int32_t xcc_a, xcc_b;
+  int32_t completed;
+  int32_t grid;
+} kie_handoff_probe_result;
+
+kie_status kie_handoff_probe(int32_t kind, int32_t wg_a, int32_t wg_b, int32_t rounds,
+                             int32_t stream_depth, int32_t stream_where, const void* buf_dev,
+                             size_t bytes, uint64_t* scratch_dev, size_t scratch_bytes,
+                             void* hip_stream, kie_handoff_probe_result* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,6 +35,12 @@ KIE_LAUNCH_PERSISTENT = 0
 KIE_LAUNCH_PER_STAGE = 1
 KIE_LAUNCH_PER_STAGE_GRAPH = 2
 KIE_STATIC_WORKSPACE_BYTES = 64 << 20  # include/kie.h
+KIE_PROBE_PING = 0
+KIE_PROBE_ALL_TO_ALL = 1
+KIE_PROBE_STREAM_NONE = 0
+KIE_PROBE_STREAM_OTHERS = 1
+KIE_PROBE_STREAM_OWN = 2
+KIE_HANDOFF_PROBE_SCRATCH_BYTES = 64 * 1024  # include/kie.h
 
 
 class KieError(RuntimeError):
@@ -68,6 +74,14 @@ class kie_info(ctypes.Structure):
         ("grid", ctypes.c_int32), ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
         ("cu_count", ctypes.c_int32), ("attn_max_chunks", ctypes.c_int32), ("pos", ctypes.c_int32),
         ("last_kernel_ms", ctypes.c_float), ("last_steps", ctypes.c_int32),
+    ]
+
+
+class kie_handoff_probe_result(ctypes.Structure):
+    _fields_ = [
+        ("exchange_us", ctypes.c_double), ("exchange_max_us", ctypes.c_double), ("stream_gbps", ctypes.c_double),
+        ("xcc_a", ctypes.c_int32), ("xcc_b", ctypes.c_int32), ("completed", ctypes.c_int32),
+        ("grid", ctypes.c_int32),
     ]
 
 
@@ -111,6 +125,10 @@ SIGNATURES = {
     "kie_gemv_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
+    "kie_handoff_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.POINTER(kie_handoff_probe_result)]),
 }
 
 _lib = None
@@ -393,3 +411,19 @@ def stream_probe(buf: torch.Tensor, depth: int = 3, reps: int = 4, stream=None) 
     npass = nbytes // 16 // grid // 512
     read = grid * 512 * 16 * (npass // depth * depth) * reps  # whole rounds of `depth` passes
     return ms.value, read
+
+
+def handoff_probe(kind: int, rounds: int = 200, wg_a: int = 0, wg_b: int = 1, where: int = KIE_PROBE_STREAM_NONE,
+                  depth: int = 3, buf: Optional[torch.Tensor] = None, scratch: Optional[torch.Tensor] = None,
+                  stream=None) -> kie_handoff_probe_result:
+    """Hand-off latency probe (ping between work-groups wg_a and wg_b, or an
+    all-to-all round over the grid), optionally beside streaming of `buf`."""
+    if scratch is None:
+        scratch = torch.zeros(KIE_HANDOFF_PROBE_SCRATCH_BYTES // 8, dtype=torch.int64, device="cuda")
+    nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+    r = kie_handoff_probe_result()
+    _check(lib().kie_handoff_probe(int(kind), int(wg_a), int(wg_b), int(rounds), int(depth), int(where),
+                                   ctypes.c_void_p(0 if buf is None else _dptr(buf)), nbytes,
+                                   ctypes.c_void_p(_dptr(scratch)), scratch.numel() * scratch.element_size(),
+                                   ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(r)), "kie_handoff_probe")
+    return r

@@ -219,7 +219,9 @@ def handoff_probe_bench(runs: int = 5):
     work-groups on different and on the same XCD, and an all-to-all round over
     the whole grid, each idle and beside non-temporal streaming of a 1 GiB
     buffer by the other work-groups and/or by the exchanging work-groups' own
-    waves 1..7.  One JSON line per case: median over `runs` launches."""
+    waves 1..7; the idle all-to-all also with its words spread 2 and 16 words
+    apart (fewer producers per 128-byte line).  One JSON line per case: median
+    over `runs` launches."""
     import statistics
 
     import torch
@@ -249,13 +251,16 @@ def handoff_probe_bench(runs: int = 5):
               (kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OWN, 8),
               (kie.KIE_PROBE_PING, 1, kie.KIE_PROBE_STREAM_OTHERS | kie.KIE_PROBE_STREAM_OWN, 3),
               (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_NONE, 3),
+              (kie.KIE_PROBE_ALL_TO_ALL, -2, kie.KIE_PROBE_STREAM_NONE, 3),
+              (kie.KIE_PROBE_ALL_TO_ALL, -16, kie.KIE_PROBE_STREAM_NONE, 3),
               (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_OWN, 1),
               (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_OWN, 3),
               (kie.KIE_PROBE_ALL_TO_ALL, 0, kie.KIE_PROBE_STREAM_OWN, 8)]
     for kind, b, where, depth in cases:
         rounds = 400 if kind == kie.KIE_PROBE_PING else 200
-        res = [kie.handoff_probe(kind, rounds=rounds, wg_a=0, wg_b=b, where=where, depth=depth, buf=buf,
-                                 scratch=scratch) for _ in range(runs)]
+        stride = -b if kind == kie.KIE_PROBE_ALL_TO_ALL and b < 0 else 1  # all-to-all: b < 0 = slot stride
+        res = [kie.handoff_probe(kind, rounds=rounds, wg_a=0, wg_b=max(b, 1), where=where, depth=depth, buf=buf,
+                                 scratch=scratch, stride=stride) for _ in range(runs)]
         line = {"handoff_probe": "ping" if kind == kie.KIE_PROBE_PING else "all-to-all", "grid": res[0].grid,
                 "rounds": rounds, "streaming": where_name[where],
                 "loads_in_flight_per_thread": depth if where else 0,
@@ -266,12 +271,74 @@ def handoff_probe_bench(runs: int = 5):
             line.update({"wg_a": 0, "wg_b": b, "xcd_a": res[0].xcc_a, "xcd_b": res[0].xcc_b,
                          "same_xcd": res[0].xcc_a == res[0].xcc_b})
         else:
+            line["slot_stride_words"] = stride
             line["slowest_wg_us_per_round"] = statistics.median(r.exchange_max_us for r in res)
         if where:
             line["stream_GBps"] = statistics.median(r.stream_gbps for r in res)
         print(json.dumps(line), flush=True)
     del buf
     torch.cuda.empty_cache()
+
+
+PF_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of the MI355X
+
+
+def gemm_mfma_bench(reps: int = 10):
+    """The prompt path's matrix-core GEMMs alone (kie_gemm_probe) at the ~2B
+    fp16 model's projection shapes, for 512 rows (a 512-token prompt) and 4096
+    rows (one chunk of the 8192-token prompt), next to torch.matmul (the
+    vendor GEMM library) on the same plain product; and the ~8B bf16 model's
+    shapes at 1024 rows (its three-term activations: three products per
+    GEMM).  One JSON line per shape; TFLOP/s counts 2 M N K per product (the
+    SwiGLU GEMM: 2 M 2F K)."""
+    import torch
+
+    from persistent_decode_monokernel_amd import kie, synth
+
+    def lib_ms(M, N, K, dt):
+        a = torch.randn(M, K, device="cuda", dtype=dt)
+        wt = torch.randn(N, K, device="cuda", dtype=dt).t()
+        for _ in range(3):
+            torch.matmul(a, wt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(a, wt)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for wl_name, rows in (("2b", (512, 4096)), ("8b", (1024,))):
+        s = synth.WORKLOADS[wl_name].shape
+        dt = torch.float16 if s.dtype == kie.KIE_F16 else torch.bfloat16
+        adt = torch.float16 if dt == torch.float16 else torch.float32
+        qd, kvd, d, F = s.n_heads * s.head_dim, s.n_kv_heads * s.head_dim, s.d_model, s.d_ffn
+        gemms = [("qkv", kie.KIE_GEMM_STORE, qd + 2 * kvd, d), ("wo", kie.KIE_GEMM_ADD, d, qd),
+                 ("gate_up_swiglu", kie.KIE_GEMM_SWIGLU, F, d), ("down", kie.KIE_GEMM_ADD, d, F)]
+        for M in rows:
+            for name, op, N, K in gemms:
+                A = torch.randn(M, K, device="cuda").to(adt)
+                W = (torch.randn(N, K, device="cuda") / K ** 0.5).to(dt)
+                W2 = (torch.randn(N, K, device="cuda") / K ** 0.5).to(dt) if op == kie.KIE_GEMM_SWIGLU else None
+                out = torch.zeros(M, N, device="cuda", dtype=adt if op == kie.KIE_GEMM_SWIGLU else torch.float32)
+                part = torch.empty(4 * M * N, device="cuda", dtype=torch.float32)
+                kie.gemm_probe(op, A, W, out, W2=W2, part=part, reps=2)  # warm-up
+                ms, S = kie.gemm_probe(op, A, W, out, W2=W2, part=part, reps=reps)
+                n_eff = 2 * N if op == kie.KIE_GEMM_SWIGLU else N
+                tf = 2 * M * n_eff * K / (ms * 1e-3) / 1e12
+                line = {"gemm": name, "workload": wl_name, "dtype": "f16" if dt == torch.float16 else "bf16",
+                        "M": M, "N": n_eff, "K": K, "split_k": S, "ms": ms, "TFLOP_per_s": tf,
+                        "frac_of_peak": tf / PF_PEAK_TFLOPS}
+                if dt == torch.bfloat16:
+                    line["mfma_products_per_gemm"] = 3
+                    line["mfma_frac_of_peak"] = 3 * tf / PF_PEAK_TFLOPS
+                else:
+                    lm = lib_ms(M, n_eff, K, dt)
+                    line.update({"library_ms": lm, "library_TFLOP_per_s": 2 * M * n_eff * K / (lm * 1e-3) / 1e12,
+                                 "vs_library": lm / ms})
+                print(json.dumps(line), flush=True)
+                del A, W, W2, out, part
+        torch.cuda.empty_cache()
 
 
 def ablation(name: str, steps: int = 64):
@@ -538,6 +605,8 @@ def main():
                     help="only compare the persistent kernel (NaN polls, arrival counters) with one launch per stage")
     ap.add_argument("--stream", action="store_true",
                     help="only run the read-stream probe (1, 2, 3, 4, 6, 8 loads in flight per thread)")
+    ap.add_argument("--gemm-mfma", action="store_true",
+                    help="only time the prompt path's matrix-core GEMMs alone, next to the vendor GEMM library")
     ap.add_argument("--handoff-probe", action="store_true",
                     help="only time work-group exchanges (ping, all-to-all) idle and beside streaming")
     ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")
@@ -574,6 +643,9 @@ def main():
         return
     if args.handoff_probe:
         handoff_probe_bench()
+        return
+    if args.gemm_mfma:
+        gemm_mfma_bench()
         return
     if args.ablation:
         ablation(args.workload, args.steps or 64)

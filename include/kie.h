@@ -433,6 +433,34 @@ kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t
 kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, int32_t reps,
                             uint32_t* sink_dev, void* hip_stream, float* kernel_ms);
 
+/* ---- matrix-core GEMM probe ----------------------------------------------- */
+
+/* One product of the prompt path's matrix-core GEMM alone, in exactly the
+ * launch sequence kie_prefill uses for it (batch-1 decode is bound by memory
+ * bandwidth, the prompt by compute: revietech.ru page, section "Tsifry
+ * proizvoditelnosti"; the prompt goes to the matrix cores):
+ *   KIE_GEMM_STORE:  C = A W^T        (the QKV projection)
+ *   KIE_GEMM_ADD:    C += A W^T       (Wo, down: the residual add)
+ *   KIE_GEMM_SWIGLU: H = silu(A W^T) * (A W2^T)   (gate W, up W2)
+ * A_dev [M][K]: fp16 for dtype KIE_F16; fp32 for KIE_BF16 (split into three
+ * bf16 terms, one product each, as the prompt path does).  W_dev, W2_dev
+ * [N][K] of dtype (W2_dev only for SWIGLU).  out_dev: C fp32 [M][N] (STORE,
+ * ADD) or H [M][N] (SWIGLU; fp16 for KIE_F16, fp32 for KIE_BF16).  1 <= M <=
+ * 65536, K a multiple of 64 up to 65536, N up to 65536 and a multiple of 128
+ * (STORE, ADD) or 64 (SWIGLU), M * N < 2^31; every pointer 16-byte aligned.
+ * With fewer than 512 output tiles of 128 x 128, STORE and ADD split the
+ * reduction into S <= 4 slices whose fp32 partial products go to part_dev
+ * (at least S * M * N * 4 bytes, KIE_ERR_CAPACITY otherwise; unused when S =
+ * 1) and are added in order; *slices receives S if not NULL.  The product
+ * runs `reps` times back to back (ADD accumulates every time); *kernel_ms
+ * receives the mean time per product (HIP events on hip_stream, which the
+ * call synchronises).  KIE_ERR_ARG for anything out of range. */
+enum { KIE_GEMM_STORE = 0, KIE_GEMM_ADD = 1, KIE_GEMM_SWIGLU = 2 };
+kie_status kie_gemm_probe(int32_t op, int32_t dtype, const void* A_dev, int32_t M, int32_t K,
+                          const void* W_dev, const void* W2_dev, int32_t N, void* out_dev, void* part_dev,
+                          size_t part_bytes, int32_t reps, void* hip_stream, int32_t* slices,
+                          float* kernel_ms);
+
 /* ---- hand-off latency probe ---------------------------------------------- */
 
 /* The cost of one exchange between work-groups, which the persistent kernel
@@ -446,7 +474,9 @@ kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, in
  *     it sees r.  exchange_us = mean round trip.
  *   KIE_PROBE_ALL_TO_ALL: every work-group publishes round r in its own word
  *     and waits until all grid words hold r (wave 0; each lane polls grid/64
- *     words together).  exchange_us = mean over work-groups of the mean round,
+ *     words together).  The words lie slot_stride 8-byte words apart (1, 2,
+ *     4, 8 or 16: 16 producers share a 128-byte line at 1, none at 16).
+ *     exchange_us = mean over work-groups of the mean round,
  *     exchange_max_us = the slowest work-group's.  wg_a, wg_b are ignored.
  * Two untimed rounds come first.  stream_where adds non-temporal dwordx4
  * streaming of buf_dev (stream_depth = 1, 2, 3, 4 or 8 loads in flight per
@@ -456,8 +486,8 @@ kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, in
  * rate over their common window.  buf_dev: 16-byte aligned, at least
  * grid * 512 * 16 * 33 * stream_depth bytes (KIE_ERR_CAPACITY below), unused
  * with KIE_PROBE_STREAM_NONE.  scratch_dev: device memory of at least
- * KIE_HANDOFF_PROBE_SCRATCH_BYTES, cleared by the call.  Each wait gives up
- * after 10 ms (completed = 0 then).  xcc_a, xcc_b: the accelerator die (XCD)
+ * KIE_HANDOFF_PROBE_SCRATCH_BYTES (enough for any grid and stride), cleared
+ * by the call.  Each wait gives up after 10 ms (completed = 0 then).  xcc_a, xcc_b: the accelerator die (XCD)
  * work-groups a and b (all-to-all: 0 and 1) ran on.  Runs on hip_stream and
  * synchronises it.  KIE_ERR_ARG for arguments out of range. */
 enum {
@@ -467,7 +497,7 @@ enum {
   KIE_PROBE_STREAM_OTHERS = 1,
   KIE_PROBE_STREAM_OWN = 2
 };
-#define KIE_HANDOFF_PROBE_SCRATCH_BYTES (64u * 1024u)
+#define KIE_HANDOFF_PROBE_SCRATCH_BYTES (192u * 1024u)
 typedef struct {
   double exchange_us;
   double exchange_max_us;
@@ -478,7 +508,7 @@ typedef struct {
 } kie_handoff_probe_result;
 
 kie_status kie_handoff_probe(int32_t kind, int32_t wg_a, int32_t wg_b, int32_t rounds,
-                             int32_t stream_depth, int32_t stream_where, const void* buf_dev,
+                             int32_t slot_stride, int32_t stream_depth, int32_t stream_where, const void* buf_dev,
                              size_t bytes, uint64_t* scratch_dev, size_t scratch_bytes,
                              void* hip_stream, kie_handoff_probe_result* out);
 

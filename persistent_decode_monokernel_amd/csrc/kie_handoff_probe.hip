@@ -21,14 +21,17 @@ constexpr int kAbortW = 0;         // set by a wait that ran out of time
 constexpr int kDoneW = 1;          // the exchange finished: streamers elsewhere stop
 constexpr int kSinkW = 2;          // keeps the streamed data live
 constexpr int kPingW = 16;         // work-group a's word; b's is 16 words (128 B) further
-constexpr int kSlotW = 64;         // all-to-all: one word per work-group
-constexpr int kRecW = 64 + kMaxWG;  // records: exchange ticks, XCC id, stream start, end, vectors, ok
+constexpr int kSlotW = 64;         // all-to-all: one word per work-group, `stride` words apart;
+                                   // the records follow the slots (exchange ticks, XCC id,
+                                   // stream start, end, vectors streamed, ok)
+constexpr int kMaxStride = 16;
 
 struct ProbeArgs {
   const uint4* buf;
   uint64_t nvec;
-  uint64_t* s;  // scratch, zeroed before the launch
-  int kind, a, b, rounds, where;
+  uint64_t* s;    // scratch, zeroed before the launch
+  uint64_t* rec;  // s + kSlotW + stride * grid
+  int kind, a, b, rounds, where, stride;
 };
 
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
@@ -66,7 +69,7 @@ __device__ __forceinline__ void ping(const ProbeArgs& p, bool is_a, uint64_t war
     if (!is_a && ok) st(mine, r);
   }
   const uint64_t te = now();
-  uint64_t* rec = p.s + kRecW + (uint64_t)blockIdx.x * kRecWords;
+  uint64_t* rec = p.rec + (uint64_t)blockIdx.x * kRecWords;
   if (is_a) {
     rec[0] = ok ? te - ts : 0;
     st(p.s + kDoneW, 1);
@@ -85,7 +88,7 @@ __device__ __forceinline__ void all_to_all(const ProbeArgs& p, int grid) {
   uint64_t ts = now();
   for (int r = 1; r <= p.rounds + 2 && ok; ++r) {
     if (r == 3) ts = now();
-    if (lane == 0) st(p.s + kSlotW + blockIdx.x, r);
+    if (lane == 0) st(p.s + kSlotW + (uint64_t)blockIdx.x * p.stride, r);
     bool rdy[kMaxPer];
 #pragma unroll
     for (int j = 0; j < kMaxPer; ++j) rdy[j] = j >= per || lane + 64 * j >= grid;
@@ -94,7 +97,8 @@ __device__ __forceinline__ void all_to_all(const ProbeArgs& p, int grid) {
     for (int n = 1;; ++n) {
       uint64_t v[kMaxPer];
 #pragma unroll
-      for (int j = 0; j < kMaxPer; ++j) v[j] = rdy[j] ? (uint64_t)r : ld(p.s + kSlotW + lane + 64 * j);
+      for (int j = 0; j < kMaxPer; ++j)
+        v[j] = rdy[j] ? (uint64_t)r : ld(p.s + kSlotW + (uint64_t)min(lane + 64 * j, grid - 1) * p.stride);
       bool all = true;
 #pragma unroll
       for (int j = 0; j < kMaxPer; ++j) {
@@ -114,7 +118,7 @@ __device__ __forceinline__ void all_to_all(const ProbeArgs& p, int grid) {
   }
   const uint64_t te = now();
   if (lane == 0) {
-    uint64_t* rec = p.s + kRecW + (uint64_t)blockIdx.x * kRecWords;
+    uint64_t* rec = p.rec + (uint64_t)blockIdx.x * kRecWords;
     rec[0] = ok ? te - ts : 0;
     rec[5] = ok ? 1 : 0;
   }
@@ -154,7 +158,7 @@ __device__ __forceinline__ void stream(const ProbeArgs& p, int grid, int nt, int
     if (stop || now() - t0 > kStreamLimit) break;
   }
   if (tt == 0) {
-    uint64_t* rec = p.s + kRecW + (uint64_t)blockIdx.x * kRecWords;
+    uint64_t* rec = p.rec + (uint64_t)blockIdx.x * kRecWords;
     rec[2] = t0;
     rec[3] = now();
     rec[4] = chunks * kSpan * nt;
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void handoff_probe(ProbeArgs p) {
   const bool own = (p.where & KIE_PROBE_STREAM_OWN) != 0;
   const bool others = (p.where & KIE_PROBE_STREAM_OTHERS) != 0;
   if (exch && t == 0)
-    p.s[kRecW + (uint64_t)wg * kRecWords + 1] = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID[3:0]
+    p.rec[(uint64_t)wg * kRecWords + 1] = __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID[3:0]
   if (exch) {
     if (t < 64) {
       if (p.kind == KIE_PROBE_ALL_TO_ALL) all_to_all(p, grid);
@@ -218,12 +222,13 @@ using namespace kie;
   } while (0)
 
 extern "C" kie_status kie_handoff_probe(int32_t kind, int32_t wg_a, int32_t wg_b, int32_t rounds,
-                                        int32_t stream_depth, int32_t stream_where, const void* buf_dev,
+                                        int32_t slot_stride, int32_t stream_depth, int32_t stream_where, const void* buf_dev,
                                         size_t bytes, uint64_t* scratch_dev, size_t scratch_bytes,
                                         void* hip_stream, kie_handoff_probe_result* out) {
   if (!out || !scratch_dev || (reinterpret_cast<uintptr_t>(scratch_dev) & 7)) return KIE_ERR_ARG;
   if (kind != KIE_PROBE_PING && kind != KIE_PROBE_ALL_TO_ALL) return KIE_ERR_ARG;
   if (rounds < 1 || rounds > 100000 || stream_where < 0 || stream_where > 3) return KIE_ERR_ARG;
+  if (slot_stride < 1 || slot_stride > kMaxStride || (slot_stride & (slot_stride - 1))) return KIE_ERR_ARG;
   if (kind == KIE_PROBE_ALL_TO_ALL && (stream_where & KIE_PROBE_STREAM_OTHERS)) return KIE_ERR_ARG;
   const bool streams = stream_where != KIE_PROBE_STREAM_NONE;
   const void* fn = handoff_probe_fn(streams ? stream_depth : 1);
@@ -236,7 +241,8 @@ extern "C" kie_status kie_handoff_probe(int32_t kind, int32_t wg_a, int32_t wg_b
   const int grid = prop.multiProcessorCount < kMaxWG ? prop.multiProcessorCount : kMaxWG;
   if (kind == KIE_PROBE_PING && (wg_a < 0 || wg_b < 0 || wg_a >= grid || wg_b >= grid || wg_a == wg_b))
     return KIE_ERR_ARG;
-  const size_t need = (size_t)(kRecW + kRecWords * grid) * 8;
+  const uint64_t rec_w = kSlotW + (uint64_t)slot_stride * grid;
+  const size_t need = (size_t)(rec_w + (uint64_t)kRecWords * grid) * 8;
   if (scratch_bytes < need) return KIE_ERR_CAPACITY;
   // every streaming work-group's share holds at least one chunk of slots of
   // 512 vectors (the wider of the two streaming widths, 512 and 448 threads)
@@ -249,12 +255,13 @@ extern "C" kie_status kie_handoff_probe(int32_t kind, int32_t wg_a, int32_t wg_b
   const uint64_t nwords = need / 8;
   hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, st, scratch_dev, nwords);
   PROBE_HIP(hipGetLastError());
-  ProbeArgs p{reinterpret_cast<const uint4*>(buf_dev), streams ? bytes / 16 : 0, scratch_dev, kind,
-              kind == KIE_PROBE_PING ? wg_a : -1, kind == KIE_PROBE_PING ? wg_b : -1, rounds, stream_where};
+  ProbeArgs p{reinterpret_cast<const uint4*>(buf_dev), streams ? bytes / 16 : 0, scratch_dev, scratch_dev + rec_w,
+              kind, kind == KIE_PROBE_PING ? wg_a : -1, kind == KIE_PROBE_PING ? wg_b : -1, rounds, stream_where,
+              slot_stride};
   void* args[] = {&p};
   PROBE_HIP(hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kThreads), args, 0, st));
   std::vector<uint64_t> rec((size_t)kRecWords * grid), hdr(2);
-  PROBE_HIP(hipMemcpyAsync(rec.data(), scratch_dev + kRecW, rec.size() * 8, hipMemcpyDeviceToHost, st));
+  PROBE_HIP(hipMemcpyAsync(rec.data(), scratch_dev + rec_w, rec.size() * 8, hipMemcpyDeviceToHost, st));
   PROBE_HIP(hipMemcpyAsync(hdr.data(), scratch_dev, 16, hipMemcpyDeviceToHost, st));
   PROBE_HIP(hipStreamSynchronize(st));
 

@@ -33,6 +33,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <cstdio>
+#include <cstdlib>
 #include <type_traits>
 
 #include "kie.h"
@@ -616,39 +618,61 @@ size_t prefill_part_floats(const kie_config& c, int chunk) {
 
 namespace {
 
+// Split-K slices of C[M][N] (+)= A[M][K] W^T: with fewer than 512 output
+// tiles (two work-groups per CU) the k-loop is split into S <= 4 slices whose
+// partial products pf_splitk adds in order; S * tiles < 1024 bounds the
+// partial buffer at 1024 tiles of 128 x 128.
+template <int DT>
+int splitk_slices(int M, int N, int K) {
+  const int tiles = (N / kTN) * ((M + kTM - 1) / kTM), nk = K / kBK<DT>;
+  int S = tiles >= 512 ? 1 : (512 + tiles - 1) / tiles;
+  S = S > 4 ? 4 : S;
+  return S > nk ? nk : S;
+}
+
+// C (+)= A W^T for EPI_STORE / EPI_ADD, split over k when splitk_slices says
+// so (partials in P: S * M * N floats).
+template <int DT>
+void launch_gemm(bool add, const act_t<DT>* A, int M, int K, const GemmB& b, int N, float* C, int ldc, float* P,
+                 hipStream_t st) {
+  const dim3 blk(256);
+  const int mt = (M + kTM - 1) / kTM, S = splitk_slices<DT>(M, N, K);
+  if (S == 1) {
+    if (add)
+      pf_gemm<EPI_ADD, DT><<<dim3(N / kTN, mt), blk, 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
+    else
+      pf_gemm<EPI_STORE, DT><<<dim3(N / kTN, mt), blk, 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
+    return;
+  }
+  pf_gemm<EPI_PART, DT><<<dim3(N / kTN, mt, S), blk, 0, st>>>(A, M, K, b, P, N, nullptr, 0);
+  const int q = (M * N / 4 + 255) / 256;
+  if (add)
+    pf_splitk<true><<<q, blk, 0, st>>>(P, S, M, N, C, ldc);
+  else
+    pf_splitk<false><<<q, blk, 0, st>>>(P, S, M, N, C, ldc);
+}
+
+// H = silu(A Wg^T) * (A Wu^T), [M][F] activations.
+template <int DT>
+void launch_swiglu(const act_t<DT>* A, int M, int K, const uint16_t* wg, const uint16_t* wu, int F, act_t<DT>* H,
+                   hipStream_t st) {
+  const int mt = (M + kTM - 1) / kTM;
+  pf_gemm<EPI_SWIGLU, DT><<<dim3(F / 64, mt), dim3(256), 0, st>>>(A, M, K, GemmB{{wg, wu}, {F, F, F}}, nullptr, 0,
+                                                                  H, F);
+}
+
 template <int DT>
 hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
   const kie_config& c = x.cfg;
   const int d = c.d_model, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim, F = c.d_ffn;
   const int ldq = qd + 2 * kvd;
   const dim3 blk(256);
-  const int mt = (M + kTM - 1) / kTM;
   hipStream_t st = x.stream;
   act_t<DT>* Xn = static_cast<act_t<DT>*>(x.Xn);
   act_t<DT>* Aa = static_cast<act_t<DT>*>(x.A);
   act_t<DT>* Hh = static_cast<act_t<DT>*>(x.H);
-  // C (+)= A W^T for EPI_STORE / EPI_ADD.  With fewer than 512 output tiles
-  // (two work-groups per CU) the k-loop is split into S <= 4 slices whose
-  // partial products the reduction adds in order; S * tiles < 1024 bounds the
-  // partial buffer (x.P) at 1024 tiles of 128 x 128.
   auto gemm = [&](bool add, const act_t<DT>* A, int K, const GemmB& b, int N, float* C, int ldc) {
-    const int tiles = (N / kTN) * mt, nk = K / kBK<DT>;
-    int S = tiles >= 512 ? 1 : (512 + tiles - 1) / tiles;
-    S = S > 4 ? 4 : S;
-    S = S > nk ? nk : S;
-    if (S == 1) {
-      if (add)
-        pf_gemm<EPI_ADD, DT><<<dim3(N / kTN, mt), blk, 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
-      else
-        pf_gemm<EPI_STORE, DT><<<dim3(N / kTN, mt), blk, 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
-      return;
-    }
-    pf_gemm<EPI_PART, DT><<<dim3(N / kTN, mt, S), blk, 0, st>>>(A, M, K, b, x.P, N, nullptr, 0);
-    const int q = (M * N / 4 + 255) / 256;
-    if (add)
-      pf_splitk<true><<<q, blk, 0, st>>>(x.P, S, M, N, C, ldc);
-    else
-      pf_splitk<false><<<q, blk, 0, st>>>(x.P, S, M, N, C, ldc);
+    launch_gemm<DT>(add, A, M, K, b, N, C, ldc, x.P, st);
   };
   pf_embed<DT><<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
   for (int l = 0; l < c.n_layers; ++l) {
@@ -670,8 +694,7 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
                                           x.vc + plane, Aa);
     gemm(true, Aa, qd, GemmB{{w[W_O]}, {d, d, d}}, d, x.X, d);
     pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, Xn);
-    pf_gemm<EPI_SWIGLU, DT><<<dim3(F / 64, mt), blk, 0, st>>>(Xn, M, d, GemmB{{w[W_GATE], w[W_UP]}, {F, F, F}},
-                                                              nullptr, 0, Hh, F);
+    launch_swiglu<DT>(Xn, M, d, w[W_GATE], w[W_UP], F, Hh, st);
     gemm(true, Hh, F, GemmB{{w[W_DOWN]}, {d, d, d}}, d, x.X, d);
   }
   return hipGetLastError();
@@ -683,4 +706,69 @@ hipError_t prefill_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M)
   return x.cfg.dtype == KIE_BF16 ? run_chunk<KIE_BF16>(x, tok_dev, p0, M) : run_chunk<KIE_F16>(x, tok_dev, p0, M);
 }
 
+namespace {
+
+template <int DT>
+void probe_launch(int op, const void* A, int M, int K, const uint16_t* w, const uint16_t* w2, int N, void* out,
+                  float* P, hipStream_t st) {
+  const act_t<DT>* a = static_cast<const act_t<DT>*>(A);
+  if (op == KIE_GEMM_SWIGLU)
+    launch_swiglu<DT>(a, M, K, w, w2, N, static_cast<act_t<DT>*>(out), st);
+  else
+    launch_gemm<DT>(op == KIE_GEMM_ADD, a, M, K, GemmB{{w}, {N, N, N}}, N, static_cast<float*>(out), N, P, st);
+}
+
+}  // namespace
 }  // namespace kie
+
+extern "C" kie_status kie_gemm_probe(int32_t op, int32_t dtype, const void* A_dev, int32_t M, int32_t K,
+                                     const void* W_dev, const void* W2_dev, int32_t N, void* out_dev, void* part_dev,
+                                     size_t part_bytes, int32_t reps, void* hip_stream, int32_t* slices,
+                                     float* kernel_ms) {
+  using namespace kie;
+  if (op != KIE_GEMM_STORE && op != KIE_GEMM_ADD && op != KIE_GEMM_SWIGLU) return KIE_ERR_ARG;
+  if (dtype != KIE_F16 && dtype != KIE_BF16) return KIE_ERR_ARG;
+  if (!A_dev || !W_dev || !out_dev || (op == KIE_GEMM_SWIGLU && !W2_dev) || reps < 1) return KIE_ERR_ARG;
+  if (M < 1 || M > 65536 || K < kBKMax || K % kBKMax || K > 65536 || N < 64 || N > 65536 ||
+      (int64_t)M * N > INT32_MAX)
+    return KIE_ERR_ARG;
+  if (N % (op == KIE_GEMM_SWIGLU ? 64 : kTN)) return KIE_ERR_ARG;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(A_dev) | reinterpret_cast<uintptr_t>(W_dev) |
+                       reinterpret_cast<uintptr_t>(W2_dev) | reinterpret_cast<uintptr_t>(out_dev) |
+                       reinterpret_cast<uintptr_t>(part_dev);
+  if (al & 15) return KIE_ERR_ARG;
+  const int S = op == KIE_GEMM_SWIGLU ? 1 : dtype == KIE_BF16 ? splitk_slices<KIE_BF16>(M, N, K)
+                                                              : splitk_slices<KIE_F16>(M, N, K);
+  if (S > 1 && (!part_dev || part_bytes < (size_t)S * M * N * sizeof(float))) return KIE_ERR_CAPACITY;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const uint16_t* w = static_cast<const uint16_t*>(W_dev);
+  const uint16_t* w2 = static_cast<const uint16_t*>(W2_dev);
+  float* P = static_cast<float*>(part_dev);
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return KIE_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return KIE_ERR_HIP;
+  }
+  hipError_t he = hipEventRecord(e0, st);
+  for (int r = 0; r < reps && he == hipSuccess; ++r) {
+    if (dtype == KIE_BF16)
+      probe_launch<KIE_BF16>(op, A_dev, M, K, w, w2, N, out_dev, P, st);
+    else
+      probe_launch<KIE_F16>(op, A_dev, M, K, w, w2, N, out_dev, P, st);
+    he = hipGetLastError();
+  }
+  if (he == hipSuccess) he = hipEventRecord(e1, st);
+  if (he == hipSuccess) he = hipStreamSynchronize(st);
+  float ms = 0.f;
+  if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (he != hipSuccess) {
+    if (getenv("KIE_VERBOSE")) fprintf(stderr, "kie: gemm probe failed: %s\n", hipGetErrorString(he));
+    return KIE_ERR_HIP;
+  }
+  if (slices) *slices = S;
+  if (kernel_ms) *kernel_ms = ms / reps;
+  return KIE_OK;
+}

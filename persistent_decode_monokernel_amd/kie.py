@@ -35,12 +35,15 @@ KIE_LAUNCH_PERSISTENT = 0
 KIE_LAUNCH_PER_STAGE = 1
 KIE_LAUNCH_PER_STAGE_GRAPH = 2
 KIE_STATIC_WORKSPACE_BYTES = 64 << 20  # include/kie.h
+KIE_GEMM_STORE = 0
+KIE_GEMM_ADD = 1
+KIE_GEMM_SWIGLU = 2
 KIE_PROBE_PING = 0
 KIE_PROBE_ALL_TO_ALL = 1
 KIE_PROBE_STREAM_NONE = 0
 KIE_PROBE_STREAM_OTHERS = 1
 KIE_PROBE_STREAM_OWN = 2
-KIE_HANDOFF_PROBE_SCRATCH_BYTES = 64 * 1024  # include/kie.h
+KIE_HANDOFF_PROBE_SCRATCH_BYTES = 192 * 1024  # include/kie.h
 
 
 class KieError(RuntimeError):
@@ -125,8 +128,13 @@ SIGNATURES = {
     "kie_gemv_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
+    "kie_gemm_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)]),
     "kie_handoff_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t,
                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                          ctypes.POINTER(kie_handoff_probe_result)]),
 }
@@ -415,15 +423,33 @@ def stream_probe(buf: torch.Tensor, depth: int = 3, reps: int = 4, stream=None) 
 
 def handoff_probe(kind: int, rounds: int = 200, wg_a: int = 0, wg_b: int = 1, where: int = KIE_PROBE_STREAM_NONE,
                   depth: int = 3, buf: Optional[torch.Tensor] = None, scratch: Optional[torch.Tensor] = None,
-                  stream=None) -> kie_handoff_probe_result:
+                  stride: int = 1, stream=None) -> kie_handoff_probe_result:
     """Hand-off latency probe (ping between work-groups wg_a and wg_b, or an
     all-to-all round over the grid), optionally beside streaming of `buf`."""
     if scratch is None:
         scratch = torch.zeros(KIE_HANDOFF_PROBE_SCRATCH_BYTES // 8, dtype=torch.int64, device="cuda")
     nbytes = 0 if buf is None else buf.numel() * buf.element_size()
     r = kie_handoff_probe_result()
-    _check(lib().kie_handoff_probe(int(kind), int(wg_a), int(wg_b), int(rounds), int(depth), int(where),
+    _check(lib().kie_handoff_probe(int(kind), int(wg_a), int(wg_b), int(rounds), int(stride), int(depth), int(where),
                                    ctypes.c_void_p(0 if buf is None else _dptr(buf)), nbytes,
                                    ctypes.c_void_p(_dptr(scratch)), scratch.numel() * scratch.element_size(),
                                    ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(r)), "kie_handoff_probe")
     return r
+
+
+def gemm_probe(op: int, A: torch.Tensor, W: torch.Tensor, out: torch.Tensor, W2: Optional[torch.Tensor] = None,
+               part: Optional[torch.Tensor] = None, reps: int = 1, stream=None) -> Tuple[float, int]:
+    """One matrix-core GEMM of the prompt path (kie_gemm_probe) into `out`.
+    Returns (mean ms per product, split-K slices)."""
+    M, K = A.shape
+    N = W.shape[0]
+    dtype = KIE_F16 if W.dtype == torch.float16 else KIE_BF16
+    ms = ctypes.c_float(0)
+    sl = ctypes.c_int32(0)
+    pbytes = 0 if part is None else part.numel() * part.element_size()
+    _check(lib().kie_gemm_probe(int(op), dtype, ctypes.c_void_p(_dptr(A)), M, K, ctypes.c_void_p(_dptr(W)),
+                                ctypes.c_void_p(0 if W2 is None else _dptr(W2)), N, ctypes.c_void_p(_dptr(out)),
+                                ctypes.c_void_p(0 if part is None else _dptr(part)), pbytes, int(reps),
+                                ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(sl), ctypes.byref(ms)),
+           "kie_gemm_probe")
+    return ms.value, sl.value

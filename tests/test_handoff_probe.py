@@ -15,10 +15,10 @@ DEV = "cuda:0"
 FAKE = 0x10000  # 8- and 16-byte aligned; never dereferenced by the rejected calls
 
 
-def _call(kind=kie.KIE_PROBE_PING, a=0, b=1, rounds=10, depth=3, where=kie.KIE_PROBE_STREAM_NONE,
+def _call(kind=kie.KIE_PROBE_PING, a=0, b=1, rounds=10, stride=1, depth=3, where=kie.KIE_PROBE_STREAM_NONE,
           buf=FAKE, nbytes=1 << 30, scratch=FAKE, sbytes=kie.KIE_HANDOFF_PROBE_SCRATCH_BYTES, out=True):
     r = kie.kie_handoff_probe_result()
-    return kie.lib().kie_handoff_probe(kind, a, b, rounds, depth, where, ctypes.c_void_p(buf), nbytes,
+    return kie.lib().kie_handoff_probe(kind, a, b, rounds, stride, depth, where, ctypes.c_void_p(buf), nbytes,
                                        ctypes.c_void_p(scratch), sbytes, None,
                                        ctypes.byref(r) if out else None)
 
@@ -31,6 +31,9 @@ def _call(kind=kie.KIE_PROBE_PING, a=0, b=1, rounds=10, depth=3, where=kie.KIE_P
     {"kind": -1},
     {"rounds": 0},
     {"rounds": 100001},
+    {"stride": 0},
+    {"stride": 3},
+    {"stride": 32},
     {"where": 4},
     {"where": -1},
     {"kind": kie.KIE_PROBE_ALL_TO_ALL, "where": kie.KIE_PROBE_STREAM_OTHERS},
@@ -72,9 +75,11 @@ def test_ping_idle_and_beside_streaming(bufs):
 @pytest.mark.gpu
 def test_all_to_all_idle_and_beside_streaming(bufs):
     buf, scratch = bufs
-    idle = kie.handoff_probe(kie.KIE_PROBE_ALL_TO_ALL, rounds=50, scratch=scratch)
-    print(f"all-to-all idle: {idle.exchange_us:.3f} us (slowest {idle.exchange_max_us:.3f})", flush=True)
-    assert idle.completed == 1 and 0.05 < idle.exchange_us <= idle.exchange_max_us < 1000
+    for stride in (1, 2, 16):
+        idle = kie.handoff_probe(kie.KIE_PROBE_ALL_TO_ALL, rounds=50, scratch=scratch, stride=stride)
+        print(f"all-to-all idle, slot stride {stride}: {idle.exchange_us:.3f} us "
+              f"(slowest {idle.exchange_max_us:.3f})", flush=True)
+        assert idle.completed == 1 and 0.05 < idle.exchange_us <= idle.exchange_max_us < 1000
     r = kie.handoff_probe(kie.KIE_PROBE_ALL_TO_ALL, rounds=50, where=kie.KIE_PROBE_STREAM_OWN, depth=8,
                           buf=buf, scratch=scratch)
     print(f"all-to-all, own waves stream: {r.exchange_us:.3f} us, {r.stream_gbps:.0f} GB/s", flush=True)

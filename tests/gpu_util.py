@@ -62,6 +62,26 @@ def check_tokens_and_logits(gpu_tokens, gpu_logits, ora_logits, what=""):
     return err, int(decisive.sum())
 
 
+def error_curve(gpu_logits, ora_logits, bucket: int = 128):
+    """Per-step max |logit_gpu - logit_oracle|, summarised per bucket of
+    `bucket` consecutive steps: (first step, last step, max, median).  Shows
+    whether the error drifts along a long decode or stays level."""
+    g = gpu_logits.detach().to("cpu", torch.float64)
+    o = ora_logits.detach().to("cpu", torch.float64)
+    per_step = (g - o).abs().amax(dim=1)
+    out = []
+    for s0 in range(0, per_step.numel(), bucket):
+        b = per_step[s0:s0 + bucket]
+        out.append((s0, s0 + b.numel() - 1, b.max().item(), b.median().item()))
+    return out
+
+
+def print_error_curve(curve, what=""):
+    print(f"{what}: per-step max |dlogit| by bucket (steps: max / median)", flush=True)
+    for s0, s1, mx, med in curve:
+        print(f"  {s0:5d}-{s1:5d}: {mx:.2e} / {med:.2e}", flush=True)
+
+
 def check_logits(gpu_logits, ora_logits, what=""):
     """max |logit_gpu - logit_oracle| <= LOGIT_TOL over all rows and vocabulary entries."""
     g = gpu_logits.detach().to("cpu", torch.float64)

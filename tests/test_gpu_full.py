@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from persistent_decode_monokernel_amd import kie, synth
-from tests.gpu_util import check_tokens_and_logits, cpu_copy
+from tests.gpu_util import check_tokens_and_logits, cpu_copy, error_curve, print_error_curve
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,7 @@ def test_2b_prefill512_decode1024(m2b):
     print(f"oracle teacher-forced pass: {time.time() - t0:.1f}s", flush=True)
     err, dec = check_tokens_and_logits(seq, gpu, ora, "2b prefill 512 + decode 1024")
     print(f"2b: max |dlogit| {err:.2e}, decisive steps {dec}/{len(seq)}")
+    print_error_curve(error_curve(gpu, ora), "2b prefill 512 + decode 1024")
 
 
 def test_2b_long_context_decode512(m2b):
@@ -76,3 +77,4 @@ def test_2b_long_context_decode512(m2b):
     print(f"oracle teacher-forced pass: {time.time() - t0:.1f}s", flush=True)
     err, dec = check_tokens_and_logits(toks, gpu, ora, "2b ctx 8192 + decode 512")
     print(f"2b long: max |dlogit| {err:.2e}, decisive steps {dec}/{len(toks)}")
+    print_error_curve(error_curve(gpu, ora), "2b ctx 8192 + decode 512")

@@ -284,13 +284,16 @@ PF_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of the MI355X
 
 
 def gemm_mfma_bench(reps: int = 10):
-    """The prompt path's matrix-core GEMMs alone (kie_gemm_probe) at the ~2B
+    """The prompt path's matrix-core GEMMs and causal attention alone
+    (kie_gemm_probe, kie_attn_probe).  GEMMs at the ~2B
     fp16 model's projection shapes, for 512 rows (a 512-token prompt) and 4096
     rows (one chunk of the 8192-token prompt), next to torch.matmul (the
     vendor GEMM library) on the same plain product; and the ~8B bf16 model's
     shapes at 1024 rows (its three-term activations: three products per
     GEMM).  One JSON line per shape; TFLOP/s counts 2 M N K per product (the
-    SwiGLU GEMM: 2 M 2F K)."""
+    SwiGLU GEMM: 2 M 2F K).  Attention of the 512- and 8192-token prompts
+    (one and two chunks), next to the library's causal
+    scaled_dot_product_attention over the whole sequence."""
     import torch
 
     from persistent_decode_monokernel_amd import kie, synth
@@ -338,6 +341,41 @@ def gemm_mfma_bench(reps: int = 10):
                                  "vs_library": lm / ms})
                 print(json.dumps(line), flush=True)
                 del A, W, W2, out, part
+        torch.cuda.empty_cache()
+
+    # causal attention of the ~2B prompts: ours over the prompt path's chunks
+    # (kie_attn_probe), the library's scaled_dot_product_attention over the
+    # whole sequence; flops 4 hq hd per (query, visible key) pair
+    s = synth.WORKLOADS["2b"].shape
+    hq, hkv, hd = s.n_heads, s.n_kv_heads, s.head_dim
+    for P in (512, 8192):
+        chunks = [(p0, min(4096, P - p0)) for p0 in range(0, P, 4096)]
+        kc = torch.randn(hkv, P, hd, device="cuda").half()
+        vc = torch.randn(hkv, P, hd, device="cuda").half()
+        ours = 0.0
+        for p0, M in chunks:
+            qkv = torch.randn(M, (hq + 2 * hkv) * hd, device="cuda")
+            out = torch.empty(M, hq * hd, device="cuda", dtype=torch.float16)
+            kie.attn_probe(qkv, kc, vc, out, hq, p0, reps=2)
+            ours += kie.attn_probe(qkv, kc, vc, out, hq, p0, reps=reps)
+        q = torch.randn(1, hq, P, hd, device="cuda", dtype=torch.float16)
+        k, v = kc[None].contiguous(), vc[None].contiguous()
+        sdpa = torch.nn.functional.scaled_dot_product_attention
+        for _ in range(3):
+            sdpa(q, k, v, is_causal=True, enable_gqa=True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sdpa(q, k, v, is_causal=True, enable_gqa=True)
+        e1.record()
+        torch.cuda.synchronize()
+        lib = e0.elapsed_time(e1) / reps
+        fl = 4 * hq * hd * P * (P + 1) / 2
+        print(json.dumps({"attention": "causal, per layer", "workload": "2b", "dtype": "f16", "prompt": P,
+                          "chunks": [M for _, M in chunks], "ms": ours, "TFLOP_per_s": fl / (ours * 1e-3) / 1e12,
+                          "frac_of_peak": fl / (ours * 1e-3) / 1e12 / PF_PEAK_TFLOPS, "library_ms": lib,
+                          "library_TFLOP_per_s": fl / (lib * 1e-3) / 1e12, "vs_library": lib / ours}), flush=True)
+        del kc, vc, q, k, v
         torch.cuda.empty_cache()
 
 
@@ -606,7 +644,7 @@ def main():
     ap.add_argument("--stream", action="store_true",
                     help="only run the read-stream probe (1, 2, 3, 4, 6, 8 loads in flight per thread)")
     ap.add_argument("--gemm-mfma", action="store_true",
-                    help="only time the prompt path's matrix-core GEMMs alone, next to the vendor GEMM library")
+                    help="only time the prompt path's matrix-core GEMMs and attention alone, next to the vendor library")
     ap.add_argument("--handoff-probe", action="store_true",
                     help="only time work-group exchanges (ping, all-to-all) idle and beside streaming")
     ap.add_argument("--ttft", action="store_true", help="only time kie_prefill of the workload's prompt per mode")

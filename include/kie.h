@@ -461,6 +461,29 @@ kie_status kie_gemm_probe(int32_t op, int32_t dtype, const void* A_dev, int32_t 
                           size_t part_bytes, int32_t reps, void* hip_stream, int32_t* slices,
                           float* kernel_ms);
 
+/* ---- matrix-core attention probe ------------------------------------------ */
+
+/* One causal flash attention of the prompt path alone, in the launch
+ * kie_prefill uses (the prompt is part of the work the pages put on the GPU:
+ * revietech.ru page, section "Chto takoye monokernel"): query row m = 0 .. M-1
+ * at position p0 + m attends to cache rows 0 .. p0 + m.
+ *   qkv_dev: fp32 [M][ldq], ldq = n_heads*head_dim + 2*n_kv_heads*head_dim
+ *     (the prompt path's QKV rows, q already rotated; only the first
+ *     n_heads*head_dim columns are read).
+ *   k_cache_dev, v_cache_dev: [n_kv_heads][max_seq][head_dim] of dtype, rows
+ *     0 .. p0+M-1 filled.
+ *   out_dev: [M][n_heads*head_dim]: fp16 for KIE_F16, fp32 for KIE_BF16.
+ * head_dim 64 or 128; n_heads / n_kv_heads in {1, 2, 4, 8}; 1 <= M <= 65536;
+ * p0 + M <= max_seq; pointers 16-byte aligned.  Scores and the weighted sum run
+ * on the matrix cores: queries (scaled by 1/sqrt(head_dim)) and softmax
+ * weights as fp16 operands (bf16 models: two bf16 terms each), fp32
+ * accumulation, softmax in base 2.  reps and *kernel_ms as for
+ * kie_gemm_probe.  KIE_ERR_ARG for anything out of range. */
+kie_status kie_attn_probe(int32_t dtype, const float* qkv_dev, int32_t M, int32_t n_heads, int32_t n_kv_heads,
+                          int32_t head_dim, int32_t p0, int32_t max_seq, const void* k_cache_dev,
+                          const void* v_cache_dev, void* out_dev, int32_t reps, void* hip_stream,
+                          float* kernel_ms);
+
 /* ---- hand-off latency probe ---------------------------------------------- */
 
 /* The cost of one exchange between work-groups, which the persistent kernel

@@ -661,6 +661,19 @@ void launch_swiglu(const act_t<DT>* A, int M, int K, const uint16_t* wg, const u
                                                                   H, F);
 }
 
+// Causal flash attention of query rows p0 .. p0+M-1 over cache rows 0 .. p0+m.
+template <int DT>
+void attn_launch(const float* qkv, int M, int hq, int hkv, int hd, int p0, int max_seq, const uint16_t* kc,
+                 const uint16_t* vc, void* out, hipStream_t st) {
+  const int G = hq / hkv, hw = G < 4 ? G : 4, rows = 32 * (4 / hw);
+  const dim3 ag((M + rows - 1) / rows, hkv * (G / hw));
+  act_t<DT>* o = static_cast<act_t<DT>*>(out);
+  if (hd == 128)
+    pf_attn<128, DT><<<ag, dim3(256), 0, st>>>(qkv, M, hq, hkv, p0, max_seq, kc, vc, o);
+  else
+    pf_attn<64, DT><<<ag, dim3(256), 0, st>>>(qkv, M, hq, hkv, p0, max_seq, kc, vc, o);
+}
+
 template <int DT>
 hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
   const kie_config& c = x.cfg;
@@ -684,14 +697,8 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
     pf_rope_kv<DT><<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope,
                                                             p0, c.max_seq, x.kc + plane, x.vc + plane);
-    const int G = c.n_heads / c.n_kv_heads, hw = G < 4 ? G : 4, rows = 32 * (4 / hw);
-    const dim3 ag((M + rows - 1) / rows, c.n_kv_heads * (G / hw));
-    if (c.head_dim == 128)
-      pf_attn<128, DT><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane,
-                                           x.vc + plane, Aa);
-    else
-      pf_attn<64, DT><<<ag, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, p0, c.max_seq, x.kc + plane,
-                                          x.vc + plane, Aa);
+    attn_launch<DT>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, p0, c.max_seq, x.kc + plane, x.vc + plane, Aa,
+                    st);
     gemm(true, Aa, qd, GemmB{{w[W_O]}, {d, d, d}}, d, x.X, d);
     pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, Xn);
     launch_swiglu<DT>(Xn, M, d, w[W_GATE], w[W_UP], F, Hh, st);
@@ -720,6 +727,52 @@ void probe_launch(int op, const void* A, int M, int K, const uint16_t* w, const 
 
 }  // namespace
 }  // namespace kie
+
+extern "C" kie_status kie_attn_probe(int32_t dtype, const float* qkv_dev, int32_t M, int32_t n_heads,
+                                     int32_t n_kv_heads, int32_t head_dim, int32_t p0, int32_t max_seq,
+                                     const void* k_cache_dev, const void* v_cache_dev, void* out_dev, int32_t reps,
+                                     void* hip_stream, float* kernel_ms) {
+  using namespace kie;
+  if (dtype != KIE_F16 && dtype != KIE_BF16) return KIE_ERR_ARG;
+  if (!qkv_dev || !k_cache_dev || !v_cache_dev || !out_dev || reps < 1) return KIE_ERR_ARG;
+  if (head_dim != 64 && head_dim != 128) return KIE_ERR_ARG;
+  if (n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads || n_heads > 256) return KIE_ERR_ARG;
+  const int G = n_heads / n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KIE_ERR_ARG;
+  if (M < 1 || M > 65536 || p0 < 0 || max_seq < 1 || (int64_t)p0 + M > max_seq) return KIE_ERR_ARG;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(qkv_dev) | reinterpret_cast<uintptr_t>(k_cache_dev) |
+                       reinterpret_cast<uintptr_t>(v_cache_dev) | reinterpret_cast<uintptr_t>(out_dev);
+  if (al & 15) return KIE_ERR_ARG;
+  hipStream_t st = reinterpret_cast<hipStream_t>(hip_stream);
+  const uint16_t* kc = static_cast<const uint16_t*>(k_cache_dev);
+  const uint16_t* vc = static_cast<const uint16_t*>(v_cache_dev);
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess) return KIE_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return KIE_ERR_HIP;
+  }
+  hipError_t he = hipEventRecord(e0, st);
+  for (int r = 0; r < reps && he == hipSuccess; ++r) {
+    if (dtype == KIE_BF16)
+      attn_launch<KIE_BF16>(qkv_dev, M, n_heads, n_kv_heads, head_dim, p0, max_seq, kc, vc, out_dev, st);
+    else
+      attn_launch<KIE_F16>(qkv_dev, M, n_heads, n_kv_heads, head_dim, p0, max_seq, kc, vc, out_dev, st);
+    he = hipGetLastError();
+  }
+  if (he == hipSuccess) he = hipEventRecord(e1, st);
+  if (he == hipSuccess) he = hipStreamSynchronize(st);
+  float ms = 0.f;
+  if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (he != hipSuccess) {
+    if (getenv("KIE_VERBOSE")) fprintf(stderr, "kie: attention probe failed: %s\n", hipGetErrorString(he));
+    return KIE_ERR_HIP;
+  }
+  if (kernel_ms) *kernel_ms = ms / reps;
+  return KIE_OK;
+}
 
 extern "C" kie_status kie_gemm_probe(int32_t op, int32_t dtype, const void* A_dev, int32_t M, int32_t K,
                                      const void* W_dev, const void* W2_dev, int32_t N, void* out_dev, void* part_dev,

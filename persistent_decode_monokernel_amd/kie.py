@@ -132,6 +132,10 @@ SIGNATURES = {
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_float)]),
+    "kie_attn_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.POINTER(ctypes.c_float)]),
     "kie_handoff_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_size_t,
@@ -453,3 +457,19 @@ def gemm_probe(op: int, A: torch.Tensor, W: torch.Tensor, out: torch.Tensor, W2:
                                 ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(sl), ctypes.byref(ms)),
            "kie_gemm_probe")
     return ms.value, sl.value
+
+
+def attn_probe(qkv: torch.Tensor, kc: torch.Tensor, vc: torch.Tensor, out: torch.Tensor, n_heads: int, p0: int,
+               reps: int = 1, stream=None) -> float:
+    """One causal flash attention of the prompt path (kie_attn_probe) into
+    `out`.  qkv fp32 [M][ldq]; kc, vc [n_kv_heads][max_seq][head_dim].
+    Returns the mean ms per launch."""
+    n_kv, max_seq, hd = kc.shape
+    M = qkv.shape[0]
+    dtype = KIE_F16 if kc.dtype == torch.float16 else KIE_BF16
+    ms = ctypes.c_float(0)
+    _check(lib().kie_attn_probe(dtype, ctypes.c_void_p(_dptr(qkv)), M, int(n_heads), n_kv, hd, int(p0), max_seq,
+                                ctypes.c_void_p(_dptr(kc)), ctypes.c_void_p(_dptr(vc)), ctypes.c_void_p(_dptr(out)),
+                                int(reps), ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(ms)),
+           "kie_attn_probe")
+    return ms.value

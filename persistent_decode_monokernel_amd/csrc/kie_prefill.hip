@@ -342,6 +342,103 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
       }
 }
 
+// ---- gate/up + SwiGLU GEMM for long prompts (fp16) --------------------------
+//
+// H = silu(A Wg^T) * (A Wu^T) with 256 x 256 work-group tiles on 8 waves (512
+// threads, one work-group per CU: 144 KB of LDS): the tile's B rows are 128
+// gate rows, then the same 128 up rows, for 128 output columns.  Wave (wm,
+// wn), wm < 2, wn < 4, computes rows 128wm .. 128wm+127 against gate rows 32wn
+// .. and the matching up rows: 4 x 2 accumulators of 32 x 32, so each 16-byte
+// LDS operand read feeds 1.33 matrix-core products (the 128 x 128 tile's
+// waves: 1).  k-tiles of 64, rows padded to 144 bytes, double-buffered, one
+// barrier per k-tile; the next k-tile's global loads are in flight during the
+// current one's products; operands read two k steps at a time.  Rows of A
+// beyond M re-read row M-1 and are not stored.  Used when the grid has at
+// least 512 tiles (long prompts); the 128 x 128 kernel covers the rest.
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));  // staging registers the compiler keeps in VGPRs
+constexpr int kBigT = 256;                                     // tile rows (A) and B rows
+
+__global__ __launch_bounds__(512, 1) void pf_swiglu_big(const uint16_t* A, int M, int K, const uint16_t* wg,
+                                                       const uint16_t* wu, uint16_t* H, int F) {
+  constexpr int BK = 64, LS = 72, NT = 512, RPP = NT / 8, PA = kBigT / RPP, PB = kBigT / RPP, BI = 4, KG = 2;
+  __shared__ __align__(16) uint16_t lds[2][2 * kBigT * LS];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 31, hf = l >> 5;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int m0 = blockIdx.y * kBigT, n0 = blockIdx.x * (kBigT / 2);
+  const int pc = tid & 7, pr = tid >> 3;  // staging: piece pc of rows pr + 64i
+  const uint16_t* ag[PA];
+  const uint16_t* bg[PB];
+#pragma unroll
+  for (int i = 0; i < PA; ++i) ag[i] = A + (size_t)min(m0 + pr + RPP * i, M - 1) * K + 8 * pc;
+#pragma unroll
+  for (int i = 0; i < PB; ++i)  // B rows 0..127 gate, 128..255 up
+    bg[i] = (i < PB / 2 ? wg : wu) + (size_t)(n0 + pr + RPP * (i % (PB / 2))) * K + 8 * pc;
+  const int soff = pr * LS + 8 * pc;
+  const int arow = 128 * wm + r, brow = 32 * wn + r;  // B block 0: gate rows, block 1: up rows (+128)
+  f16x_t acc[BI][2];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) acc[i][0] = acc[i][1] = f16x_t{};
+  v4u_t sa[PA], sb[PB];
+  const int nk = K / BK;
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i) sa[i] = *reinterpret_cast<const v4u_t*>(ag[i] + k0);
+#pragma unroll
+    for (int i = 0; i < PB; ++i) sb[i] = *reinterpret_cast<const v4u_t*>(bg[i] + k0);
+  };
+  auto stage = [&](uint16_t* d) {
+#pragma unroll
+    for (int i = 0; i < PA; ++i) *reinterpret_cast<v4u_t*>(&d[soff + RPP * i * LS]) = sa[i];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) *reinterpret_cast<v4u_t*>(&d[kBigT * LS + soff + RPP * i * LS]) = sb[i];
+  };
+  fetch(0);
+  stage(lds[0]);
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) fetch((t + 1) * BK);
+    const uint16_t* la = lds[t & 1];
+    const uint16_t* lb = la + kBigT * LS;
+#pragma unroll
+    for (int k0 = 0; k0 < BK / 16; k0 += KG) {
+      v4u_t oa[KG][BI], ob[KG][2];
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk) {
+        const int ko = 16 * (k0 + kk) + 8 * hf;
+#pragma unroll
+        for (int i = 0; i < BI; ++i) oa[kk][i] = *reinterpret_cast<const v4u_t*>(la + (arow + 32 * i) * LS + ko);
+        ob[kk][0] = *reinterpret_cast<const v4u_t*>(lb + brow * LS + ko);
+        ob[kk][1] = *reinterpret_cast<const v4u_t*>(lb + (brow + 128) * LS + ko);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its products
+#pragma unroll
+      for (int kk = 0; kk < KG; ++kk)
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, oa[kk][i]),
+                                                               __builtin_bit_cast(h8_t, ob[kk][j]), acc[i][j], 0, 0,
+                                                               0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t + 1 < nk) stage(lds[(t + 1) & 1]);
+    __syncthreads();
+  }
+  // accumulator element 4ii + jj of acc[i][*]: row 128wm + 32i + 8ii + 4hf + jj, output column 32wn + r
+#pragma unroll
+  for (int i = 0; i < BI; ++i)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int m = m0 + 128 * wm + 32 * i + 8 * ii + 4 * hf + jj;
+        if (m >= M) continue;
+        const float gt = acc[i][0][4 * ii + jj], up = acc[i][1][4 * ii + jj];
+        H[(size_t)m * F + n0 + 32 * wn + r] = f2h(gt / (1.0f + expf(-gt)) * up);
+      }
+}
+
 // Split-K reduction: C[m][n] (+)= sum over z = 0 .. S-1 of P[z][m][n], the
 // slices added in order (deterministic).  Four columns per thread; N % 4 == 0.
 template <bool ADD>
@@ -656,6 +753,13 @@ void launch_gemm(bool add, const act_t<DT>* A, int M, int K, const GemmB& b, int
 template <int DT>
 void launch_swiglu(const act_t<DT>* A, int M, int K, const uint16_t* wg, const uint16_t* wu, int F, act_t<DT>* H,
                    hipStream_t st) {
+  if constexpr (DT == KIE_F16) {
+    const int big = (F / (kBigT / 2)) * ((M + kBigT - 1) / kBigT);
+    if (F % (kBigT / 2) == 0 && big >= 512) {
+      pf_swiglu_big<<<dim3(F / (kBigT / 2), (M + kBigT - 1) / kBigT), dim3(512), 0, st>>>(A, M, K, wg, wu, H, F);
+      return;
+    }
+  }
   const int mt = (M + kTM - 1) / kTM;
   pf_gemm<EPI_SWIGLU, DT><<<dim3(F / 64, mt), dim3(256), 0, st>>>(A, M, K, GemmB{{wg, wu}, {F, F, F}}, nullptr, 0,
                                                                   H, F);

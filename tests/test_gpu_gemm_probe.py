@@ -1,10 +1,12 @@
-"""The prompt path's matrix-core GEMM through kie_gemm_probe.
+"""The prompt path's matrix-core GEMMs through kie_gemm_probe.
 
 Host side (no GPU): argument and capacity errors the call rejects before it
 touches the device.  GPU: C = A W^T, C += A W^T and silu(A Wg^T) * (A Wu^T) for
 fp16 (fp16 activations) and bf16 (fp32 activations split into three bf16
 terms) against a float64 product of the same inputs on the CPU: ragged row
-counts, split-K shapes (fewer than 512 output tiles) and an unsplit one.
+counts, split-K shapes (fewer than 512 output tiles) and an unsplit one; the
+fp16 gate/up + SwiGLU GEMM on grids of 512 and more 256 x 256 tiles (the
+long-prompt kernel), with a ragged last row tile.
 """
 import ctypes
 
@@ -78,8 +80,10 @@ def test_gemm_store_and_add(dt, M, N, K):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("dt", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
-@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (77, 192, 512), (300, 128, 256), (640, 1024, 128)],
-                         ids=["1x64x128", "77x192x512", "300x128x256", "640x1024x128"])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (77, 192, 512), (300, 128, 256), (640, 1024, 128),
+                                   (1100, 16384, 64), (2048, 8192, 128)],
+                         ids=["1x64x128", "77x192x512", "300x128x256", "640x1024x128",
+                              "1100x16384x64", "2048x8192x128"])  # the last two: fp16 takes the 256 x 256 tiles
 def test_gemm_swiglu(dt, M, N, K):
     a, w, w2 = _inputs(M, N, K, dt, 13)
     gt = a.double() @ w.double().t()

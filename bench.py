@@ -286,8 +286,9 @@ PF_PEAK_TFLOPS = 2500.0  # dense fp16 / bf16 matrix-core peak of the MI355X
 def gemm_mfma_bench(reps: int = 10):
     """The prompt path's matrix-core GEMMs and causal attention alone
     (kie_gemm_probe, kie_attn_probe).  GEMMs at the ~2B
-    fp16 model's projection shapes, for 512 rows (a 512-token prompt) and 4096
-    rows (one chunk of the 8192-token prompt), next to torch.matmul (the
+    fp16 model's projection shapes, for 512 rows (a 512-token prompt), 8192
+    rows (the 8192-token prompt's one chunk) and 4096 rows (that prompt in
+    two chunks), next to torch.matmul (the
     vendor GEMM library) on the same plain product; and the ~8B bf16 model's
     shapes at 1024 rows (its three-term activations: three products per
     GEMM).  One JSON line per shape; TFLOP/s counts 2 M N K per product (the
@@ -311,7 +312,7 @@ def gemm_mfma_bench(reps: int = 10):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    for wl_name, rows in (("2b", (512, 4096)), ("8b", (1024,))):
+    for wl_name, rows in (("2b", (512, 4096, 8192)), ("8b", (1024,))):
         s = synth.WORKLOADS[wl_name].shape
         dt = torch.float16 if s.dtype == kie.KIE_F16 else torch.bfloat16
         adt = torch.float16 if dt == torch.float16 else torch.float32
@@ -324,7 +325,8 @@ def gemm_mfma_bench(reps: int = 10):
                 W = (torch.randn(N, K, device="cuda") / K ** 0.5).to(dt)
                 W2 = (torch.randn(N, K, device="cuda") / K ** 0.5).to(dt) if op == kie.KIE_GEMM_SWIGLU else None
                 out = torch.zeros(M, N, device="cuda", dtype=adt if op == kie.KIE_GEMM_SWIGLU else torch.float32)
-                part = torch.empty(4 * M * N, device="cuda", dtype=torch.float32)
+                # split-K partials: only below 512 tiles of 128 x 128, at most 4 slices
+                part = torch.empty(4 * min(M * N, 512 * 128 * 128), device="cuda", dtype=torch.float32)
                 kie.gemm_probe(op, A, W, out, W2=W2, part=part, reps=2)  # warm-up
                 ms, S = kie.gemm_probe(op, A, W, out, W2=W2, part=part, reps=reps)
                 n_eff = 2 * N if op == kie.KIE_GEMM_SWIGLU else N

@@ -214,7 +214,7 @@ kie_status kie_set_grid(kie_engine* e, int32_t grid);
 
 /* Prompt positions per matrix-core chunk in KIE_PREFILL_AUTO (each chunk runs
  * every layer before the next starts).  The workspace holds the activations of
- * min(max_seq, 4096) positions; 0 (default) uses all of them, a smaller value
+ * min(max_seq, 8192) positions; 0 (default) uses all of them, a smaller value
  * trades throughput for shorter launch sequences.  KIE_ERR_CAPACITY above the
  * workspace's chunk (0 for shapes without the matrix-core path), KIE_ERR_ARG
  * below 0.  Same results for every chunk size up to rounding order. */
@@ -448,6 +448,8 @@ kie_status kie_stream_probe(const void* buf_dev, size_t bytes, int32_t depth, in
  * ADD) or H [M][N] (SWIGLU; fp16 for KIE_F16, fp32 for KIE_BF16).  1 <= M <=
  * 65536, K a multiple of 64 up to 65536, N up to 65536 and a multiple of 128
  * (STORE, ADD) or 64 (SWIGLU), M * N < 2^31; every pointer 16-byte aligned.
+ * fp16 products run on 256 x 256 tiles when that grid fills the GPU (at least
+ * 256 tiles; gate/up + SwiGLU 512), on 128 x 128 tiles otherwise.
  * With fewer than 512 output tiles of 128 x 128, STORE and ADD split the
  * reduction into S <= 4 slices whose fp32 partial products go to part_dev
  * (at least S * M * N * 4 bytes, KIE_ERR_CAPACITY otherwise; unused when S =

@@ -342,39 +342,54 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
       }
 }
 
-// ---- gate/up + SwiGLU GEMM for long prompts (fp16) --------------------------
+// ---- GEMMs for long prompts (fp16) -------------------------------------------
 //
-// H = silu(A Wg^T) * (A Wu^T) with 256 x 256 work-group tiles on 8 waves (512
-// threads, one work-group per CU: 144 KB of LDS): the tile's B rows are 128
-// gate rows, then the same 128 up rows, for 128 output columns.  Wave (wm,
-// wn), wm < 2, wn < 4, computes rows 128wm .. 128wm+127 against gate rows 32wn
-// .. and the matching up rows: 4 x 2 accumulators of 32 x 32, so each 16-byte
-// LDS operand read feeds 1.33 matrix-core products (the 128 x 128 tile's
-// waves: 1).  k-tiles of 64, rows padded to 144 bytes, double-buffered, one
-// barrier per k-tile; the next k-tile's global loads are in flight during the
-// current one's products; operands read two k steps at a time.  Rows of A
-// beyond M re-read row M-1 and are not stored.  Used when the grid has at
-// least 512 tiles (long prompts); the 128 x 128 kernel covers the rest.
+// The three GEMM forms on 256 x 256 work-group tiles, 8 waves (512 threads, one
+// work-group per CU: 144 KB of LDS).  Wave (wm, wn), wm < 2, wn < 4, computes
+// rows 128wm .. 128wm+127 of the tile against two 32-row blocks of its B rows:
+// 4 x 2 accumulators of 32 x 32, so each 16-byte LDS operand read feeds 1.33
+// matrix-core products (the 128 x 128 tile's 64 x 64 wave blocks: 1).
+//   EPI_STORE / EPI_ADD: 256 consecutive rows of one stacked matrix (segment
+//   widths multiples of 256); wave wn takes B rows 64wn .. 64wn+63.
+//   EPI_SWIGLU: 128 gate rows, then the same 128 up rows, for 128 output
+//   columns; wave wn takes gate rows 32wn .. and the matching up rows, so gate
+//   and up of one output land in the same lane.
+// k-tiles of 64, rows padded to 144 bytes, double-buffered, one barrier per
+// k-tile; the next k-tile's global loads are in flight during the current
+// one's products; operands read two k steps at a time.  Rows of A beyond M
+// re-read row M-1 and are not stored.  Used when the grid fills the chip
+// (big_tiles_pay); the 128 x 128 kernel covers the rest.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));  // staging registers the compiler keeps in VGPRs
-constexpr int kBigT = 256;                                     // tile rows (A) and B rows
+constexpr int kBigT = 256;                                     // tile rows of A and of B
 
-__global__ __launch_bounds__(512, 1) void pf_swiglu_big(const uint16_t* A, int M, int K, const uint16_t* wg,
-                                                       const uint16_t* wu, uint16_t* H, int F) {
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void pf_gemm_big(const uint16_t* A, int M, int K, GemmB wb, float* C, int ldc,
+                                                     uint16_t* H, int ldh) {
   constexpr int BK = 64, LS = 72, NT = 512, RPP = NT / 8, PA = kBigT / RPP, PB = kBigT / RPP, BI = 4, KG = 2;
+  constexpr bool SWI = EPI == EPI_SWIGLU;
   __shared__ __align__(16) uint16_t lds[2][2 * kBigT * LS];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 31, hf = l >> 5;
   const int wm = wave >> 2, wn = wave & 3;
-  const int m0 = blockIdx.y * kBigT, n0 = blockIdx.x * (kBigT / 2);
+  const int m0 = blockIdx.y * kBigT, n0 = blockIdx.x * (SWI ? kBigT / 2 : kBigT);
   const int pc = tid & 7, pr = tid >> 3;  // staging: piece pc of rows pr + 64i
   const uint16_t* ag[PA];
   const uint16_t* bg[PB];
 #pragma unroll
   for (int i = 0; i < PA; ++i) ag[i] = A + (size_t)min(m0 + pr + RPP * i, M - 1) * K + 8 * pc;
+  if constexpr (SWI) {
 #pragma unroll
-  for (int i = 0; i < PB; ++i)  // B rows 0..127 gate, 128..255 up
-    bg[i] = (i < PB / 2 ? wg : wu) + (size_t)(n0 + pr + RPP * (i % (PB / 2))) * K + 8 * pc;
+    for (int i = 0; i < PB; ++i)  // B rows 0..127 gate, 128..255 up
+      bg[i] = (i < PB / 2 ? wb.w[0] : wb.w[1]) + (size_t)(n0 + pr + RPP * (i % (PB / 2))) * K + 8 * pc;
+  } else {
+    const bool s0 = n0 < wb.end[0], s1 = n0 < wb.end[1];  // selects, not an indexed argument
+    const uint16_t* wsel = s0 ? wb.w[0] : s1 ? wb.w[1] : wb.w[2];
+    const uint16_t* b0 = wsel + (size_t)(n0 - (s0 ? 0 : s1 ? wb.end[0] : wb.end[1])) * K;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) bg[i] = b0 + (size_t)(pr + RPP * i) * K + 8 * pc;
+  }
   const int soff = pr * LS + 8 * pc;
-  const int arow = 128 * wm + r, brow = 32 * wn + r;  // B block 0: gate rows, block 1: up rows (+128)
+  const int arow = 128 * wm + r;
+  const int brow0 = SWI ? 32 * wn + r : 64 * wn + r, bstep = SWI ? 128 : 32;  // B rows of blocks 0 and 1
   f16x_t acc[BI][2];
 #pragma unroll
   for (int i = 0; i < BI; ++i) acc[i][0] = acc[i][1] = f16x_t{};
@@ -407,8 +422,8 @@ __global__ __launch_bounds__(512, 1) void pf_swiglu_big(const uint16_t* A, int M
         const int ko = 16 * (k0 + kk) + 8 * hf;
 #pragma unroll
         for (int i = 0; i < BI; ++i) oa[kk][i] = *reinterpret_cast<const v4u_t*>(la + (arow + 32 * i) * LS + ko);
-        ob[kk][0] = *reinterpret_cast<const v4u_t*>(lb + brow * LS + ko);
-        ob[kk][1] = *reinterpret_cast<const v4u_t*>(lb + (brow + 128) * LS + ko);
+        ob[kk][0] = *reinterpret_cast<const v4u_t*>(lb + brow0 * LS + ko);
+        ob[kk][1] = *reinterpret_cast<const v4u_t*>(lb + (brow0 + bstep) * LS + ko);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its products
 #pragma unroll
@@ -425,7 +440,8 @@ __global__ __launch_bounds__(512, 1) void pf_swiglu_big(const uint16_t* A, int M
     if (t + 1 < nk) stage(lds[(t + 1) & 1]);
     __syncthreads();
   }
-  // accumulator element 4ii + jj of acc[i][*]: row 128wm + 32i + 8ii + 4hf + jj, output column 32wn + r
+  // accumulator element 4ii + jj of acc[i][j]: row 128wm + 32i + 8ii + 4hf + jj; column: SwiGLU 32wn + r
+  // (gate j = 0, up j = 1), otherwise 64wn + 32j + r
 #pragma unroll
   for (int i = 0; i < BI; ++i)
 #pragma unroll
@@ -434,9 +450,29 @@ __global__ __launch_bounds__(512, 1) void pf_swiglu_big(const uint16_t* A, int M
       for (int jj = 0; jj < 4; ++jj) {
         const int m = m0 + 128 * wm + 32 * i + 8 * ii + 4 * hf + jj;
         if (m >= M) continue;
-        const float gt = acc[i][0][4 * ii + jj], up = acc[i][1][4 * ii + jj];
-        H[(size_t)m * F + n0 + 32 * wn + r] = f2h(gt / (1.0f + expf(-gt)) * up);
+        const int e = 4 * ii + jj;
+        if constexpr (SWI) {
+          const float gt = acc[i][0][e], up = acc[i][1][e];
+          H[(size_t)m * ldh + n0 + 32 * wn + r] = f2h(gt / (1.0f + expf(-gt)) * up);
+        } else {
+          float* cp = C + (size_t)m * ldc + n0 + 64 * wn + r;
+          if constexpr (EPI == EPI_ADD) {
+            cp[0] += acc[i][0][e];
+            cp[32] += acc[i][1][e];
+          } else {
+            cp[0] = acc[i][0][e];
+            cp[32] = acc[i][1][e];
+          }
+        }
       }
+}
+
+// Whether the 256 x 256 kernel pays for an output of M rows and `cols` tile
+// columns: one full round of work-groups (one per CU of the 256) for the store
+// and add forms, two for gate/up + SwiGLU (measured: 128 x 128 tiles win on
+// smaller grids).
+__host__ __device__ constexpr bool big_tiles_pay(int M, int cols, bool swiglu) {
+  return cols * ((M + kBigT - 1) / kBigT) >= (swiglu ? 512 : 256);
 }
 
 // Split-K reduction: C[m][n] (+)= sum over z = 0 .. S-1 of P[z][m][n], the
@@ -732,6 +768,16 @@ int splitk_slices(int M, int N, int K) {
 template <int DT>
 void launch_gemm(bool add, const act_t<DT>* A, int M, int K, const GemmB& b, int N, float* C, int ldc, float* P,
                  hipStream_t st) {
+  if constexpr (DT == KIE_F16) {
+    if (N % kBigT == 0 && b.end[0] % kBigT == 0 && b.end[1] % kBigT == 0 && big_tiles_pay(M, N / kBigT, false)) {
+      const dim3 g(N / kBigT, (M + kBigT - 1) / kBigT);
+      if (add)
+        pf_gemm_big<EPI_ADD><<<g, dim3(512), 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
+      else
+        pf_gemm_big<EPI_STORE><<<g, dim3(512), 0, st>>>(A, M, K, b, C, ldc, nullptr, 0);
+      return;
+    }
+  }
   const dim3 blk(256);
   const int mt = (M + kTM - 1) / kTM, S = splitk_slices<DT>(M, N, K);
   if (S == 1) {
@@ -754,9 +800,9 @@ template <int DT>
 void launch_swiglu(const act_t<DT>* A, int M, int K, const uint16_t* wg, const uint16_t* wu, int F, act_t<DT>* H,
                    hipStream_t st) {
   if constexpr (DT == KIE_F16) {
-    const int big = (F / (kBigT / 2)) * ((M + kBigT - 1) / kBigT);
-    if (F % (kBigT / 2) == 0 && big >= 512) {
-      pf_swiglu_big<<<dim3(F / (kBigT / 2), (M + kBigT - 1) / kBigT), dim3(512), 0, st>>>(A, M, K, wg, wu, H, F);
+    if (F % (kBigT / 2) == 0 && big_tiles_pay(M, F / (kBigT / 2), true)) {
+      pf_gemm_big<EPI_SWIGLU><<<dim3(F / (kBigT / 2), (M + kBigT - 1) / kBigT), dim3(512), 0, st>>>(
+          A, M, K, GemmB{{wg, wu}, {F, F, F}}, nullptr, 0, H, F);
       return;
     }
   }

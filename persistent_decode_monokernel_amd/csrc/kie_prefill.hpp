@@ -7,7 +7,7 @@
 
 namespace kie {
 
-constexpr int kPfChunk = 4096;  // prompt positions per chunk (bounds the activation buffers)
+constexpr int kPfChunk = 8192;  // prompt positions per chunk (bounds the activation buffers)
 
 // Device buffers and weights of one engine for the prompt path.
 struct PrefillCtx {

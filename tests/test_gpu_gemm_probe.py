@@ -5,8 +5,9 @@ touches the device.  GPU: C = A W^T, C += A W^T and silu(A Wg^T) * (A Wu^T) for
 fp16 (fp16 activations) and bf16 (fp32 activations split into three bf16
 terms) against a float64 product of the same inputs on the CPU: ragged row
 counts, split-K shapes (fewer than 512 output tiles) and an unsplit one; the
-fp16 gate/up + SwiGLU GEMM on grids of 512 and more 256 x 256 tiles (the
-long-prompt kernel), with a ragged last row tile.
+fp16 GEMMs on grids that fill the GPU with 256 x 256 tiles (the long-prompt
+kernel: store and add from 256 tiles, gate/up + SwiGLU from 512), with a
+ragged last row tile.
 """
 import ctypes
 
@@ -41,7 +42,10 @@ def test_split_k_needs_partial_buffer():
     assert _call(M=1, N=128, K=1024, pbytes=4 * 128 * 4 - 1) == kie.KIE_ERR_CAPACITY
 
 
-SHAPES = [(1, 128, 128), (77, 256, 512), (300, 384, 256), (512, 256, 2048), (1024, 8192, 128)]  # last: unsplit
+# (1024, 8192, 128): unsplit 128 x 128 tiles; the last two: fp16 on 256 x 256 tiles (256 and 320 of them,
+# the second with a ragged last row tile)
+SHAPES = [(1, 128, 128), (77, 256, 512), (300, 384, 256), (512, 256, 2048), (1024, 8192, 128), (2048, 8192, 64),
+          (1100, 16384, 64)]
 
 
 def _inputs(M, N, K, dt, seed):

@@ -3,9 +3,10 @@ reduced-depth models of the stated shapes.
 
 The ~2B decoder at long context takes a seeded 8192-token prompt, and the
 ~8B-shaped bf16 decoder a seeded 1024-token prompt.  Here both prompts (the
-workloads' own seeds) run through kie_prefill in the default mode with the
-default chunk: 8192 positions are two 4096-row matrix-core chunks, 1024 bf16
-positions one chunk with three-term activations.  The models have the exact
+workloads' own seeds) run through kie_prefill in the default mode: 8192
+positions as one 8192-row matrix-core chunk (the default; the fp16 GEMMs on
+256 x 256 tiles) and as two 4096-row chunks (set by kie_set_prefill_chunk),
+1024 bf16 positions as one chunk with three-term activations.  The models have the exact
 widths of the stated configurations (d 2048, GQA 16/4 x 128, SwiGLU 8192,
 vocab 32000, fp16; d 4096, GQA 32/8 x 128, SwiGLU 14336, vocab 128256, bf16)
 and two layers, so the float64 oracle finishes the whole prompt in seconds.
@@ -33,14 +34,16 @@ S2 = dataclasses.replace(synth.M2B, name="2b_2layers", n_layers=2)
 S8 = dataclasses.replace(synth.M8B, name="8b_2layers", n_layers=2)
 
 
-def run_prompt(shape, workload: str, n_decode: int, seg: int = 1024):
+def run_prompt(shape, workload: str, n_decode: int, seg: int = 1024, chunk: int = 0):
     wl = synth.WORKLOADS[workload]
     w = synth.make_weights(shape, wl.weight_seed, device="cuda")
     prompt = synth.make_prompt(shape, wl.n_prompt, wl.prompt_seed).tolist()
     P = len(prompt)
-    print(f"[prompt shapes] {shape.name}: prompt {P}, decode {n_decode}", flush=True)
+    print(f"[prompt shapes] {shape.name}: prompt {P}, decode {n_decode}, chunk {chunk or 'default'}", flush=True)
     eng = kie.Engine(shape, max_seq=P + n_decode + 1)
     eng.load_weights(w)
+    if chunk:
+        eng.set_prefill_chunk(chunk)
     tok0, lg0 = eng.prefill(prompt, want_logits=True)
     k, v, pend = eng.export_kv()
     assert pend == tok0 and k.shape[2] == P
@@ -76,8 +79,9 @@ def run_prompt(shape, workload: str, n_decode: int, seg: int = 1024):
     assert kerr <= KV_TOL and verr <= KV_TOL, (kerr, verr)
 
 
-def test_2b_shape_8192_token_prompt():
-    run_prompt(S2, "2b_long", 128)
+@pytest.mark.parametrize("chunk", [0, 4096], ids=["one_chunk", "two_chunks"])
+def test_2b_shape_8192_token_prompt(chunk):
+    run_prompt(S2, "2b_long", 128, chunk=chunk)
 
 
 def test_8b_shape_bf16_1024_token_prompt():

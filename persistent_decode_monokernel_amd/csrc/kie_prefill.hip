@@ -356,7 +356,8 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
 //   and up of one output land in the same lane.
 // k-tiles of 64, rows padded to 144 bytes, double-buffered, one barrier per
 // k-tile; the next k-tile's global loads are in flight during the current
-// one's products; operands read two k steps at a time.  Rows of A beyond M
+// one's products, and its LDS writes are spread over them, a quarter after
+// each 16-deep k step.  Rows of A beyond M
 // re-read row M-1 and are not stored.  Used when the grid fills the chip
 // (big_tiles_pay); the 128 x 128 kernel covers the rest.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));  // staging registers the compiler keeps in VGPRs
@@ -365,7 +366,8 @@ constexpr int kBigT = 256;                                     // tile rows of A
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void pf_gemm_big(const uint16_t* A, int M, int K, GemmB wb, float* C, int ldc,
                                                      uint16_t* H, int ldh) {
-  constexpr int BK = 64, LS = 72, NT = 512, RPP = NT / 8, PA = kBigT / RPP, PB = kBigT / RPP, BI = 4, KG = 2;
+  constexpr int BK = 64, LS = 72, NT = 512, RPP = NT / 8, PA = kBigT / RPP, PB = kBigT / RPP, BI = 4;
+  static_assert(PA == BK / 16 && PB == BK / 16, "one staging piece of A and of B per k step");
   constexpr bool SWI = EPI == EPI_SWIGLU;
   __shared__ __align__(16) uint16_t lds[2][2 * kBigT * LS];
   const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, r = l & 31, hf = l >> 5;
@@ -401,43 +403,39 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_big(const uint16_t* A, int M, 
 #pragma unroll
     for (int i = 0; i < PB; ++i) sb[i] = *reinterpret_cast<const v4u_t*>(bg[i] + k0);
   };
-  auto stage = [&](uint16_t* d) {
-#pragma unroll
-    for (int i = 0; i < PA; ++i) *reinterpret_cast<v4u_t*>(&d[soff + RPP * i * LS]) = sa[i];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) *reinterpret_cast<v4u_t*>(&d[kBigT * LS + soff + RPP * i * LS]) = sb[i];
+  auto stage = [&](uint16_t* d, int i) {  // staging piece i of A and of B
+    *reinterpret_cast<v4u_t*>(&d[soff + RPP * i * LS]) = sa[i];
+    *reinterpret_cast<v4u_t*>(&d[kBigT * LS + soff + RPP * i * LS]) = sb[i];
   };
   fetch(0);
-  stage(lds[0]);
+#pragma unroll
+  for (int i = 0; i < PA; ++i) stage(lds[0], i);
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
     if (t + 1 < nk) fetch((t + 1) * BK);
     const uint16_t* la = lds[t & 1];
     const uint16_t* lb = la + kBigT * LS;
+    // per 16-deep k step: read its operands, run its 8 products, then write one
+    // quarter of the next k-tile into the other buffer (last read before the
+    // previous barrier), so the LDS writes spread over the tile's products
 #pragma unroll
-    for (int k0 = 0; k0 < BK / 16; k0 += KG) {
-      v4u_t oa[KG][BI], ob[KG][2];
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int ko = 16 * kk + 8 * hf;
+      v4u_t oa[BI], ob[2];
 #pragma unroll
-      for (int kk = 0; kk < KG; ++kk) {
-        const int ko = 16 * (k0 + kk) + 8 * hf;
+      for (int i = 0; i < BI; ++i) oa[i] = *reinterpret_cast<const v4u_t*>(la + (arow + 32 * i) * LS + ko);
+      ob[0] = *reinterpret_cast<const v4u_t*>(lb + brow0 * LS + ko);
+      ob[1] = *reinterpret_cast<const v4u_t*>(lb + (brow0 + bstep) * LS + ko);
+      __builtin_amdgcn_sched_barrier(0);  // keep the step's reads ahead of its products
 #pragma unroll
-        for (int i = 0; i < BI; ++i) oa[kk][i] = *reinterpret_cast<const v4u_t*>(la + (arow + 32 * i) * LS + ko);
-        ob[kk][0] = *reinterpret_cast<const v4u_t*>(lb + brow0 * LS + ko);
-        ob[kk][1] = *reinterpret_cast<const v4u_t*>(lb + (brow0 + bstep) * LS + ko);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the group's reads ahead of its products
+      for (int i = 0; i < BI; ++i)
 #pragma unroll
-      for (int kk = 0; kk < KG; ++kk)
-#pragma unroll
-        for (int i = 0; i < BI; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, oa[kk][i]),
-                                                               __builtin_bit_cast(h8_t, ob[kk][j]), acc[i][j], 0, 0,
-                                                               0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, oa[i]),
+                                                             __builtin_bit_cast(h8_t, ob[j]), acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < nk) stage(lds[(t + 1) & 1], kk);
     }
-    if (t + 1 < nk) stage(lds[(t + 1) & 1]);
     __syncthreads();
   }
   // accumulator element 4ii + jj of acc[i][j]: row 128wm + 32i + 8ii + 4hf + jj; column: SwiGLU 32wn + r

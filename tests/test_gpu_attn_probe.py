@@ -3,8 +3,8 @@
 Host side (no GPU): argument errors the call rejects before it touches the
 device.  GPU: query rows p0 .. p0+M-1 against cache rows 0 .. p0+m, fp16 and
 bf16 caches, head widths 64 and 128, 1 / 2 / 4 / 8 query heads per KV head,
-ragged row counts and a nonzero start position, against plain softmax
-attention in float64 on the CPU over the same (stored) cache values.
+ragged row counts (up to 2100) and a nonzero start position, against plain
+softmax attention in float64 on the CPU over the same (stored) cache values.
 """
 import ctypes
 import math
@@ -35,7 +35,7 @@ def test_argument_errors_before_any_device_call(kw):
 
 CASES = [  # (hq, hkv, hd, p0, M)
     (4, 1, 128, 0, 1), (4, 1, 128, 0, 77), (8, 2, 64, 37, 130), (2, 2, 128, 5, 40), (8, 1, 64, 0, 200),
-    (16, 4, 128, 100, 64),
+    (16, 4, 128, 100, 64), (16, 4, 128, 0, 2100), (8, 1, 64, 64, 2048), (2, 2, 128, 3, 2077),
 ]
 
 
@@ -52,17 +52,18 @@ def test_causal_attention(dt, hq, hkv, hd, p0, M):
     out = torch.full((M, hq * hd), float("nan"), dtype=torch.float16 if dt == torch.float16 else torch.float32,
                      device=DEV)
     kie.attn_probe(qkv.to(DEV), kc.to(DEV), vc.to(DEV), out, hq, p0)
-    # plain softmax attention in float64 over the stored cache values
+    # plain softmax attention in float64 over the stored cache values: query m
+    # (position p0 + m) sees cache rows 0 .. p0 + m
     q = qkv[:, :hq * hd].double().view(M, hq, hd)
     K, V = kc.double(), vc.double()
+    n = p0 + M
+    visible = torch.arange(n)[None, :] <= (p0 + torch.arange(M))[:, None]
     ref = torch.empty(M, hq, hd, dtype=torch.float64)
     G = hq // hkv
-    for m in range(M):
-        n = p0 + m + 1
-        for h in range(hq):
-            s = K[h // G, :n] @ q[m, h] / math.sqrt(hd)
-            p = torch.softmax(s, 0)
-            ref[m, h] = p @ V[h // G, :n]
+    for h in range(hq):
+        sc = (q[:, h] @ K[h // G, :n].t()) / math.sqrt(hd)
+        sc = sc.masked_fill(~visible, float("-inf"))
+        ref[:, h] = torch.softmax(sc, 1) @ V[h // G, :n]
     got = out.cpu().double().view(M, hq, hd)
     err = (got - ref).abs().max().item()
     print(f"attention h{hq}/{hkv} d{hd} p0 {p0} M {M} {dt}: max |d| {err:.2e}", flush=True)

@@ -499,6 +499,57 @@ __global__ __launch_bounds__(256) void pf_splitk(const float* P, int S, int M, i
   *c = a;
 }
 
+// Split-K reduction into the residual, fused with the RMSNorm that consumes
+// it: one work-group per row m; X[m] += sum over z = 0 .. S-1 of P[z][m]
+// (slices added in order, then the residual, as pf_splitk), then Xn[m] =
+// RMSNorm(X[m]) * g.  Each thread keeps its 4-column groups of the row (at
+// most 16 values: d <= 4096) in registers between the two steps.
+template <int DT>
+__global__ __launch_bounds__(256) void pf_splitk_norm(const float* P, int S, int M, int d, float* X,
+                                                      const uint16_t* g, float eps, act_t<DT>* Xn) {
+  __shared__ float part[4];
+  const int m = blockIdx.x;
+  if (m >= M) return;
+  float4 v[4];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 4 * (int)threadIdx.x + 1024 * j;
+    if (n >= d) continue;
+    float4 a = *reinterpret_cast<const float4*>(P + (size_t)m * d + n);
+    for (int z = 1; z < S; ++z) {
+      const float4 b = *reinterpret_cast<const float4*>(P + ((size_t)z * M + m) * d + n);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    float4* xp = reinterpret_cast<float4*>(X + (size_t)m * d + n);
+    const float4 o = *xp;
+    a.x += o.x;
+    a.y += o.y;
+    a.z += o.z;
+    a.w += o.w;
+    *xp = a;
+    v[j] = a;
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 4 * (int)threadIdx.x + 1024 * j;
+    if (n >= d) continue;
+    act_t<DT>* xn = Xn + (size_t)m * d + n;
+    xn[0] = to_act<DT>(v[j].x * r * to_f<DT>(g[n]));
+    xn[1] = to_act<DT>(v[j].y * r * to_f<DT>(g[n + 1]));
+    xn[2] = to_act<DT>(v[j].z * r * to_f<DT>(g[n + 2]));
+    xn[3] = to_act<DT>(v[j].w * r * to_f<DT>(g[n + 3]));
+  }
+}
+
 // ---- rotary embedding, KV append ------------------------------------------
 //
 // Thread (m, i) for rotary pair i < hd/2 of every head: q rotated in place
@@ -793,6 +844,23 @@ void launch_gemm(bool add, const act_t<DT>* A, int M, int K, const GemmB& b, int
     pf_splitk<false><<<q, blk, 0, st>>>(P, S, M, N, C, ldc);
 }
 
+// X += A W^T (the residual add), then, if g is not null, Xn = RMSNorm(X) * g:
+// with split-K the reduction and the norm run as one pass over the rows.
+template <int DT>
+void launch_add_norm(const act_t<DT>* A, int M, int K, const GemmB& b, int d, float* X, float* P, const uint16_t* g,
+                     float eps, act_t<DT>* Xn, hipStream_t st) {
+  const int S = splitk_slices<DT>(M, d, K);
+  const bool big = DT == KIE_F16 && d % kBigT == 0 && b.end[0] % kBigT == 0 && b.end[1] % kBigT == 0 &&
+                   big_tiles_pay(M, d / kBigT, false);
+  if (S == 1 || big || !g || d > 4096) {
+    launch_gemm<DT>(true, A, M, K, b, d, X, d, P, st);
+    if (g) pf_rmsnorm<DT><<<M, dim3(256), 0, st>>>(X, g, eps, M, d, Xn);
+    return;
+  }
+  pf_gemm<EPI_PART, DT><<<dim3(d / kTN, (M + kTM - 1) / kTM, S), dim3(256), 0, st>>>(A, M, K, b, P, d, nullptr, 0);
+  pf_splitk_norm<DT><<<M, dim3(256), 0, st>>>(P, S, M, d, X, g, eps, Xn);
+}
+
 // H = silu(A Wg^T) * (A Wu^T), [M][F] activations.
 template <int DT>
 void launch_swiglu(const act_t<DT>* A, int M, int K, const uint16_t* wg, const uint16_t* wu, int F, act_t<DT>* H,
@@ -836,10 +904,11 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
     launch_gemm<DT>(add, A, M, K, b, N, C, ldc, x.P, st);
   };
   pf_embed<DT><<<M, blk, 0, st>>>(x.tok_emb, tok_dev, M, d, x.X);
+  pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, x.wtab[W_ATTN_NORM], c.rms_eps, M, d, Xn);
   for (int l = 0; l < c.n_layers; ++l) {
     const uint16_t* const* w = x.wtab + (size_t)l * W_PER_LAYER;
     const size_t plane = (size_t)l * c.n_kv_heads * c.max_seq * c.head_dim;
-    pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_ATTN_NORM], c.rms_eps, M, d, Xn);
+    // Xn holds RMSNorm(X) * g_attn of this layer (the previous layer's last step made it)
     const GemmB bqkv{{w[W_Q], w[W_K], w[W_V]}, {qd, qd + kvd, ldq}};
     gemm(false, Xn, d, bqkv, ldq, x.QKV, ldq);
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
@@ -847,10 +916,10 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
                                                             p0, c.max_seq, x.kc + plane, x.vc + plane);
     attn_launch<DT>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, p0, c.max_seq, x.kc + plane, x.vc + plane, Aa,
                     st);
-    gemm(true, Aa, qd, GemmB{{w[W_O]}, {d, d, d}}, d, x.X, d);
-    pf_rmsnorm<DT><<<M, blk, 0, st>>>(x.X, w[W_FFN_NORM], c.rms_eps, M, d, Xn);
+    launch_add_norm<DT>(Aa, M, qd, GemmB{{w[W_O]}, {d, d, d}}, d, x.X, x.P, w[W_FFN_NORM], c.rms_eps, Xn, st);
     launch_swiglu<DT>(Xn, M, d, w[W_GATE], w[W_UP], F, Hh, st);
-    gemm(true, Hh, F, GemmB{{w[W_DOWN]}, {d, d, d}}, d, x.X, d);
+    const uint16_t* g_next = l + 1 < c.n_layers ? x.wtab[(size_t)(l + 1) * W_PER_LAYER + W_ATTN_NORM] : nullptr;
+    launch_add_norm<DT>(Hh, M, F, GemmB{{w[W_DOWN]}, {d, d, d}}, d, x.X, x.P, g_next, c.rms_eps, Xn, st);
   }
   return hipGetLastError();
 }

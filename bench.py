@@ -293,7 +293,7 @@ def gemm_mfma_bench(reps: int = 10):
     shapes at 1024 rows (its three-term activations: three products per
     GEMM).  One JSON line per shape; TFLOP/s counts 2 M N K per product (the
     SwiGLU GEMM: 2 M 2F K).  Attention of the 512- and 8192-token prompts
-    (one and two chunks), next to the library's causal
+    (one chunk each), next to the library's causal
     scaled_dot_product_attention over the whole sequence."""
     import torch
 
@@ -346,12 +346,13 @@ def gemm_mfma_bench(reps: int = 10):
         torch.cuda.empty_cache()
 
     # causal attention of the ~2B prompts: ours over the prompt path's chunks
+    # (up to 8192 rows)
     # (kie_attn_probe), the library's scaled_dot_product_attention over the
     # whole sequence; flops 4 hq hd per (query, visible key) pair
     s = synth.WORKLOADS["2b"].shape
     hq, hkv, hd = s.n_heads, s.n_kv_heads, s.head_dim
     for P in (512, 8192):
-        chunks = [(p0, min(4096, P - p0)) for p0 in range(0, P, 4096)]
+        chunks = [(p0, min(8192, P - p0)) for p0 in range(0, P, 8192)]  # the prompt path's chunks
         kc = torch.randn(hkv, P, hd, device="cuda").half()
         vc = torch.randn(hkv, P, hd, device="cuda").half()
         ours = 0.0

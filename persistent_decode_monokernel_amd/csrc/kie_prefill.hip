@@ -605,9 +605,13 @@ __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int
 //     16c + 8(s/4) + 4(l/32) + s%4 for product c = 0, 1 of the tile, and V^T is
 //     read from LDS in that same row order.
 // Rows past the work-group's last key re-read that key (finite values, masked).
+// On large grids a work-group takes two query blocks in turn, the longest and
+// the shortest key range of a pair, so causal work is even across
+// work-groups; smaller grids keep one block per work-group (pairing would
+// leave compute units idle).
 template <int HD, int DT>
 __global__ __launch_bounds__(256, 2) void pf_attn(const float* QKV, int M, int hq, int hkv, int p0, int max_seq,
-                                               const uint16_t* kc, const uint16_t* vc, act_t<DT>* Aout) {
+                                               const uint16_t* kc, const uint16_t* vc, act_t<DT>* Aout, int pair) {
   constexpr int KS = HD + 8;  // K tile row stride (halves): 16-byte aligned rows, 4-bank skew
   constexpr int VS = 36;      // V^T tile row stride (halves): 8-byte reads of 32 rows hit distinct banks
   constexpr int KT = 32 * KS, VT = HD * VS, NO = HD / 32, NK = HD / 16;
@@ -616,167 +620,173 @@ __global__ __launch_bounds__(256, 2) void pf_attn(const float* QKV, int M, int h
   const int G = hq / hkv, HW = G < 4 ? G : 4, QB = 4 / HW, sets = G / HW;
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, hf = l >> 5;
   const int rows = 32 * QB, nqb = (M + rows - 1) / rows;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // longest key ranges first
-  const int g = (int)blockIdx.y / sets, h = g * G + ((int)blockIdx.y % sets) * HW + wave % HW;
-  const int mq0 = qb * rows + (wave / HW) * 32;
-  const int nkeys = p0 + min((qb + 1) * rows, M), nt = (nkeys + 31) / 32;
-  const int qd = hq * HD, ldq = qd + 2 * hkv * HD;
+  // work-group b takes query block nqb-1-b (the longest key range first);
+  // with `pair`, then block b (the shortest): every work-group streams about
+  // the same number of key tiles, so one round of work-groups ends together
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qb = pass == 0 ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;
+    if (pass == 1 && (!pair || qb >= nqb - 1 - (int)blockIdx.x)) break;  // an odd count's middle block runs once
+    const int g = (int)blockIdx.y / sets, h = g * G + ((int)blockIdx.y % sets) * HW + wave % HW;
+    const int mq0 = qb * rows + (wave / HW) * 32;
+    const int nkeys = p0 + min((qb + 1) * rows, M), nt = (nkeys + 31) / 32;
+    const int qd = hq * HD, ldq = qd + 2 * hkv * HD;
 
-  // this lane's query, scaled for base-2 exponentials, as B operands (bf16:
-  // QT terms of the split, each a product of its own)
-  constexpr int QT = DT == KIE_BF16 ? 2 : 1;
-  const float scale = 1.4426950408889634f / sqrtf((float)HD);
-  uint4 qf[QT][NK];
-  {
-    const float* qp = QKV + (size_t)min(mq0 + r, M - 1) * ldq + (size_t)h * HD + 8 * hf;
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(qp + 16 * kk);
-      const float4 b = *reinterpret_cast<const float4*>(qp + 16 * kk + 4);
-      const float x[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
-                          b.x * scale, b.y * scale, b.z * scale, b.w * scale};
-      if constexpr (DT == KIE_BF16) {
-        uint32_t w[4][QT];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_pair<QT>(x[2 * e], x[2 * e + 1], w[e]);
-#pragma unroll
-        for (int t = 0; t < QT; ++t) qf[t][kk] = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
-      } else {
-        qf[0][kk] = __builtin_bit_cast(uint4, h8_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
-                                                   (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]});
-      }
-    }
-  }
-
-  // tile staging.  K: thread t moves 16-byte piece t%CPR of cache rows
-  // 2(t/CPR), +1 (a wave's row-major writes cover consecutive banks).  V:
-  // thread t moves piece t/16 of rows 2(t%16), +1, so that the 16 lanes of a
-  // piece write the transposed words of 16 consecutive row pairs, 64 lanes
-  // spanning all banks.
-  const int tid = threadIdx.x, pe = tid % CPR, pr = tid / CPR, vpe = tid >> 4, vpr = tid & 15;
-  const bool loader = tid < 16 * CPR;
-  const uint16_t* kb = kc + (size_t)g * max_seq * HD + 8 * pe;
-  const uint16_t* vb = vc + (size_t)g * max_seq * HD + 8 * vpe;
-  uint4 k0r, k1r, v0r, v1r;
-  auto fetch = [&](int t) {
-    const int j0 = min(32 * t + 2 * pr, nkeys - 1), j1 = min(32 * t + 2 * pr + 1, nkeys - 1);
-    k0r = *reinterpret_cast<const uint4*>(kb + (size_t)j0 * HD);
-    k1r = *reinterpret_cast<const uint4*>(kb + (size_t)j1 * HD);
-    const int i0 = min(32 * t + 2 * vpr, nkeys - 1), i1 = min(32 * t + 2 * vpr + 1, nkeys - 1);
-    v0r = *reinterpret_cast<const uint4*>(vb + (size_t)i0 * HD);
-    v1r = *reinterpret_cast<const uint4*>(vb + (size_t)i1 * HD);
-  };
-  auto stage = [&](int buf) {
-    uint16_t* kt = lds + buf * (KT + VT);
-    uint16_t* vt = kt + KT;
-    *reinterpret_cast<uint4*>(kt + (2 * pr) * KS + 8 * pe) = k0r;
-    *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * KS + 8 * pe) = k1r;
-    const uint32_t a[4] = {v0r.x, v0r.y, v0r.z, v0r.w}, b[4] = {v1r.x, v1r.y, v1r.z, v1r.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {  // dimensions 8vpe+2u and 8vpe+2u+1, rows 2vpr (low half) and 2vpr+1
-      *reinterpret_cast<uint32_t*>(vt + (8 * vpe + 2 * u) * VS + 2 * vpr) = (a[u] & 0xFFFFu) | (b[u] << 16);
-      *reinterpret_cast<uint32_t*>(vt + (8 * vpe + 2 * u + 1) * VS + 2 * vpr) =
-          (a[u] >> 16) | (b[u] & 0xFFFF0000u);
-    }
-  };
-
-  f16x_t o[NO] = {};
-  float mrun = -INFINITY, lrun = 0.f;
-  const int qpos = p0 + mq0 + r;
-  if (loader) {
-    fetch(0);
-    stage(0);
-  }
-  __syncthreads();
-  for (int t = 0; t < nt; ++t) {
-    if (loader && t + 1 < nt) fetch(t + 1);
-    const uint16_t* kt = lds + (t & 1) * (KT + VT);
-    const uint16_t* vt = kt + KT;
-    f16x_t s = {};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const uint4 ka = *reinterpret_cast<const uint4*>(kt + r * KS + 16 * kk + 8 * hf);
-#pragma unroll
-      for (int t = QT - 1; t >= 0; --t) s = mma<DT>(ka, qf[t][kk], s);
-    }
-    const int k0 = 32 * t;
-    if (k0 + 31 > p0 + mq0) {  // the tile reaches past this wave's first query: causal mask
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (k0 + 8 * (e >> 2) + 4 * hf + (e & 3) > qpos) s[e] = -INFINITY;
-    }
-    float tm = s[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tm = fmaxf(tm, s[e]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
-    // Lazy rescaling: the reference maximum mrun moves only when a score
-    // exceeds it by more than 8 (base 2), so probabilities stay below 2^8 and
-    // most tiles skip rescaling the accumulators (the first tile always moves
-    // it: cache row 0 is in every query's range, so tm is finite).
-    const bool grow = tm > mrun + 8.f;
-    if (__any(grow)) {
-      const float mn = grow ? tm : mrun;
-      const float al = __builtin_amdgcn_exp2f(mrun - mn);
-      lrun *= al;
-#pragma unroll
-      for (int ot = 0; ot < NO; ++ot) o[ot] *= al;
-      mrun = mn;
-    }
-    const float mn = mrun;
-    float ps = 0.f;
-    float pv[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(s[e] - mn);
-      ps += pv[e];
-    }
-    uint4 pb[QT][2];  // probabilities as B operands (bf16: QT terms)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if constexpr (DT == KIE_BF16) {
-        uint32_t w[4][QT];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_pair<QT>(pv[8 * c + 2 * e], pv[8 * c + 2 * e + 1], w[e]);
-#pragma unroll
-        for (int t = 0; t < QT; ++t) pb[t][c] = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
-      } else {
-        const float* q = pv + 8 * c;
-        pb[0][c] = __builtin_bit_cast(uint4, h8_t{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3],
-                                                  (_Float16)q[4], (_Float16)q[5], (_Float16)q[6], (_Float16)q[7]});
-      }
-    }
-    lrun += ps;
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int ot = 0; ot < NO; ++ot) {
-        const uint16_t* vp = vt + (32 * ot + r) * VS + 16 * c + 4 * hf;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp), hi = *reinterpret_cast<const uint2*>(vp + 8);
-        const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-#pragma unroll
-        for (int t = QT - 1; t >= 0; --t) o[ot] = mma<DT>(a, pb[t][c], o[ot]);
-      }
-    if (loader && t + 1 < nt) stage((t + 1) & 1);
-    __syncthreads();
-  }
-  const float inv = 1.0f / (lrun + __shfl_xor(lrun, 32));
-  const int m = mq0 + r;
-  if (m < M) {
-    act_t<DT>* op = Aout + (size_t)m * qd + (size_t)h * HD + 4 * hf;
-#pragma unroll
-    for (int ot = 0; ot < NO; ++ot)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // dimensions 32ot + 8i + 4(l/32) + 0..3
-        const f16x_t& v = o[ot];
+    // this lane's query, scaled for base-2 exponentials, as B operands (bf16:
+    // QT terms of the split, each a product of its own)
+    constexpr int QT = DT == KIE_BF16 ? 2 : 1;
+    const float scale = 1.4426950408889634f / sqrtf((float)HD);
+    uint4 qf[QT][NK];
+    {
+      const float* qp = QKV + (size_t)min(mq0 + r, M - 1) * ldq + (size_t)h * HD + 8 * hf;
+  #pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const float4 a = *reinterpret_cast<const float4*>(qp + 16 * kk);
+        const float4 b = *reinterpret_cast<const float4*>(qp + 16 * kk + 4);
+        const float x[8] = {a.x * scale, a.y * scale, a.z * scale, a.w * scale,
+                            b.x * scale, b.y * scale, b.z * scale, b.w * scale};
         if constexpr (DT == KIE_BF16) {
-          *reinterpret_cast<float4*>(op + 32 * ot + 8 * i) =
-              make_float4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+          uint32_t w[4][QT];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) split_pair<QT>(x[2 * e], x[2 * e + 1], w[e]);
+  #pragma unroll
+          for (int t = 0; t < QT; ++t) qf[t][kk] = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
         } else {
-          *reinterpret_cast<uint2*>(op + 32 * ot + 8 * i) =
-              make_uint2((uint32_t)f2h(v[4 * i] * inv) | ((uint32_t)f2h(v[4 * i + 1] * inv) << 16),
-                         (uint32_t)f2h(v[4 * i + 2] * inv) | ((uint32_t)f2h(v[4 * i + 3] * inv) << 16));
+          qf[0][kk] = __builtin_bit_cast(uint4, h8_t{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                                                     (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]});
         }
       }
+    }
+
+    // tile staging.  K: thread t moves 16-byte piece t%CPR of cache rows
+    // 2(t/CPR), +1 (a wave's row-major writes cover consecutive banks).  V:
+    // thread t moves piece t/16 of rows 2(t%16), +1, so that the 16 lanes of a
+    // piece write the transposed words of 16 consecutive row pairs, 64 lanes
+    // spanning all banks.
+    const int tid = threadIdx.x, pe = tid % CPR, pr = tid / CPR, vpe = tid >> 4, vpr = tid & 15;
+    const bool loader = tid < 16 * CPR;
+    const uint16_t* kb = kc + (size_t)g * max_seq * HD + 8 * pe;
+    const uint16_t* vb = vc + (size_t)g * max_seq * HD + 8 * vpe;
+    uint4 k0r, k1r, v0r, v1r;
+    auto fetch = [&](int t) {
+      const int j0 = min(32 * t + 2 * pr, nkeys - 1), j1 = min(32 * t + 2 * pr + 1, nkeys - 1);
+      k0r = *reinterpret_cast<const uint4*>(kb + (size_t)j0 * HD);
+      k1r = *reinterpret_cast<const uint4*>(kb + (size_t)j1 * HD);
+      const int i0 = min(32 * t + 2 * vpr, nkeys - 1), i1 = min(32 * t + 2 * vpr + 1, nkeys - 1);
+      v0r = *reinterpret_cast<const uint4*>(vb + (size_t)i0 * HD);
+      v1r = *reinterpret_cast<const uint4*>(vb + (size_t)i1 * HD);
+    };
+    auto stage = [&](int buf) {
+      uint16_t* kt = lds + buf * (KT + VT);
+      uint16_t* vt = kt + KT;
+      *reinterpret_cast<uint4*>(kt + (2 * pr) * KS + 8 * pe) = k0r;
+      *reinterpret_cast<uint4*>(kt + (2 * pr + 1) * KS + 8 * pe) = k1r;
+      const uint32_t a[4] = {v0r.x, v0r.y, v0r.z, v0r.w}, b[4] = {v1r.x, v1r.y, v1r.z, v1r.w};
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {  // dimensions 8vpe+2u and 8vpe+2u+1, rows 2vpr (low half) and 2vpr+1
+        *reinterpret_cast<uint32_t*>(vt + (8 * vpe + 2 * u) * VS + 2 * vpr) = (a[u] & 0xFFFFu) | (b[u] << 16);
+        *reinterpret_cast<uint32_t*>(vt + (8 * vpe + 2 * u + 1) * VS + 2 * vpr) =
+            (a[u] >> 16) | (b[u] & 0xFFFF0000u);
+      }
+    };
+
+    f16x_t o[NO] = {};
+    float mrun = -INFINITY, lrun = 0.f;
+    const int qpos = p0 + mq0 + r;
+    if (loader) {
+      fetch(0);
+      stage(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
+      if (loader && t + 1 < nt) fetch(t + 1);
+      const uint16_t* kt = lds + (t & 1) * (KT + VT);
+      const uint16_t* vt = kt + KT;
+      f16x_t s = {};
+  #pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(kt + r * KS + 16 * kk + 8 * hf);
+  #pragma unroll
+        for (int t = QT - 1; t >= 0; --t) s = mma<DT>(ka, qf[t][kk], s);
+      }
+      const int k0 = 32 * t;
+      if (k0 + 31 > p0 + mq0) {  // the tile reaches past this wave's first query: causal mask
+  #pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (k0 + 8 * (e >> 2) + 4 * hf + (e & 3) > qpos) s[e] = -INFINITY;
+      }
+      float tm = s[0];
+  #pragma unroll
+      for (int e = 1; e < 16; ++e) tm = fmaxf(tm, s[e]);
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      // Lazy rescaling: the reference maximum mrun moves only when a score
+      // exceeds it by more than 8 (base 2), so probabilities stay below 2^8 and
+      // most tiles skip rescaling the accumulators (the first tile always moves
+      // it: cache row 0 is in every query's range, so tm is finite).
+      const bool grow = tm > mrun + 8.f;
+      if (__any(grow)) {
+        const float mn = grow ? tm : mrun;
+        const float al = __builtin_amdgcn_exp2f(mrun - mn);
+        lrun *= al;
+  #pragma unroll
+        for (int ot = 0; ot < NO; ++ot) o[ot] *= al;
+        mrun = mn;
+      }
+      const float mn = mrun;
+      float ps = 0.f;
+      float pv[16];
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        pv[e] = __builtin_amdgcn_exp2f(s[e] - mn);
+        ps += pv[e];
+      }
+      uint4 pb[QT][2];  // probabilities as B operands (bf16: QT terms)
+  #pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (DT == KIE_BF16) {
+          uint32_t w[4][QT];
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) split_pair<QT>(pv[8 * c + 2 * e], pv[8 * c + 2 * e + 1], w[e]);
+  #pragma unroll
+          for (int t = 0; t < QT; ++t) pb[t][c] = make_uint4(w[0][t], w[1][t], w[2][t], w[3][t]);
+        } else {
+          const float* q = pv + 8 * c;
+          pb[0][c] = __builtin_bit_cast(uint4, h8_t{(_Float16)q[0], (_Float16)q[1], (_Float16)q[2], (_Float16)q[3],
+                                                    (_Float16)q[4], (_Float16)q[5], (_Float16)q[6], (_Float16)q[7]});
+        }
+      }
+      lrun += ps;
+  #pragma unroll
+      for (int c = 0; c < 2; ++c)
+  #pragma unroll
+        for (int ot = 0; ot < NO; ++ot) {
+          const uint16_t* vp = vt + (32 * ot + r) * VS + 16 * c + 4 * hf;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vp), hi = *reinterpret_cast<const uint2*>(vp + 8);
+          const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  #pragma unroll
+          for (int t = QT - 1; t >= 0; --t) o[ot] = mma<DT>(a, pb[t][c], o[ot]);
+        }
+      if (loader && t + 1 < nt) stage((t + 1) & 1);
+      __syncthreads();
+    }
+    const float inv = 1.0f / (lrun + __shfl_xor(lrun, 32));
+    const int m = mq0 + r;
+    if (m < M) {
+      act_t<DT>* op = Aout + (size_t)m * qd + (size_t)h * HD + 4 * hf;
+  #pragma unroll
+      for (int ot = 0; ot < NO; ++ot)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {  // dimensions 32ot + 8i + 4(l/32) + 0..3
+          const f16x_t& v = o[ot];
+          if constexpr (DT == KIE_BF16) {
+            *reinterpret_cast<float4*>(op + 32 * ot + 8 * i) =
+                make_float4(v[4 * i] * inv, v[4 * i + 1] * inv, v[4 * i + 2] * inv, v[4 * i + 3] * inv);
+          } else {
+            *reinterpret_cast<uint2*>(op + 32 * ot + 8 * i) =
+                make_uint2((uint32_t)f2h(v[4 * i] * inv) | ((uint32_t)f2h(v[4 * i + 1] * inv) << 16),
+                           (uint32_t)f2h(v[4 * i + 2] * inv) | ((uint32_t)f2h(v[4 * i + 3] * inv) << 16));
+          }
+        }
+    }
   }
 }
 
@@ -881,13 +891,18 @@ void launch_swiglu(const act_t<DT>* A, int M, int K, const uint16_t* wg, const u
 template <int DT>
 void attn_launch(const float* qkv, int M, int hq, int hkv, int hd, int p0, int max_seq, const uint16_t* kc,
                  const uint16_t* vc, void* out, hipStream_t st) {
-  const int G = hq / hkv, hw = G < 4 ? G : 4, rows = 32 * (4 / hw);
-  const dim3 ag((M + rows - 1) / rows, hkv * (G / hw));
+  const int G = hq / hkv, hw = G < 4 ? G : 4, rows = 32 * (4 / hw), nqb = (M + rows - 1) / rows;
+  const int ny = hkv * (G / hw);
+  // pairs of query blocks while the paired grid still gives every compute
+  // unit two work-groups (measured: 8192 rows from position 0 gain, 4096-row
+  // chunks and short prompts lose)
+  const int pair = ((nqb + 1) / 2) * ny >= 512 ? 1 : 0;
+  const dim3 ag(pair ? (nqb + 1) / 2 : nqb, ny);
   act_t<DT>* o = static_cast<act_t<DT>*>(out);
   if (hd == 128)
-    pf_attn<128, DT><<<ag, dim3(256), 0, st>>>(qkv, M, hq, hkv, p0, max_seq, kc, vc, o);
+    pf_attn<128, DT><<<ag, dim3(256), 0, st>>>(qkv, M, hq, hkv, p0, max_seq, kc, vc, o, pair);
   else
-    pf_attn<64, DT><<<ag, dim3(256), 0, st>>>(qkv, M, hq, hkv, p0, max_seq, kc, vc, o);
+    pf_attn<64, DT><<<ag, dim3(256), 0, st>>>(qkv, M, hq, hkv, p0, max_seq, kc, vc, o, pair);
 }
 
 template <int DT>

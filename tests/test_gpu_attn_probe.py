@@ -3,8 +3,10 @@
 Host side (no GPU): argument errors the call rejects before it touches the
 device.  GPU: query rows p0 .. p0+M-1 against cache rows 0 .. p0+m, fp16 and
 bf16 caches, head widths 64 and 128, 1 / 2 / 4 / 8 query heads per KV head,
-ragged row counts (up to 2100) and a nonzero start position, against plain
-softmax attention in float64 on the CPU over the same (stored) cache values.
+ragged row counts (up to 2100) and a nonzero start position, grids with one
+query block per work-group and grids large enough for pairs of blocks,
+against plain softmax attention in float64 on the CPU over the same (stored)
+cache values.
 """
 import ctypes
 import math
@@ -36,6 +38,8 @@ def test_argument_errors_before_any_device_call(kw):
 CASES = [  # (hq, hkv, hd, p0, M)
     (4, 1, 128, 0, 1), (4, 1, 128, 0, 77), (8, 2, 64, 37, 130), (2, 2, 128, 5, 40), (8, 1, 64, 0, 200),
     (16, 4, 128, 100, 64), (16, 4, 128, 0, 2100), (8, 1, 64, 64, 2048), (2, 2, 128, 3, 2077),
+    # 63 query blocks x 16 head groups: work-groups take pairs of blocks (the middle one alone)
+    (64, 16, 64, 0, 2010), (64, 16, 64, 40, 2010),
 ]
 
 

@@ -112,20 +112,47 @@ __global__ __launch_bounds__(256) void pf_embed(const uint16_t* E, const int* to
   for (int i = threadIdx.x; i < d; i += 256) X[(size_t)m * d + i] = to_f<DT>(row[i]);
 }
 
+// Xn[n .. n+3] = v * r * g[n .. n+3] as activations (one 8- or 16-byte store).
+template <int DT>
+__device__ __forceinline__ void norm_store4(act_t<DT>* xn, const uint16_t* g, float4 v, float r) {
+  const uint2 gw = *reinterpret_cast<const uint2*>(g);
+  const float g0 = to_f<DT>((uint16_t)gw.x), g1 = to_f<DT>((uint16_t)(gw.x >> 16));
+  const float g2 = to_f<DT>((uint16_t)gw.y), g3 = to_f<DT>((uint16_t)(gw.y >> 16));
+  if constexpr (DT == KIE_BF16) {
+    *reinterpret_cast<float4*>(xn) = make_float4(v.x * r * g0, v.y * r * g1, v.z * r * g2, v.w * r * g3);
+  } else {
+    *reinterpret_cast<uint2*>(xn) = make_uint2((uint32_t)f2h(v.x * r * g0) | ((uint32_t)f2h(v.y * r * g1) << 16),
+                                               (uint32_t)f2h(v.z * r * g2) | ((uint32_t)f2h(v.w * r * g3) << 16));
+  }
+}
+
+// One work-group per row: the row (d <= 4096, a multiple of 128) in float4
+// pieces, 4 consecutive columns per thread and pass, kept in registers between
+// the sum of squares and the scaled store.
 template <int DT>
 __global__ __launch_bounds__(256) void pf_rmsnorm(const float* X, const uint16_t* g, float eps, int M, int d,
                                                   act_t<DT>* Xn) {
   __shared__ float part[4];
   const int m = blockIdx.x;
   if (m >= M) return;
-  const float* x = X + (size_t)m * d;
+  float4 v[4];
   float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) ss += x[i] * x[i];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 4 * (int)threadIdx.x + 1024 * j;
+    if (n >= d) continue;
+    v[j] = *reinterpret_cast<const float4*>(X + (size_t)m * d + n);
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
   __syncthreads();
   const float r = 1.0f / sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)d + eps);
-  for (int i = threadIdx.x; i < d; i += 256) Xn[(size_t)m * d + i] = to_act<DT>(x[i] * r * to_f<DT>(g[i]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = 4 * (int)threadIdx.x + 1024 * j;
+    if (n < d) norm_store4<DT>(Xn + (size_t)m * d + n, g + n, v[j], r);
+  }
 }
 
 // ---- GEMM: C[M][N] = A[M][K] W[N][K]^T on the matrix cores --------------------
@@ -541,49 +568,56 @@ __global__ __launch_bounds__(256) void pf_splitk_norm(const float* P, int S, int
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = 4 * (int)threadIdx.x + 1024 * j;
-    if (n >= d) continue;
-    act_t<DT>* xn = Xn + (size_t)m * d + n;
-    xn[0] = to_act<DT>(v[j].x * r * to_f<DT>(g[n]));
-    xn[1] = to_act<DT>(v[j].y * r * to_f<DT>(g[n + 1]));
-    xn[2] = to_act<DT>(v[j].z * r * to_f<DT>(g[n + 2]));
-    xn[3] = to_act<DT>(v[j].w * r * to_f<DT>(g[n + 3]));
+    if (n < d) norm_store4<DT>(Xn + (size_t)m * d + n, g + n, v[j], r);
   }
 }
 
 // ---- rotary embedding, KV append ------------------------------------------
 //
-// Thread (m, i) for rotary pair i < hd/2 of every head: q rotated in place
-// (fp32, as the decode path keeps it); k rotated and v copied into the cache
-// rows at position p0 + m.
+// Thread (m, i) for rotary pairs i .. i+3 (i a multiple of 4, < hd/2) of every
+// head: q rotated in place (fp32, as the decode path keeps it); k rotated and
+// v copied into the cache rows at position p0 + m.  16-byte loads of the
+// fp32 rows and of the (cos, sin) table, 8-byte stores into the cache.
+template <int DT>
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+  return make_uint2((uint32_t)from_f<DT>(a) | ((uint32_t)from_f<DT>(b) << 16),
+                    (uint32_t)from_f<DT>(c) | ((uint32_t)from_f<DT>(d) << 16));
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void pf_rope_kv(float* QKV, int M, int hq, int hkv, int hd, const float* rope,
                                                   int p0, int max_seq, uint16_t* kc, uint16_t* vc) {
   const int half = hd >> 1, qd = hq * hd, kvd = hkv * hd, ld = qd + 2 * kvd;
-  const int per_row = (hq + hkv) * half + hkv * half;  // q pairs, k pairs, v pairs
+  const int per_row = ((hq + hkv) * half + hkv * half) / 4;  // groups of 4 q, k and v pairs
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= M * per_row) return;
-  const int m = idx / per_row, r = idx % per_row, pos = p0 + m;
-  const float* row = QKV + (size_t)m * ld;
+  const int m = idx / per_row, r = 4 * (idx % per_row), pos = p0 + m;
+  float* row = QKV + (size_t)m * ld;
   if (r < (hq + hkv) * half) {
     const int h = r / half, i = r % half;
-    const float c = rope[((size_t)pos * half + i) * 2], s = rope[((size_t)pos * half + i) * 2 + 1];
-    float* src = QKV + (size_t)m * ld + (size_t)h * hd;  // q heads, then k heads (contiguous)
-    const float a = src[i], b = src[i + half];
-    const float ra = a * c - b * s, rb = a * s + b * c;
+    const float4 cs0 = *reinterpret_cast<const float4*>(rope + ((size_t)pos * half + i) * 2);
+    const float4 cs1 = *reinterpret_cast<const float4*>(rope + ((size_t)pos * half + i) * 2 + 4);
+    float* src = row + (size_t)h * hd;  // q heads, then k heads (contiguous)
+    const float4 a = *reinterpret_cast<const float4*>(src + i), b = *reinterpret_cast<const float4*>(src + i + half);
+    const float4 ra = make_float4(a.x * cs0.x - b.x * cs0.y, a.y * cs0.z - b.y * cs0.w, a.z * cs1.x - b.z * cs1.y,
+                                  a.w * cs1.z - b.w * cs1.w);
+    const float4 rb = make_float4(a.x * cs0.y + b.x * cs0.x, a.y * cs0.w + b.y * cs0.z, a.z * cs1.y + b.z * cs1.x,
+                                  a.w * cs1.w + b.w * cs1.z);
     if (h < hq) {
-      src[i] = ra;
-      src[i + half] = rb;
+      *reinterpret_cast<float4*>(src + i) = ra;
+      *reinterpret_cast<float4*>(src + i + half) = rb;
     } else {
       uint16_t* dst = kc + ((size_t)(h - hq) * max_seq + pos) * hd;
-      dst[i] = from_f<DT>(ra);
-      dst[i + half] = from_f<DT>(rb);
+      *reinterpret_cast<uint2*>(dst + i) = pack4<DT>(ra.x, ra.y, ra.z, ra.w);
+      *reinterpret_cast<uint2*>(dst + i + half) = pack4<DT>(rb.x, rb.y, rb.z, rb.w);
     }
   } else {
     const int rr = r - (hq + hkv) * half, g = rr / half, i = rr % half;
     const float* src = row + qd + kvd + (size_t)g * hd;
     uint16_t* dst = vc + ((size_t)g * max_seq + pos) * hd;
-    dst[i] = from_f<DT>(src[i]);
-    dst[i + half] = from_f<DT>(src[i + half]);
+    const float4 a = *reinterpret_cast<const float4*>(src + i), b = *reinterpret_cast<const float4*>(src + i + half);
+    *reinterpret_cast<uint2*>(dst + i) = pack4<DT>(a.x, a.y, a.z, a.w);
+    *reinterpret_cast<uint2*>(dst + i + half) = pack4<DT>(b.x, b.y, b.z, b.w);
   }
 }
 
@@ -927,7 +961,7 @@ hipError_t run_chunk(const PrefillCtx& x, const int* tok_dev, int p0, int M) {
     const GemmB bqkv{{w[W_Q], w[W_K], w[W_V]}, {qd, qd + kvd, ldq}};
     gemm(false, Xn, d, bqkv, ldq, x.QKV, ldq);
     const int pairs = (c.n_heads + 2 * c.n_kv_heads) * (c.head_dim / 2);
-    pf_rope_kv<DT><<<(M * pairs + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope,
+    pf_rope_kv<DT><<<(M * (pairs / 4) + 255) / 256, blk, 0, st>>>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, x.rope,
                                                             p0, c.max_seq, x.kc + plane, x.vc + plane);
     attn_launch<DT>(x.QKV, M, c.n_heads, c.n_kv_heads, c.head_dim, p0, c.max_seq, x.kc + plane, x.vc + plane, Aa,
                     st);

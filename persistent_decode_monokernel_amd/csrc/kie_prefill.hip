@@ -382,9 +382,10 @@ __global__ __launch_bounds__(256, 2) void pf_gemm(const act_t<DT>* A, int M, int
 //   columns; wave wn takes gate rows 32wn .. and the matching up rows, so gate
 //   and up of one output land in the same lane.
 // k-tiles of 64, rows padded to 144 bytes, double-buffered, one barrier per
-// k-tile; the next k-tile's global loads are in flight during the current
-// one's products, and its LDS writes are spread over them, a quarter after
-// each 16-deep k step.  Rows of A beyond M
+// k-tile; the next k-tile's LDS writes are spread over the current one's
+// products, a quarter after each 16-deep k step, and each quarter's registers
+// are then refilled from the k-tile after that, so a global load has a whole
+// k-tile of products to land.  Rows of A beyond M
 // re-read row M-1 and are not stored.  Used when the grid fills the chip
 // (big_tiles_pay); the 128 x 128 kernel covers the rest.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));  // staging registers the compiler keeps in VGPRs
@@ -424,27 +425,36 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_big(const uint16_t* A, int M, 
   for (int i = 0; i < BI; ++i) acc[i][0] = acc[i][1] = f16x_t{};
   v4u_t sa[PA], sb[PB];
   const int nk = K / BK;
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < PA; ++i) sa[i] = *reinterpret_cast<const v4u_t*>(ag[i] + k0);
-#pragma unroll
-    for (int i = 0; i < PB; ++i) sb[i] = *reinterpret_cast<const v4u_t*>(bg[i] + k0);
+  auto fetch = [&](int k0, int i) {  // staging piece i of A and of B from global memory
+    sa[i] = *reinterpret_cast<const v4u_t*>(ag[i] + k0);
+    sb[i] = *reinterpret_cast<const v4u_t*>(bg[i] + k0);
   };
-  auto stage = [&](uint16_t* d, int i) {  // staging piece i of A and of B
+  auto stage = [&](uint16_t* d, int i) {  // staging piece i of A and of B into LDS
     *reinterpret_cast<v4u_t*>(&d[soff + RPP * i * LS]) = sa[i];
     *reinterpret_cast<v4u_t*>(&d[kBigT * LS + soff + RPP * i * LS]) = sb[i];
   };
-  fetch(0);
+  // The refills and LDS writes run on every k-tile, the k offset clamped to the
+  // last tile (repeated loads of it, written to the buffer no later tile
+  // reads): without branches around them the compiler waits for each piece's
+  // own loads, not for all loads in flight.
+#pragma unroll
+  for (int i = 0; i < PA; ++i) fetch(0, i);
 #pragma unroll
   for (int i = 0; i < PA; ++i) stage(lds[0], i);
+#pragma unroll
+  for (int i = 0; i < PA; ++i) {  // in piece order, as the loop issues them
+    fetch(min(1, nk - 1) * BK, i);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   __syncthreads();
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) fetch((t + 1) * BK);
     const uint16_t* la = lds[t & 1];
     const uint16_t* lb = la + kBigT * LS;
     // per 16-deep k step: read its operands, run its 8 products, then write one
     // quarter of the next k-tile into the other buffer (last read before the
-    // previous barrier), so the LDS writes spread over the tile's products
+    // previous barrier), so the LDS writes spread over the tile's products,
+    // and refill the freed registers with the same quarter of the k-tile after
+    // that: every global load has a whole k-tile of products to land in
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int ko = 16 * kk + 8 * hf;
@@ -461,7 +471,8 @@ __global__ __launch_bounds__(512, 1) void pf_gemm_big(const uint16_t* A, int M, 
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, oa[i]),
                                                              __builtin_bit_cast(h8_t, ob[j]), acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < nk) stage(lds[(t + 1) & 1], kk);
+      stage(lds[(t + 1) & 1], kk);
+      fetch(min(t + 2, nk - 1) * BK, kk);
     }
     __syncthreads();
   }

@@ -167,6 +167,9 @@ def gemv_probe_bench(n_copies: int = 16):
     1000 fresh vectors in ONE persistent launch of the same GEMV engine the
     decode stages use, over n_copies rotating weight copies (16 x 32 MiB = 512
     MiB, beyond the 256 MB Infinity Cache) or one copy (cache-resident).
+    Two forms: "stage" (each product loads its input first, as a decode stage
+    whose input arrives by hand-off) and "streaming" (the next input and the
+    next product's first weight vectors are read during the current product).
     Algorithmic bytes per vector: the matrix, the input vector, the output."""
     import torch
 
@@ -175,14 +178,16 @@ def gemv_probe_bench(n_copies: int = 16):
     for (rows, cols), seed in zip(synth.GEMV_SHAPES, synth.GEMV_SEEDS):
         for nc in (n_copies, 1):
             W, x = synth.make_gemv(rows, cols, synth.GEMV_N_VEC, seed, n_copies=nc, device="cuda")
-            kie.gemv_probe(W, x[:8])  # warm-up
-            _, ms = kie.gemv_probe(W, x)
-            per = rows * cols * 2 + cols * 2 + rows * 4
-            gbs = per * synth.GEMV_N_VEC / (ms / 1e3) / 1e9
-            print(json.dumps({"gemv": f"{rows}x{cols} fp16", "copies": nc, "vectors": synth.GEMV_N_VEC,
-                              "kernel_ms": ms, "us_per_gemv": ms * 1e3 / synth.GEMV_N_VEC, "GB/s": gbs,
-                              "frac_of_8000": gbs / HBM_PEAK_GBS,
-                              "note": "HBM stream" if nc > 1 else "Infinity-Cache resident"}), flush=True)
+            for streaming in (False, True):
+                kie.gemv_probe(W, x[:8], streaming=streaming)  # warm-up
+                _, ms = kie.gemv_probe(W, x, streaming=streaming)
+                per = rows * cols * 2 + cols * 2 + rows * 4
+                gbs = per * synth.GEMV_N_VEC / (ms / 1e3) / 1e9
+                print(json.dumps({"gemv": f"{rows}x{cols} fp16", "form": "streaming" if streaming else "stage",
+                                  "copies": nc, "vectors": synth.GEMV_N_VEC,
+                                  "kernel_ms": ms, "us_per_gemv": ms * 1e3 / synth.GEMV_N_VEC, "GB/s": gbs,
+                                  "frac_of_8000": gbs / HBM_PEAK_GBS,
+                                  "note": "HBM stream" if nc > 1 else "Infinity-Cache resident"}), flush=True)
             del W, x
             torch.cuda.empty_cache()
 
@@ -532,7 +537,8 @@ def timeline(wl, step: int = 10, n_decode: int = 32, samp=None, handoff: int = 0
     eng.decode(n_decode)
     ms = eng.info().last_kernel_ms
     G = eng.info().grid
-    tr = buf.cpu().numpy().astype(np.float64).reshape(-1, G, 4) / 100.0  # microseconds
+    # work-group-major layout [grid][slot][4] -> [slot][grid][4]
+    tr = buf.cpu().numpy().astype(np.float64).reshape(G, -1, 4).transpose(1, 0, 2) / 100.0  # microseconds
     L = s.n_layers
     print(f"workload {wl.name}: kie_decode({n_decode}) after {P} prompt positions, {ms:.2f} ms "
           f"({ms / n_decode * 1e3:.1f} us/token); timeline of step {step}, grid {G}")

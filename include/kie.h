@@ -376,13 +376,14 @@ kie_status kie_set_launch_mode(kie_engine* e, int32_t mode);
 kie_status kie_check_idle_sets(const kie_engine* e, uint64_t* dirty_words);
 
 /* Per-token timeline.  kie_trace_words(e) = uint64 words a trace buffer
- * needs: (n_layers*6 + 2) slots x grid work-groups x 4 stamps.  After
+ * needs: (n_layers*6 + 3) slots x grid work-groups x 4 stamps.  After
  * kie_set_trace(e, buf, step), every persistent launch of the engine stamps
  * loop iteration `step` (relative to the launch) into buf: for slot s (layer l
  * stage k at s = 6*l + k with k = 0 QKV, 1 attention, 2 merge, 3 Wo,
  * 4 gate/up, 5 down; then s = 6*L LM head, 6*L + 1 step tail: partial
  * published / partials gathered / exchange set recycled / token known) and
- * work-group w, buf[(s*grid + w)*4 + j] holds the 100 MHz real-time counter at
+ * work-group w, buf[(w*S + s)*4 + j] (S = n_layers*6 + 3 slots per work-group)
+ * holds the 100 MHz real-time counter at
  * stage entry (j = 0), when the stage's input had arrived (j = 1), when its
  * arithmetic was done (j = 2) and at stage exit (j = 3).  Thread 0 of each
  * work-group writes them (the recycling stamp: thread 256); entries a
@@ -409,11 +410,17 @@ kie_status kie_check_tiling(const kie_config* cfg, int32_t grid, int32_t full);
  * [n_copies][rows][cols] of dtype: vector i uses copy i % n_copies (several
  * copies defeat the memory-side cache).  x_dev [n_vec][cols] of dtype;
  * y_dev [n_vec][rows] float.  cols a multiple of 256; rows >= 1.
+ * streaming = 0 (stage form): each product first loads its input vector and
+ * then streams its weights, as a decode stage whose input arrives by hand-off.
+ * streaming = 1 (streaming form): the next input vector and the next
+ * product's first weight vectors are read while the current product streams,
+ * so the weight stream runs on across products.  Both forms give the same y.
  * *kernel_ms receives the launch duration (HIP events) if not NULL.
- * Runs on hip_stream (NULL = default) and synchronises it. */
+ * Runs on hip_stream (NULL = default) and synchronises it.  KIE_ERR_ARG for a
+ * NULL or misaligned pointer, a bad size, dtype or streaming flag. */
 kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
                           const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
-                          void* hip_stream, float* kernel_ms);
+                          int32_t streaming, void* hip_stream, float* kernel_ms);
 
 /* ---- read-stream probe --------------------------------------------------- */
 

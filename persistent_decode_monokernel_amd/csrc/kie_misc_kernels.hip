@@ -48,9 +48,12 @@ const void* stream_probe_fn(int depth) {
   return nullptr;
 }
 
-const void* gemv_probe_fn(int dtype) {
-  return dtype == KIE_F16 ? reinterpret_cast<const void*>(&gemv_probe<KIE_F16>)
-                          : reinterpret_cast<const void*>(&gemv_probe<KIE_BF16>);
+const void* gemv_probe_fn(int dtype, bool pipelined) {
+  if (pipelined)
+    return dtype == KIE_F16 ? reinterpret_cast<const void*>(&gemv_probe<KIE_F16, true>)
+                            : reinterpret_cast<const void*>(&gemv_probe<KIE_BF16, true>);
+  return dtype == KIE_F16 ? reinterpret_cast<const void*>(&gemv_probe<KIE_F16, false>)
+                          : reinterpret_cast<const void*>(&gemv_probe<KIE_BF16, false>);
 }
 
 hipError_t launch_fill(uint32_t* p, uint64_t n, uint32_t v, hipStream_t st) {

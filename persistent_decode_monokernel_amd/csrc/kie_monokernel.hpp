@@ -62,10 +62,13 @@ typedef const __attribute__((address_space(4))) Params CParams;
 __device__ __forceinline__ CParams& cparams(const Params* Pp) { return *(CParams*)opaque_s(Pp); }
 
 // Timeline stamp k of a slot, by thread `who` of the work-group (only on the
-// traced step).  k: 0 entry, 1 input arrived, 2 compute done, 3 exit.
+// traced step).  k: 0 entry, 1 input arrived, 2 compute done, 3 exit.  tr is
+// this work-group's row of the trace (work-group-major layout, so no grid
+// size is needed here: reading gridDim is a vector-memory load of the
+// dispatch packet, and waiting for it would also wait for every weight load
+// in flight).
 __device__ __forceinline__ void stamp(uint64_t* tr, int slot, int k, int t, int who = 0) {
-  if (tr && t == who)
-    tr[((size_t)slot * gridDim.x + blockIdx.x) * kTraceStamps + k] = __builtin_amdgcn_s_memrealtime();
+  if (tr && t == who) tr[(size_t)slot * kTraceStamps + k] = __builtin_amdgcn_s_memrealtime();
 }
 
 // Wait until every store this thread issued has been performed.  Exchange and
@@ -88,7 +91,25 @@ __device__ __forceinline__ void publish_delay(CParams& P) {
   }
 }
 
-// Issue the first kDepth vectors of the next GEMV stage into the ring.
+// The ring's first kRingSplit slots of a GEMV stage are issued ahead of the
+// stage's input poll (by the previous stage, or the stage's prologue); the
+// other slots right after the poll's loads, before its result is awaited.
+// Loads return in issue order, so a poll issued behind the whole ring waits
+// for all of it; issued behind part of it, the poll returns sooner while the
+// rest of the ring keeps the weight stream going.
+#ifndef KIE_RING_SPLIT
+#define KIE_RING_SPLIT 8
+#endif
+constexpr int kRingSplit = KIE_RING_SPLIT;
+static_assert(kRingSplit >= 1 && kRingSplit <= kDepth, "ring split");
+
+// Slots issued ahead of a stage's poll for a GEMV of width class VC (rows of
+// at least 512 columns: kRingSplit; the narrow rows of small models keep the
+// whole ring ahead -- the compiler crashed on the split form of those).
+template <int VC>
+constexpr int ring_split() { return VC > 0 ? kRingSplit : kDepth; }
+// Issue the first RS vectors of the next GEMV stage into the ring.
+template <int RS>
 __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np);
 
 // ---------------------------------------------------------------------------
@@ -130,7 +151,7 @@ struct Sc {
 __device__ __forceinline__ Sc stage_ctx(const Params* Pp, char* smem) {
   CParams& P = cparams(Pp);
   return Sc{P, lds_view(smem, P), Watch{P.timeout, P.ctl + CTL_STATUS}, opaque_v((int)threadIdx.x),
-            (int)blockIdx.x, (int)gridDim.x};
+            (int)blockIdx.x, P.grid};  // the grid from the parameters: a scalar load (see stamp)
 }
 
 // Work-group-wide "any thread failed" with a barrier.
@@ -158,7 +179,7 @@ __device__ __forceinline__ bool await_all(CParams& P, uint32_t* X, int k, const 
   bool ok = true;
   if (t == 0) {
     const uint32_t* p = X + P.xl.cnt + k;
-    const uint32_t want = kSent + (uint32_t)gridDim.x;
+    const uint32_t want = kSent + (uint32_t)P.grid;
     if (xld32(p) != want) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       int n = 0;
@@ -192,74 +213,164 @@ __device__ __forceinline__ float block_sum(float v, float* misc, int t) {
 // ---------------------------------------------------------------------------
 // Batched poll of nw 8-byte exchange words src[2i..2i+1], i < nw, spread over
 // the work-group (word i on thread i % 512).  Each thread issues the loads of
-// up to kPollBatch words at once and waits once, then re-polls only the words
+// a batch of its words at once and waits once, then re-polls only the words
 // that were not written yet, so a vector costs about one memory round trip
 // instead of one per word.  store(i, v) receives every word once.  Ends with a
 // barrier; false if a poll expired.
+//
+// The first batch holds NB words per thread and is issued unconditionally
+// (a thread past the vector re-reads its first word) and outside any loop, and
+// it is first looked at outside the re-poll loop.  The compiler's waits for
+// loaded registers are only exact on straight-line code: with the loads under
+// branches or in a loop it waited, before each load and before the first
+// look, for every older load -- the next GEMV stage's weight vectors
+// included, also those that after() issues behind the batch.
 constexpr int kPollBatch = 8;
-template <class Ready, class Store>
-__device__ __forceinline__ bool poll_words(const uint32_t* src, int nw, const Watch& w, int t, Ready ready,
-                                           Store store) {
-  bool ok = true;
-  for (int base = t; base < nw && ok; base += kPollBatch * kThreads) {
-    uint64_t v[kPollBatch];
-    uint32_t pending = 0;
+constexpr int kPollD = 4;  // first batch of model-width vectors: d <= 4096 floats = 4 words per thread
+struct NoAfter {
+  __device__ void operator()() const {}
+};
+// Re-poll the words of mask `again` until all are written.
+template <int NB, class Ready, class Store>
+__device__ __forceinline__ bool repoll(const uint32_t* src, int base, uint32_t again, uint64_t (&v)[NB],
+                                       const Watch& w, Ready ready, Store store) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  int n = 0;
+  for (;;) {
+    __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-    for (int k = 0; k < kPollBatch; ++k) {
-      const int i = base + k * kThreads;
-      if (i < nw) {
-        v[k] = xld64(src + 2 * (size_t)i);
-        pending |= 1u << k;
+    for (int k = 0; k < NB; ++k)
+      if (again & (1u << k)) v[k] = xld64(src + 2 * (size_t)(base + k * kThreads));
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t pending = again;
+    again = 0;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (pending & (1u << k)) {
+        if (ready(v[k])) store(base + k * kThreads, v[k]);
+        else again |= 1u << k;
       }
     }
-    uint64_t t0 = 0;
-    int n = 0;
-    for (;;) {
-      uint32_t again = 0;
+    if (!again) return true;
+    if (w.expired(t0, n)) return false;
+  }
+}
+// First batch: words t + k * 512, k < NB; after() runs once the loads are issued.
+template <int NB, class Ready, class Store, class After>
+__device__ __forceinline__ bool poll_first(const uint32_t* src, int nw, int t, const Watch& w, Ready ready,
+                                           Store store, After after) {
+  uint64_t v[NB];
+  uint32_t pending = 0;
+  const int own = t < nw ? t : 0;
 #pragma unroll
-      for (int k = 0; k < kPollBatch; ++k) {
-        if (pending & (1u << k)) {
-          if (ready(v[k])) store(base + k * kThreads, v[k]);
-          else again |= 1u << k;
-        }
-      }
-      if (!again) break;
-      if (t0 == 0) {
-        t0 = __builtin_amdgcn_s_memrealtime();
-      } else if (w.expired(t0, n)) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+  for (int k = 0; k < NB; ++k) {
+    const int i = t + k * kThreads;
+    v[k] = xld64(src + 2 * (size_t)(i < nw ? i : own));
+    pending |= (i < nw ? 1u : 0u) << k;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load of the batch issued before any look
+  after();
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t again = 0;
 #pragma unroll
-      for (int k = 0; k < kPollBatch; ++k)
-        if (again & (1u << k)) v[k] = xld64(src + 2 * (size_t)(base + k * kThreads));
-      pending = again;
+  for (int k = 0; k < NB; ++k) {
+    if (pending & (1u << k)) {
+      if (ready(v[k])) store(t + k * kThreads, v[k]);
+      else again |= 1u << k;
     }
   }
+  return !again || repoll<NB>(src, t, again, v, w, ready, store);
+}
+// Later batches (vectors beyond NB * 512 words): words base + k * 512.  Which
+// loads a wave issues is decided on the wave's first word (a scalar branch;
+// every vector length is a multiple of 64 words).
+template <class Ready, class Store>
+__device__ __forceinline__ bool poll_batch(const uint32_t* src, int nw, int base, const Watch& w, Ready ready,
+                                           Store store) {
+  uint64_t v[kPollBatch];
+  uint32_t pending = 0;
+  const int b0 = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+  for (int k = 0; k < kPollBatch; ++k) {
+    const int i = base + k * kThreads;
+    if (b0 + k * kThreads < nw) {
+      v[k] = xld64(src + 2 * (size_t)(i < nw ? i : 0));
+      pending |= (i < nw ? 1u : 0u) << k;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t again = 0;
+#pragma unroll
+  for (int k = 0; k < kPollBatch; ++k) {
+    if (pending & (1u << k)) {
+      if (ready(v[k])) store(base + k * kThreads, v[k]);
+      else again |= 1u << k;
+    }
+  }
+  return !again || repoll<kPollBatch>(src, base, again, v, w, ready, store);
+}
+template <int NB = kPollBatch, class Ready, class Store, class After = NoAfter>
+__device__ __forceinline__ bool poll_words(const uint32_t* src, int nw, const Watch& w, int t, Ready ready,
+                                           Store store, After after = NoAfter{}) {
+  static_assert(NB >= 1 && NB <= 32, "first poll batch");
+  bool ok = poll_first<NB>(src, nw, t, w, ready, store, after);
+  for (int base = t + NB * kThreads; base < nw && ok; base += kPollBatch * kThreads)
+    ok = poll_batch(src, nw, base, w, ready, store);
   return !any_failed(!ok);
 }
 // Poll n fp32 words (n even) of an exchange buffer into LDS as fp32.
-__device__ __forceinline__ bool poll_f32(const uint32_t* src, int n, float* dst, const Watch& w, int t) {
-  return poll_words(src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) {
-    dst[2 * i] = lo_f(v);
-    dst[2 * i + 1] = hi_f(v);
-  });
+// NB: words per thread of the first batch (see poll_words).
+template <int NB = kPollBatch, class After = NoAfter>
+__device__ __forceinline__ bool poll_f32(const uint32_t* src, int n, float* dst, const Watch& w, int t,
+                                         After after = NoAfter{}) {
+  return poll_words<NB>(
+      src, n >> 1, w, t, Ready32x2{},
+      [&](int i, uint64_t v) {
+        dst[2 * i] = lo_f(v);
+        dst[2 * i + 1] = hi_f(v);
+      },
+      after);
 }
 // Poll n fp32 words into LDS as 16-bit activations.
-template <int DT>
-__device__ __forceinline__ bool poll_to16(const uint32_t* src, int n, uint16_t* dst, const Watch& w, int t) {
-  return poll_words(src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) { act_store2<DT>(dst, i, lo_f(v), hi_f(v)); });
+template <int DT, int NB = kPollBatch, class After = NoAfter>
+__device__ __forceinline__ bool poll_to16(const uint32_t* src, int n, uint16_t* dst, const Watch& w, int t,
+                                          After after = NoAfter{}) {
+  return poll_words<NB>(
+      src, n >> 1, w, t, Ready32x2{}, [&](int i, uint64_t v) { act_store2<DT>(dst, i, lo_f(v), hi_f(v)); }, after);
 }
-// xn = RMSNorm(x) * g, rounded to 16 bits.  Ends with a barrier.
+// The RMSNorm gains of this thread's elements t + k * 512 (n <= 4096), read
+// before the stage's poll: issued after it, they cost one more memory round
+// trip on the hand-off's critical path.  The loads are unconditional (a lane
+// past n re-reads element 0) and fenced from the code that uses them: under a
+// branch the compiler converted each value right after its load, waiting for
+// it and for every older load.
+constexpr int kGainRegs = 8;
+struct Gains {
+  uint32_t v[kGainRegs];  // one 16-bit gain each
+};
+__device__ __forceinline__ Gains load_gains(const uint16_t* g, int n, int t) {
+  Gains r;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    r.v[k] = g[i < n ? i : 0];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  return r;
+}
+// xn = RMSNorm(x) * g, rounded to 16 bits, with g from load_gains.  Ends with a barrier.
 template <int DT>
-__device__ __forceinline__ void rmsnorm_to16(const float* x, const uint16_t* g, int n, float eps, uint16_t* xn,
+__device__ __forceinline__ void rmsnorm_to16(const float* x, const Gains& g, int n, float eps, uint16_t* xn,
                                              float* misc, int t) {
   float ss = 0.f;
   for (int i = t; i < n; i += kThreads) ss += x[i] * x[i];
   ss = block_sum(ss, misc, t);
   const float r = 1.0f / sqrtf(ss / (float)n + eps);
-  for (int i = t; i < n; i += kThreads) act_store<DT>(xn, i, x[i] * r * to_f32<DT>(g[i]));
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    if (i < n) act_store<DT>(xn, i, x[i] * r * to_f32<DT>((uint16_t)g.v[k]));
+  }
   __syncthreads();
 }
 
@@ -375,7 +486,9 @@ __device__ __forceinline__ uint4 plan_load(const StagePlan& g, const WideRows& w
 // this stage drains its last block it issues the first kDepth vectors of the
 // next GEMV stage (next(i) = address of that stage's vector i, or nullptr when
 // there is none), so the weight stream does not stop at the hand-off.
-template <int DT, int VPT, bool WIDE, class Prep>
+// RS: ring slots issued ahead of prep (the decode stages: kRingSplit; the
+// GEMV probe: all of them).
+template <int DT, int VPT, bool WIDE, class Prep, int RS = kRingSplit>
 __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv, int t,
                                      uint4 (&ring)[kDepth], bool prefilled, const StagePlan next, uint64_t* tr,
                                      int slot) {
@@ -388,11 +501,20 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
     if constexpr (WIDE) return wr.load(pj, i);
     else return ldw(g.addr<VPT>(pj * VPT + i));
   };
-  if (Jp > 0 && !prefilled) {
+  const bool any = uni(Jp) > 0;
+  if (any && !prefilled) {
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = wload(i / VPT, i % VPT);
+    for (int i = 0; i < RS; ++i) ring[i] = wload(i / VPT, i % VPT);
   }
-  if (!prep()) return false;
+  // prep(fill) must call fill() once: it issues the ring's other slots.  No
+  // branch around them (every work-group owns rows of every GEMV stage: the
+  // host keeps the grid within d_model, d_ffn and the vocabulary), so the
+  // compiler's wait for the poll before them stays exact.
+  auto fill = [&]() {
+#pragma unroll
+    for (int i = RS; i < kDepth; ++i) ring[i] = wload(i / VPT, i % VPT);
+  };
+  if (!prep(fill)) return false;
   const bool has_next = next.nrows > 0;
   if (Jp > 0) {
     constexpr int AW = kActWords<DT>;
@@ -428,7 +550,7 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
 #pragma unroll
       for (int i = 0; i < kDepth; ++i) {  // last block: drain, refill with the next stage
         acc = dot(ring[i], i, acc);
-        ring[i] = plan_load(next, nw, i);
+        if (i < RS) ring[i] = plan_load(next, nw, i);
         if (i % VPT == VPT - 1) {
           gv_park<WIDE>(acc, (j0 + i) / VPT, g, red, t);
           acc = 0.f;
@@ -447,7 +569,7 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
   } else if (has_next) {
     const WideRows nw = next.lpr >= 64 ? wide_rows(next) : WideRows{};
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = plan_load(next, nw, i);
+    for (int i = 0; i < RS; ++i) ring[i] = plan_load(next, nw, i);
   }
   stamp(tr, slot, 2, t);
   __syncthreads();
@@ -460,11 +582,12 @@ __device__ __forceinline__ bool gemv(const StagePlan& g, Prep prep, const uint16
   return true;
 }
 
+template <int RS>
 __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const StagePlan& np) {
   if (np.nrows > 0) {
     const WideRows nw = np.lpr >= 64 ? wide_rows(np) : WideRows{};
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) ring[i] = plan_load(np, nw, i);
+    for (int i = 0; i < RS; ++i) ring[i] = plan_load(np, nw, i);
   }
 }
 
@@ -473,17 +596,18 @@ __device__ __forceinline__ void ring_prefetch(uint4 (&ring)[kDepth], const Stage
 template <int DT, int VC, class Prep>
 __device__ __forceinline__ bool gemv_cls(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv,
                                          int t, uint4 (&ring)[kDepth], bool prefilled, uint64_t* tr, int slot) {
-  return gemv<DT, (VC > 0 ? VC : 1), (VC > 0)>(g, prep, xs, red, yv, t, ring, prefilled, StagePlan{}, tr, slot);
+  return gemv<DT, (VC > 0 ? VC : 1), (VC > 0), Prep, ring_split<VC>()>(g, prep, xs, red, yv, t, ring, prefilled,
+                                                                       StagePlan{}, tr, slot);
 }
 
 template <int DT, class Prep>
 __device__ __forceinline__ bool gemv_any(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv,
                                          int t, uint4 (&ring)[kDepth], bool prefilled, const StagePlan next,
                                          uint64_t* tr = nullptr, int slot = 0) {
-  if (g.vpr < 64) return gemv<DT, 1, false>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
-  if (g.vpt == 1) return gemv<DT, 1, true>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
-  if (g.vpt == 2) return gemv<DT, 2, true>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
-  return gemv<DT, 4, true>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpr < 64) return gemv<DT, 1, false, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpt == 1) return gemv<DT, 1, true, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpt == 2) return gemv<DT, 2, true, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  return gemv<DT, 4, true, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
 }
 
 
@@ -521,10 +645,12 @@ __device__ KIE_INLINE bool st_qkv(const Params* Pp, char* smem, int l, uint32_t*
   const int N = nq + 2 * nk;
   const int r0 = split_lo(N, c.nb, c.wg), r1 = split_lo(N, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, l, GS_QKV, c.t, c.wg, c.nb);
-  auto prep = [&]() -> bool {
+  auto prep = [&](auto fill) -> bool {
+    const Gains gn = load_gains(lw_ptr(P, l, W_ATTN_NORM), d, c.t);
+    if (l == 0) fill();  // the embedding row is already in LDS
     if (l > 0 && !await_all<HO>(P, X, (l - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
-    if (l > 0 && !poll_f32(X + P.xl.xout + (size_t)(l - 1) * d, d, c.s.xres, c.w, c.t)) return false;
-    rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_ATTN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
+    if (l > 0 && !poll_f32<kPollD>(X + P.xl.xout + (size_t)(l - 1) * d, d, c.s.xres, c.w, c.t, fill)) return false;
+    rmsnorm_to16<DT>(c.s.xres, gn, d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
     return true;
   };
@@ -623,6 +749,7 @@ __device__ KIE_INLINE bool st_attn(const Params* Pp, char* smem, int l, int pos,
                          : role == 1 ? src + (size_t)hq * hd + (size_t)g * hd
                                      : src + (size_t)(hq + hkv) * hd + (size_t)g * hd;
       uint64_t va = xld64(sp + 2 * m), vb2 = xld64(sp + 2 * m + half);  // both in flight, one wait
+      __builtin_amdgcn_sched_barrier(0);  // (the compiler had hoisted the first check above the second load)
       if (!(Ready32x2{}(va) && Ready32x2{}(vb2)))
         ok = poll64(sp + 2 * m, va, c.w, Ready32x2{}) && poll64(sp + 2 * m + half, vb2, c.w, Ready32x2{});
       float a0 = lo_f(va), a1 = hi_f(va), b0 = lo_f(vb2), b1 = hi_f(vb2);
@@ -790,6 +917,7 @@ __device__ KIE_INLINE bool st_merge(const Params* Pp, char* smem, int l, int pos
       const uint32_t* op = rowp + 4 + sl * 8;
       // issue all five loads, then wait once
       uint64_t mlv = xld64(rowp), o01 = xld64(op), o23 = xld64(op + 2), o45 = xld64(op + 4), o67 = xld64(op + 6);
+      __builtin_amdgcn_sched_barrier(0);
       const Ready32x2 rd{};
       if (!(rd(mlv) && rd(o01) && rd(o23) && rd(o45) && rd(o67))) {
         ok = poll64(rowp, mlv, c.w, rd) && poll64(op, o01, c.w, rd) && poll64(op + 2, o23, c.w, rd) &&
@@ -839,9 +967,9 @@ __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* 
   const int d = P.d, K = P.hq * P.hd;
   const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, l, GS_WO, c.t, c.wg, c.nb);
-  auto prep = [&]() -> bool {
+  auto prep = [&](auto fill) -> bool {
     if (!await_all<HO>(P, X, l * kStagesPerLayer + 2, c.w, c.t)) return false;
-    const bool r = poll_to16<DT>(X + P.xl.a + (size_t)l * K, K, c.s.xn, c.w, c.t);
+    const bool r = poll_to16<DT, kPollD>(X + P.xl.a + (size_t)l * K, K, c.s.xn, c.w, c.t, fill);
     stamp(tr, slot, 1, c.t);
     return r;
   };
@@ -852,13 +980,13 @@ __device__ KIE_INLINE bool st_wo(const Params* Pp, char* smem, int l, uint32_t* 
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
   arrive<HO>(P, X, l * kStagesPerLayer + 3, c.t);
-  if constexpr (!PS) ring_prefetch(ring, np);  // after the output stores: they must not queue behind it
+  if constexpr (!PS) ring_prefetch<ring_split<VD>()>(ring, np);  // after the output stores: they must not queue behind it
   stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // h = silu(Wg n) * (Wu n), n = RMSNorm(x_mid) * g_ffn
-template <int DT, int VD, bool HO, bool PS>
+template <int DT, int VD, int VF, bool HO, bool PS>
 __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
@@ -868,10 +996,11 @@ __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32
   const int f0 = split_lo(F, c.nb, c.wg), f1 = split_lo(F, c.nb, c.wg + 1);
   const int nf = f1 - f0;
   const StagePlan pl = plan_stage(P, l, GS_GATEUP, c.t, c.wg, c.nb);
-  auto prep = [&]() -> bool {
+  auto prep = [&](auto fill) -> bool {
+    const Gains gn = load_gains(lw_ptr(P, l, W_FFN_NORM), d, c.t);
     if (!await_all<HO>(P, X, l * kStagesPerLayer + 3, c.w, c.t)) return false;
-    if (!poll_f32(X + P.xl.xmid + (size_t)l * d, d, c.s.xres, c.w, c.t)) return false;
-    rmsnorm_to16<DT>(c.s.xres, lw_ptr(P, l, W_FFN_NORM), d, P.eps, c.s.xn, c.s.misc, c.t);
+    if (!poll_f32<kPollD>(X + P.xl.xmid + (size_t)l * d, d, c.s.xres, c.w, c.t, fill)) return false;
+    rmsnorm_to16<DT>(c.s.xres, gn, d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
     return true;
   };
@@ -884,13 +1013,13 @@ __device__ KIE_INLINE bool st_gateup(const Params* Pp, char* smem, int l, uint32
     xst32(dst + f0 + f, __float_as_uint(gt / (1.0f + expf(-gt)) * up));
   }
   arrive<HO>(P, X, l * kStagesPerLayer + 4, c.t);
-  if constexpr (!PS) ring_prefetch(ring, np);
+  if constexpr (!PS) ring_prefetch<ring_split<VF>()>(ring, np);
   stamp(tr, slot, 3, c.t);
   return true;
 }
 
 // x_next = x_mid + Wd h
-template <int DT, int VF, bool HO, bool PS>
+template <int DT, int VD, int VF, bool HO, bool PS>
 __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t* X, uint64_t* tr, uint4 (&ring)[kDepth]) {
   const Sc c = stage_ctx(Pp, smem);
   CParams& P = c.P;
@@ -899,9 +1028,9 @@ __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t
   const int d = P.d, F = P.F;
   const int r0 = split_lo(d, c.nb, c.wg), r1 = split_lo(d, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, l, GS_DOWN, c.t, c.wg, c.nb);
-  auto prep = [&]() -> bool {
+  auto prep = [&](auto fill) -> bool {
     if (!await_all<HO>(P, X, l * kStagesPerLayer + 4, c.w, c.t)) return false;
-    const bool r = poll_to16<DT>(X + P.xl.h + (size_t)l * F, F, c.s.xn, c.w, c.t);
+    const bool r = poll_to16<DT, kPollBatch>(X + P.xl.h + (size_t)l * F, F, c.s.xn, c.w, c.t, fill);
     stamp(tr, slot, 1, c.t);
     return r;
   };
@@ -913,7 +1042,7 @@ __device__ KIE_INLINE bool st_down(const Params* Pp, char* smem, int l, uint32_t
   for (int r = c.t; r < r1 - r0; r += kThreads)
     xst32(dst + r0 + r, __float_as_uint(c.s.xres[r0 + r] + c.s.yv[r]));
   arrive<HO>(P, X, l * kStagesPerLayer + 5, c.t);
-  if constexpr (!PS) ring_prefetch(ring, np);
+  if constexpr (!PS) ring_prefetch<ring_split<VD>()>(ring, np);
   stamp(tr, slot, 3, c.t);
   return true;
 }
@@ -1251,7 +1380,7 @@ __device__ KIE_INLINE bool gather_sample(const Params* Pp, char* smem, uint32_t*
 // The sampled token: work-groups 0 .. ceil(grid/8)-1 merge groups of lists,
 // work-group 0 draws the token and publishes it, the others poll it.
 __device__ KIE_INLINE bool sampled_token(const Params* Pp, char* smem, uint32_t* X, int pos, int& tok, uint64_t* tr) {
-  if ((int)blockIdx.x < ((int)gridDim.x + 7) / 8 && !group_merge(Pp, smem, X)) return false;
+  if ((int)blockIdx.x < (cparams(Pp).grid + 7) / 8 && !group_merge(Pp, smem, X)) return false;
   if (blockIdx.x == 0) {
     if (!gather_sample(Pp, smem, X, pos, tok, tr)) return false;
     publish_delay(cparams(Pp));
@@ -1287,10 +1416,11 @@ __device__ KIE_INLINE bool st_lmhead(const Params* Pp, char* smem, uint32_t* X, 
   const int d = P.d, V = P.V;
   const int v0 = split_lo(V, c.nb, c.wg), v1 = split_lo(V, c.nb, c.wg + 1);
   const StagePlan pl = plan_stage(P, 0, GS_LM, c.t, c.wg, c.nb);
-  auto prep = [&]() -> bool {
+  auto prep = [&](auto fill) -> bool {
     if (!await_all<HO>(P, X, (P.L - 1) * kStagesPerLayer + 5, c.w, c.t)) return false;
-    if (!poll_f32(X + P.xl.xout + (size_t)(P.L - 1) * d, d, c.s.xres, c.w, c.t)) return false;
-    rmsnorm_to16<DT>(c.s.xres, P.final_norm, d, P.eps, c.s.xn, c.s.misc, c.t);
+    const Gains gn = load_gains(P.final_norm, d, c.t);
+    if (!poll_f32<kPollD>(X + P.xl.xout + (size_t)(P.L - 1) * d, d, c.s.xres, c.w, c.t, fill)) return false;
+    rmsnorm_to16<DT>(c.s.xres, gn, d, P.eps, c.s.xn, c.s.misc, c.t);
     stamp(tr, slot, 1, c.t);
     return true;
   };
@@ -1405,11 +1535,13 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     const int pos = P.pos0 + s;
     if (P.forced) tok = P.forced[s];
     uint32_t* X = P.xch + (size_t)(s % kRingSets) * P.xl.words;
-    uint64_t* tr = (P.trace && s == P.trace_step) ? P.trace : nullptr;
+    uint64_t* tr = (P.trace && s == P.trace_step)
+                       ? P.trace + (size_t)wg * (P.L * kStagesPerLayer + 3) * kTraceStamps
+                       : nullptr;
     const bool lm_only = cparams(Pp).lm_only != 0;
     if (lm_only) {  // the LM head's first weight vectors (no down stage issued them)
       const Sc c = stage_ctx(Pp, smem);
-      ring_prefetch(ring, plan_stage(c.P, 0, GS_LM, c.t, c.wg, c.nb));
+      ring_prefetch<ring_split<VD>()>(ring, plan_stage(c.P, 0, GS_LM, c.t, c.wg, c.nb));
     } else {  // embedding row -> residual stream
       const Sc c = stage_ctx(Pp, smem);
       const uint16_t* er = c.P.tok_emb + (size_t)tok * c.P.d;
@@ -1419,8 +1551,8 @@ __global__ __launch_bounds__(kThreads, 1) void monokernel(const Params* __restri
     for (int l = 0; l < L && ok && !lm_only; ++l) {
       ok = st_qkv<DT, VD, HO>(Pp, smem, l, X, tr, ring) && st_attn<DT, G, HO>(Pp, smem, l, pos, X, tr) &&
            st_merge<DT, HO>(Pp, smem, l, pos, X, tr) && st_wo<DT, VD, HO, false>(Pp, smem, l, X, tr, ring) &&
-           st_gateup<DT, VD, HO, false>(Pp, smem, l, X, tr, ring) &&
-           st_down<DT, VF, HO, false>(Pp, smem, l, X, tr, ring);
+           st_gateup<DT, VD, VF, HO, false>(Pp, smem, l, X, tr, ring) &&
+           st_down<DT, VD, VF, HO, false>(Pp, smem, l, X, tr, ring);
     }
     if (!ok) break;
     float bv = 0.f;
@@ -1496,7 +1628,11 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __rest
     for (int i = c.t; i < P.d; i += kThreads) c.s.xres[i] = to_f32<DT>(er[i]);
     __syncthreads();
   };
-  auto own_prefetch = [&](int lay, int gs) { ring_prefetch(ring, plan_stage(P, lay, gs, c.t, c.wg, c.nb)); };
+  auto own_prefetch = [&](int lay, int gs) {
+    const StagePlan np = plan_stage(P, lay, gs, c.t, c.wg, c.nb);
+    if (gs == GS_DOWN) ring_prefetch<ring_split<VF>()>(ring, np);
+    else ring_prefetch<ring_split<VD>()>(ring, np);
+  };
   bool ok = true;
   switch (st) {
     case 0:
@@ -1513,12 +1649,12 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __rest
       break;
     case 4:
       own_prefetch(l, GS_GATEUP);
-      ok = st_gateup<DT, VD, false, true>(Pp, smem, l, X, nullptr, ring);
+      ok = st_gateup<DT, VD, VF, false, true>(Pp, smem, l, X, nullptr, ring);
       break;
     case 5:  // the residual x_mid that the down outputs add to
       ok = poll_f32(X + P.xl.xmid + (size_t)l * P.d, P.d, c.s.xres, c.w, c.t);
       own_prefetch(l, GS_DOWN);
-      ok = ok && st_down<DT, VF, false, true>(Pp, smem, l, X, nullptr, ring);
+      ok = ok && st_down<DT, VD, VF, false, true>(Pp, smem, l, X, nullptr, ring);
       break;
     case 6: {
       own_prefetch(0, GS_LM);
@@ -1553,8 +1689,66 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __rest
 // ---------------------------------------------------------------------------
 // Isolated GEMV probe: y[i] = W[i % ncopy] x[i], rows split over the grid,
 // one launch for all vectors.  Same engine as the decode stages.
+//
+// PIPE = false (stage form): each product first loads its input vector into
+// LDS and only then streams its weights, as a decode stage does with an input
+// that arrives by hand-off.
+// PIPE = true (streaming form): the inputs are all known before the launch,
+// so while product i streams, each thread already holds its part of vector
+// i + 1 in registers, and product i's last ring block issues the first
+// weight vectors of product i + 1 (the cross-stage prefetch of the decode
+// stages); the weight stream does not stop between products.
 // ---------------------------------------------------------------------------
+constexpr int kProbeXv = 4;  // input vectors per thread: cols <= 16384 = 4 * 512 * 8
+
 template <int DT>
+__device__ __forceinline__ void probe_x_to_lds(uint16_t* xs, const uint4 (&xv)[kProbeXv], int nv8, int t) {
+  constexpr int AW = kActWords<DT>;  // the probe's input is 16-bit already: bf16 residual terms are zero
+#pragma unroll
+  for (int k = 0; k < kProbeXv; ++k) {
+    const int i = t + k * kThreads;
+    if (i < nv8) {
+      reinterpret_cast<uint4*>(xs)[i * AW] = xv[k];
+      for (int a = 1; a < AW; ++a) reinterpret_cast<uint4*>(xs)[i * AW + a] = make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+// The streaming form's product loop for one width class (VPT, WIDE), so that
+// no branch of a width dispatch joins inside the loop: at such a join the
+// compiler copies the in-flight input registers and first waits for every
+// outstanding load, including the next product's prefetched weights.
+template <int DT, int VPT, bool WIDE, class PlanOf, class LoadX>
+__device__ __forceinline__ void probe_stream_loop(PlanOf plan_of, LoadX load_x, uint16_t* xs, float* red, float* yv,
+                                                  float* y, int rows, int r0, int nr, int nv8, int nvec) {
+  uint4 ring[kDepth];
+  uint4 xv[kProbeXv];
+  {
+    const int t = (int)threadIdx.x;
+    load_x(xv, 0, t);
+    probe_x_to_lds<DT>(xs, xv, nv8, t);
+    __syncthreads();
+  }
+  for (int iv = 0; iv < nvec; ++iv) {
+    const int t = opaque_v((int)threadIdx.x);
+    const StagePlan pl = plan_of(iv, t);
+    const StagePlan np = iv + 1 < nvec ? plan_of(iv + 1, t) : StagePlan{};
+    // vector i + 1 is read while product i streams (its loads queue behind
+    // this product's first ring block, which the previous product issued)
+    auto prep = [&](auto fill) -> bool {
+      fill();
+      if (iv + 1 < nvec) load_x(xv, iv + 1, t);
+      return true;
+    };
+    gemv<DT, VPT, WIDE, decltype(prep), kDepth>(pl, prep, xs, red, yv, t, ring, iv > 0, np, nullptr, 0);
+    // gemv ended with a barrier after its last read of xs
+    for (int r = t; r < nr; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
+    if (iv + 1 < nvec) probe_x_to_lds<DT>(xs, xv, nv8, t);
+    __syncthreads();
+  }
+}
+
+template <int DT, bool PIPE>
 __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int rows, int cols, int ncopy,
                                                           const uint16_t* x, float* y, int nvec) {
   extern __shared__ __align__(16) char smem[];
@@ -1563,25 +1757,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
   float* yv = red + kRedCap;
   const int nb = gridDim.x, wg = blockIdx.x;
   const int r0 = split_lo(rows, nb, wg), r1 = split_lo(rows, nb, wg + 1);
-  for (int iv = 0; iv < nvec; ++iv) {
-    const int t = opaque_v((int)threadIdx.x);
-    const uint16_t* Wc = W + (size_t)(iv % ncopy) * rows * cols;
+  const int nv8 = cols >> 3;
+  auto load_x = [&](uint4 (&xv)[kProbeXv], int iv, int t) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
+#pragma unroll
+    for (int k = 0; k < kProbeXv; ++k) {
+      const int i = t + k * kThreads;
+      xv[k] = i < nv8 ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto plan_of = [&](int iv, int t) {
     StagePlan pl = plan_rows(r1 - r0, cols, t);
-    pl.seg0 = Wc + (size_t)r0 * cols;
-    auto prep = [&]() -> bool {  // the probe's input is 16-bit already: bf16 residuals are zero
-      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
-      constexpr int AW = kActWords<DT>;
-      for (int i = t; i < (cols >> 3); i += kThreads) {
-        reinterpret_cast<uint4*>(xs)[i * AW] = src[i];
-        for (int a = 1; a < AW; ++a) reinterpret_cast<uint4*>(xs)[i * AW + a] = make_uint4(0, 0, 0, 0);
-      }
+    pl.seg0 = W + (size_t)(iv % ncopy) * rows * cols + (size_t)r0 * cols;
+    return pl;
+  };
+  if constexpr (!PIPE) {
+    for (int iv = 0; iv < nvec; ++iv) {
+      const int t = opaque_v((int)threadIdx.x);
+      const StagePlan pl = plan_of(iv, t);
+      auto prep = [&](auto fill) -> bool {
+        fill();
+        uint4 xv[kProbeXv];
+        load_x(xv, iv, t);
+        probe_x_to_lds<DT>(xs, xv, nv8, t);
+        __syncthreads();
+        return true;
+      };
+      uint4 ring[kDepth];
+      gemv_any<DT>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
+      for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
       __syncthreads();
-      return true;
-    };
-    uint4 ring[kDepth];
-    gemv_any<DT>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
-    for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
-    __syncthreads();
+    }
+  } else {
+    const StagePlan g = plan_of(0, (int)threadIdx.x);  // the width class is the same for every product
+    if (g.vpr < 64)
+      probe_stream_loop<DT, 1, false>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
+    else if (g.vpt == 1)
+      probe_stream_loop<DT, 1, true>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
+    else if (g.vpt == 2)
+      probe_stream_loop<DT, 2, true>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
+    else
+      probe_stream_loop<DT, 4, true>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
   }
 }
 

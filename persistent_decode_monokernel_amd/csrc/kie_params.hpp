@@ -91,6 +91,7 @@ struct Params {
   uint64_t timeout;           // poll deadline, ticks of the 100 MHz counter
   // dynamic LDS layout (bytes)
   int lds_xres, lds_xn, lds_scr, lds_misc, lds_bytes;
+  int grid;                   // work-groups of the launch (gridDim.x, read as a kernel parameter)
 };
 
 }  // namespace kie

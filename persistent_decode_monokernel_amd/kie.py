@@ -127,7 +127,7 @@ SIGNATURES = {
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
     "kie_gemv_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                      ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.POINTER(ctypes.c_float)]),
     "kie_gemm_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
@@ -396,15 +396,24 @@ class Engine:
         return int(n.value)
 
 
-def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None) -> Tuple[torch.Tensor, float]:
-    """y[i] = W[i % n_copies] @ x[i] in one persistent launch.  Returns (y fp32, kernel ms)."""
-    assert W.dim() == 3 and x.dim() == 2 and W.shape[2] == x.shape[1]
+def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None, streaming: bool = False) -> Tuple[torch.Tensor, float]:
+    """y[i] = W[i % n_copies] @ x[i] in one persistent launch.  streaming: the
+    next input and first weight vectors are read during the current product
+    (else each product loads its input first, as a decode stage).  Returns
+    (y fp32, kernel ms)."""
+    if not (isinstance(W, torch.Tensor) and isinstance(x, torch.Tensor) and W.dim() == 3 and x.dim() == 2
+            and W.shape[2] == x.shape[1]):
+        raise KieError(KIE_ERR_ARG, "gemv_probe: W must be [n_copies][rows][cols] and x [n_vec][cols]")
+    if W.device.type != "cuda" or x.device != W.device or not (W.is_contiguous() and x.is_contiguous()):
+        raise KieError(KIE_ERR_ARG, "gemv_probe: W and x must be contiguous tensors on one GPU")
+    if W.dtype not in (torch.float16, torch.bfloat16) or x.dtype != W.dtype:
+        raise KieError(KIE_ERR_ARG, f"gemv_probe: dtypes {W.dtype}, {x.dtype} (float16 or bfloat16, both alike)")
     n_copies, rows, cols = W.shape
     dtype = KIE_F16 if W.dtype == torch.float16 else KIE_BF16
     y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=W.device)
     ms = ctypes.c_float(0)
     _check(lib().kie_gemv_probe(ctypes.c_void_p(_dptr(W)), rows, cols, n_copies, ctypes.c_void_p(_dptr(x)),
-                                ctypes.c_void_p(_dptr(y)), x.shape[0], dtype,
+                                ctypes.c_void_p(_dptr(y)), x.shape[0], dtype, int(bool(streaming)),
                                 ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(ms)), "kie_gemv_probe")
     return y, ms.value
 

@@ -95,14 +95,19 @@ __device__ __forceinline__ void all_to_all(const ProbeArgs& p, int grid) {
     bool failed = false;
     const uint64_t tw = now();
     for (int n = 1;; ++n) {
+      // Every word of the lane is re-read each round, under a scalar test
+      // only (per is the same for the whole grid): with the loads under a
+      // per-lane test, the compiler waited for each load before issuing the
+      // next, and a round cost one memory round trip per word.
       uint64_t v[kMaxPer];
 #pragma unroll
       for (int j = 0; j < kMaxPer; ++j)
-        v[j] = rdy[j] ? (uint64_t)r : ld(p.s + kSlotW + (uint64_t)min(lane + 64 * j, grid - 1) * p.stride);
+        if (j < per) v[j] = ld(p.s + kSlotW + (uint64_t)min(lane + 64 * j, grid - 1) * p.stride);
+      __builtin_amdgcn_sched_barrier(0);
       bool all = true;
 #pragma unroll
       for (int j = 0; j < kMaxPer; ++j) {
-        rdy[j] = rdy[j] || v[j] >= (uint64_t)r;
+        if (j < per) rdy[j] = rdy[j] || v[j] >= (uint64_t)r;
         all = all && rdy[j];
       }
       if (all) break;

@@ -167,9 +167,9 @@ def gemv_probe_bench(n_copies: int = 16):
     1000 fresh vectors in ONE persistent launch of the same GEMV engine the
     decode stages use, over n_copies rotating weight copies (16 x 32 MiB = 512
     MiB, beyond the 256 MB Infinity Cache) or one copy (cache-resident).
-    Two forms: "stage" (each product loads its input first, as a decode stage
-    whose input arrives by hand-off) and "streaming" (the next input and the
-    next product's first weight vectors are read during the current product).
+    Two orders: "stage" (each product's first weight block, then its input
+    vector, as a decode stage whose weights were prefetched before its input
+    arrived) and "input first" (the input vector, then the weights).
     Algorithmic bytes per vector: the matrix, the input vector, the output."""
     import torch
 
@@ -178,12 +178,12 @@ def gemv_probe_bench(n_copies: int = 16):
     for (rows, cols), seed in zip(synth.GEMV_SHAPES, synth.GEMV_SEEDS):
         for nc in (n_copies, 1):
             W, x = synth.make_gemv(rows, cols, synth.GEMV_N_VEC, seed, n_copies=nc, device="cuda")
-            for streaming in (False, True):
-                kie.gemv_probe(W, x[:8], streaming=streaming)  # warm-up
-                _, ms = kie.gemv_probe(W, x, streaming=streaming)
+            for input_first in (False, True):
+                kie.gemv_probe(W, x[:8], input_first=input_first)  # warm-up
+                _, ms = kie.gemv_probe(W, x, input_first=input_first)
                 per = rows * cols * 2 + cols * 2 + rows * 4
                 gbs = per * synth.GEMV_N_VEC / (ms / 1e3) / 1e9
-                print(json.dumps({"gemv": f"{rows}x{cols} fp16", "form": "streaming" if streaming else "stage",
+                print(json.dumps({"gemv": f"{rows}x{cols} fp16", "order": "input first" if input_first else "stage",
                                   "copies": nc, "vectors": synth.GEMV_N_VEC,
                                   "kernel_ms": ms, "us_per_gemv": ms * 1e3 / synth.GEMV_N_VEC, "GB/s": gbs,
                                   "frac_of_8000": gbs / HBM_PEAK_GBS,

@@ -410,17 +410,18 @@ kie_status kie_check_tiling(const kie_config* cfg, int32_t grid, int32_t full);
  * [n_copies][rows][cols] of dtype: vector i uses copy i % n_copies (several
  * copies defeat the memory-side cache).  x_dev [n_vec][cols] of dtype;
  * y_dev [n_vec][rows] float.  cols a multiple of 256; rows >= 1.
- * streaming = 0 (stage form): each product first loads its input vector and
- * then streams its weights, as a decode stage whose input arrives by hand-off.
- * streaming = 1 (streaming form): the next input vector and the next
- * product's first weight vectors are read while the current product streams,
- * so the weight stream runs on across products.  Both forms give the same y.
+ * input_first = 0 (stage order): each product issues its first block of
+ * weight vectors, then reads its input vector, as a decode stage whose
+ * weights were prefetched before its input arrived by hand-off.
+ * input_first = 1: each product reads its input vector first and issues its
+ * weight vectors right behind it (the order when the input is at hand).
+ * Both orders give the same y.
  * *kernel_ms receives the launch duration (HIP events) if not NULL.
  * Runs on hip_stream (NULL = default) and synchronises it.  KIE_ERR_ARG for a
- * NULL or misaligned pointer, a bad size, dtype or streaming flag. */
+ * NULL or misaligned pointer, a bad size, dtype or input_first flag. */
 kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
                           const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
-                          int32_t streaming, void* hip_stream, float* kernel_ms);
+                          int32_t input_first, void* hip_stream, float* kernel_ms);
 
 /* ---- read-stream probe --------------------------------------------------- */
 

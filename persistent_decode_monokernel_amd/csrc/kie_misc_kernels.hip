@@ -48,8 +48,8 @@ const void* stream_probe_fn(int depth) {
   return nullptr;
 }
 
-const void* gemv_probe_fn(int dtype, bool pipelined) {
-  if (pipelined)
+const void* gemv_probe_fn(int dtype, bool input_first) {
+  if (input_first)
     return dtype == KIE_F16 ? reinterpret_cast<const void*>(&gemv_probe<KIE_F16, true>)
                             : reinterpret_cast<const void*>(&gemv_probe<KIE_BF16, true>);
   return dtype == KIE_F16 ? reinterpret_cast<const void*>(&gemv_probe<KIE_F16, false>)

@@ -600,14 +600,15 @@ __device__ __forceinline__ bool gemv_cls(const StagePlan& g, Prep prep, const ui
                                                                        StagePlan{}, tr, slot);
 }
 
-template <int DT, class Prep>
+template <int DT, int RS = kDepth, class Prep>
 __device__ __forceinline__ bool gemv_any(const StagePlan& g, Prep prep, const uint16_t* xs, float* red, float* yv,
                                          int t, uint4 (&ring)[kDepth], bool prefilled, const StagePlan next,
                                          uint64_t* tr = nullptr, int slot = 0) {
+  // rows narrower than 512 columns keep the whole ring ahead (the compiler crashed on their split form)
   if (g.vpr < 64) return gemv<DT, 1, false, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
-  if (g.vpt == 1) return gemv<DT, 1, true, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
-  if (g.vpt == 2) return gemv<DT, 2, true, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
-  return gemv<DT, 4, true, Prep, kDepth>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpt == 1) return gemv<DT, 1, true, Prep, RS>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  if (g.vpt == 2) return gemv<DT, 2, true, Prep, RS>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
+  return gemv<DT, 4, true, Prep, RS>(g, prep, xs, red, yv, t, ring, prefilled, next, tr, slot);
 }
 
 
@@ -1690,14 +1691,13 @@ __global__ __launch_bounds__(kThreads, 1) void stage_kernel(const Params* __rest
 // Isolated GEMV probe: y[i] = W[i % ncopy] x[i], rows split over the grid,
 // one launch for all vectors.  Same engine as the decode stages.
 //
-// PIPE = false (stage form): each product first loads its input vector into
-// LDS and only then streams its weights, as a decode stage does with an input
-// that arrives by hand-off.
-// PIPE = true (streaming form): the inputs are all known before the launch,
-// so while product i streams, each thread already holds its part of vector
-// i + 1 in registers, and product i's last ring block issues the first
-// weight vectors of product i + 1 (the cross-stage prefetch of the decode
-// stages); the weight stream does not stop between products.
+// INPUT_FIRST = false (stage order): each product issues its first weight
+// block, then reads its input vector, as a decode stage whose weights were
+// prefetched before its input arrived by hand-off.  Loads return in issue
+// order, so the input waits behind that block.
+// INPUT_FIRST = true: each product reads its input vector first and issues
+// the whole weight block right behind it (the order when the input is at
+// hand), so the input returns one round trip later while the weights stream.
 // ---------------------------------------------------------------------------
 constexpr int kProbeXv = 4;  // input vectors per thread: cols <= 16384 = 4 * 512 * 8
 
@@ -1714,41 +1714,7 @@ __device__ __forceinline__ void probe_x_to_lds(uint16_t* xs, const uint4 (&xv)[k
   }
 }
 
-// The streaming form's product loop for one width class (VPT, WIDE), so that
-// no branch of a width dispatch joins inside the loop: at such a join the
-// compiler copies the in-flight input registers and first waits for every
-// outstanding load, including the next product's prefetched weights.
-template <int DT, int VPT, bool WIDE, class PlanOf, class LoadX>
-__device__ __forceinline__ void probe_stream_loop(PlanOf plan_of, LoadX load_x, uint16_t* xs, float* red, float* yv,
-                                                  float* y, int rows, int r0, int nr, int nv8, int nvec) {
-  uint4 ring[kDepth];
-  uint4 xv[kProbeXv];
-  {
-    const int t = (int)threadIdx.x;
-    load_x(xv, 0, t);
-    probe_x_to_lds<DT>(xs, xv, nv8, t);
-    __syncthreads();
-  }
-  for (int iv = 0; iv < nvec; ++iv) {
-    const int t = opaque_v((int)threadIdx.x);
-    const StagePlan pl = plan_of(iv, t);
-    const StagePlan np = iv + 1 < nvec ? plan_of(iv + 1, t) : StagePlan{};
-    // vector i + 1 is read while product i streams (its loads queue behind
-    // this product's first ring block, which the previous product issued)
-    auto prep = [&](auto fill) -> bool {
-      fill();
-      if (iv + 1 < nvec) load_x(xv, iv + 1, t);
-      return true;
-    };
-    gemv<DT, VPT, WIDE, decltype(prep), kDepth>(pl, prep, xs, red, yv, t, ring, iv > 0, np, nullptr, 0);
-    // gemv ended with a barrier after its last read of xs
-    for (int r = t; r < nr; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
-    if (iv + 1 < nvec) probe_x_to_lds<DT>(xs, xv, nv8, t);
-    __syncthreads();
-  }
-}
-
-template <int DT, bool PIPE>
+template <int DT, bool INPUT_FIRST>
 __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int rows, int cols, int ncopy,
                                                           const uint16_t* x, float* y, int nvec) {
   extern __shared__ __align__(16) char smem[];
@@ -1758,46 +1724,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemv_probe(const uint16_t* W, int
   const int nb = gridDim.x, wg = blockIdx.x;
   const int r0 = split_lo(rows, nb, wg), r1 = split_lo(rows, nb, wg + 1);
   const int nv8 = cols >> 3;
-  auto load_x = [&](uint4 (&xv)[kProbeXv], int iv, int t) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
-#pragma unroll
-    for (int k = 0; k < kProbeXv; ++k) {
-      const int i = t + k * kThreads;
-      xv[k] = i < nv8 ? src[i] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto plan_of = [&](int iv, int t) {
+  for (int iv = 0; iv < nvec; ++iv) {
+    const int t = opaque_v((int)threadIdx.x);
     StagePlan pl = plan_rows(r1 - r0, cols, t);
     pl.seg0 = W + (size_t)(iv % ncopy) * rows * cols + (size_t)r0 * cols;
-    return pl;
-  };
-  if constexpr (!PIPE) {
-    for (int iv = 0; iv < nvec; ++iv) {
-      const int t = opaque_v((int)threadIdx.x);
-      const StagePlan pl = plan_of(iv, t);
-      auto prep = [&](auto fill) -> bool {
-        fill();
-        uint4 xv[kProbeXv];
-        load_x(xv, iv, t);
-        probe_x_to_lds<DT>(xs, xv, nv8, t);
-        __syncthreads();
-        return true;
-      };
-      uint4 ring[kDepth];
-      gemv_any<DT>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
-      for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
+    auto prep = [&](auto fill) -> bool {
+      const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)iv * cols);
+      uint4 xv[kProbeXv];
+#pragma unroll
+      for (int k = 0; k < kProbeXv; ++k) {
+        const int i = t + k * kThreads;
+        xv[k] = i < nv8 ? src[i] : make_uint4(0, 0, 0, 0);
+      }
+      fill();  // the rest of the ring (all of it with INPUT_FIRST) right behind the input's loads
+      probe_x_to_lds<DT>(xs, xv, nv8, t);
       __syncthreads();
-    }
-  } else {
-    const StagePlan g = plan_of(0, (int)threadIdx.x);  // the width class is the same for every product
-    if (g.vpr < 64)
-      probe_stream_loop<DT, 1, false>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
-    else if (g.vpt == 1)
-      probe_stream_loop<DT, 1, true>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
-    else if (g.vpt == 2)
-      probe_stream_loop<DT, 2, true>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
-    else
-      probe_stream_loop<DT, 4, true>(plan_of, load_x, xs, red, yv, y, rows, r0, r1 - r0, nv8, nvec);
+      return true;
+    };
+    uint4 ring[kDepth];
+    gemv_any<DT, INPUT_FIRST ? 0 : kDepth>(pl, prep, xs, red, yv, t, ring, false, StagePlan{});
+    for (int r = t; r < r1 - r0; r += kThreads) y[(size_t)iv * rows + r0 + r] = yv[r];
+    __syncthreads();
   }
 }
 

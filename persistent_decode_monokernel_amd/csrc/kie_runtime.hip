@@ -34,7 +34,7 @@ const void* stage_kernel_fn_bf16_g1(int vd, int vf);
 const void* stage_kernel_fn_bf16_g2(int vd, int vf);
 const void* stage_kernel_fn_bf16_g4(int vd, int vf);
 const void* stage_kernel_fn_bf16_g8(int vd, int vf);
-const void* gemv_probe_fn(int dtype, bool pipelined);
+const void* gemv_probe_fn(int dtype, bool input_first);
 const void* stream_probe_fn(int depth);
 hipError_t launch_fill(uint32_t* p, uint64_t n, uint32_t v, hipStream_t st);
 }  // namespace kie
@@ -911,9 +911,9 @@ extern "C" kie_status kie_check_idle_sets(const kie_engine* e, uint64_t* dirty_w
 
 extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t cols, int32_t n_copies,
                                      const void* x_dev, float* y_dev, int32_t n_vec, int32_t dtype,
-                                     int32_t streaming, void* hip_stream, float* kernel_ms) {
+                                     int32_t input_first, void* hip_stream, float* kernel_ms) {
   if (!W_dev || !x_dev || !y_dev || rows < 1 || n_copies < 1 || n_vec < 0) return KIE_ERR_ARG;
-  if (streaming != 0 && streaming != 1) return KIE_ERR_ARG;
+  if (input_first != 0 && input_first != 1) return KIE_ERR_ARG;
   if (dtype != KIE_F16 && dtype != KIE_BF16) return KIE_ERR_ARG;
   if (!k_ok(cols)) return KIE_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(W_dev) & 15) || (reinterpret_cast<uintptr_t>(x_dev) & 15)) return KIE_ERR_ARG;
@@ -932,7 +932,7 @@ extern "C" kie_status kie_gemv_probe(const void* W_dev, int32_t rows, int32_t co
   const int max_rows = (rows + grid - 1) / grid;
   const int vpr = cols / 8, lpr = vpr < kThreads ? vpr : kThreads, nwr = lpr >= 64 ? lpr / 64 : 1;
   if ((long long)max_rows * nwr > kRedCap || max_rows > kYCap) return KIE_ERR_UNSUPPORTED;
-  const void* fn = gemv_probe_fn(dtype, streaming != 0);
+  const void* fn = gemv_probe_fn(dtype, input_first != 0);
   KIE_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   hipEvent_t a, b;
   KIE_HIP(hipEventCreate(&a));

@@ -396,11 +396,10 @@ class Engine:
         return int(n.value)
 
 
-def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None, streaming: bool = False) -> Tuple[torch.Tensor, float]:
-    """y[i] = W[i % n_copies] @ x[i] in one persistent launch.  streaming: the
-    next input and first weight vectors are read during the current product
-    (else each product loads its input first, as a decode stage).  Returns
-    (y fp32, kernel ms)."""
+def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None, input_first: bool = False) -> Tuple[torch.Tensor, float]:
+    """y[i] = W[i % n_copies] @ x[i] in one persistent launch.  input_first:
+    each product reads its input vector before its weights (else after its
+    first weight block, a decode stage's order).  Returns (y fp32, kernel ms)."""
     if not (isinstance(W, torch.Tensor) and isinstance(x, torch.Tensor) and W.dim() == 3 and x.dim() == 2
             and W.shape[2] == x.shape[1]):
         raise KieError(KIE_ERR_ARG, "gemv_probe: W must be [n_copies][rows][cols] and x [n_vec][cols]")
@@ -413,7 +412,7 @@ def gemv_probe(W: torch.Tensor, x: torch.Tensor, stream=None, streaming: bool = 
     y = torch.empty((x.shape[0], rows), dtype=torch.float32, device=W.device)
     ms = ctypes.c_float(0)
     _check(lib().kie_gemv_probe(ctypes.c_void_p(_dptr(W)), rows, cols, n_copies, ctypes.c_void_p(_dptr(x)),
-                                ctypes.c_void_p(_dptr(y)), x.shape[0], dtype, int(bool(streaming)),
+                                ctypes.c_void_p(_dptr(y)), x.shape[0], dtype, int(bool(input_first)),
                                 ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(ms)), "kie_gemv_probe")
     return y, ms.value
 

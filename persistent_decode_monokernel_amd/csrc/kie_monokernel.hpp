@@ -98,7 +98,7 @@ __device__ __forceinline__ void publish_delay(CParams& P) {
 // for all of it; issued behind part of it, the poll returns sooner while the
 // rest of the ring keeps the weight stream going.
 #ifndef KIE_RING_SPLIT
-#define KIE_RING_SPLIT 8
+#define KIE_RING_SPLIT KIE_DEPTH
 #endif
 constexpr int kRingSplit = KIE_RING_SPLIT;
 static_assert(kRingSplit >= 1 && kRingSplit <= kDepth, "ring split");

@@ -13,7 +13,10 @@ constexpr int kClMin = 16;               // shortest split-KV chunk (positions)
 constexpr int kAttnUnits = 256;          // target (KV head, chunk) units per layer
 constexpr int kRedCap = 8192;            // LDS floats for per-wave GEMV partial sums
 constexpr int kYCap = 1024;              // LDS floats for finished GEMV rows
-constexpr int kDepth = 8;               // weight vectors in flight per thread
+#ifndef KIE_DEPTH
+#define KIE_DEPTH 8
+#endif
+constexpr int kDepth = KIE_DEPTH;       // weight vectors in flight per thread (a multiple of 4)
 constexpr uint32_t kSent = 0xFFFFFFFFu;  // NaN pattern that marks "not written yet"
 constexpr int kCand = 64;                // sampling: candidates per work-group list and in the global list
 constexpr int kPadIdx = 0x40000000;      // sampling: indices of padding candidates (logit -inf) start here

@@ -67,11 +67,11 @@ def bytes_per_launch(s, pos0: int, n_steps: int) -> int:
 MEASURED_TRAFFIC = {
     # (workload, timed steps): the timed kie_decode after the 512-token prefill,
     # FETCH_SIZE x 2.0, WRITE_SIZE x 1.0 (KiB per dispatch x 1024)
-    ("2b", 1024): {"src_sha": "858107c9ed519d0a",
-                   "fetch_bytes": 1858159576 * 1024 * 2, "write_bytes": 33028477 * 1024},
+    ("2b", 1024): {"src_sha": "33cf3cfcb7b100bd",
+                   "fetch_bytes": 1858231760 * 1024 * 2, "write_bytes": 33028477 * 1024},
     # the same command as `--gpus 1 --steps 20 --warmup 5`
-    ("2b", 20): {"src_sha": "858107c9ed519d0a",
-                 "fetch_bytes": 35850047 * 1024 * 2, "write_bytes": 417800 * 1024},
+    ("2b", 20): {"src_sha": "33cf3cfcb7b100bd",
+                 "fetch_bytes": 35848209 * 1024 * 2, "write_bytes": 417800 * 1024},
 }
 
 KERNEL_SRC_DIR = os.path.join(ROOT, "persistent_decode_monokernel_amd", "csrc")
